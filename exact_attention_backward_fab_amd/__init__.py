@@ -1,0 +1,245 @@
+"""Python binding of libfab, the exact attention backward for AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfab.so`` (built in-tree by ``build.py``).  PyTorch supplies
+device memory and the stream; no attention arithmetic happens here.  If the
+library is missing the import of this module's compute entry points fails
+loudly; there is no fallback.
+
+Tensors use ggml ne order stored C-contiguous with the shape reversed (see
+include/fab.h): q (B,H,N,DK), k (B,Hkv,M,DK), v (B,Hkv,M,DV), d and O
+(B,N,H,DV), lse (B,H,N), mask (N,M) int16/uint16 f16 bit patterns or float16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfab.so")
+
+FAB_MODE_F32 = 0
+FAB_MODE_BF16 = 1
+MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
+         FAB_MODE_BF16: FAB_MODE_BF16}
+
+FAB_OK = 0
+FAB_E_INVAL = -1
+FAB_E_UNSUPPORTED = -2
+FAB_E_WORKSPACE = -3
+FAB_E_ALIGN = -4
+FAB_E_HIP = -5
+
+# every symbol include/fab.h declares
+EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
+           "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
+           "fab_strerror", "fab_last_error", "fab_version")
+KERNELS = ("block_map", "forward", "prep", "backward", "gqa_reduce")
+
+
+class FabShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "H", "Hkv", "N", "M", "DK", "DV")]
+
+
+class FabError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libfab error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libfab.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python exact_attention_backward_fab_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        SP = ctypes.POINTER(FabShape)
+        L.fab_blob_layout.restype = I
+        L.fab_blob_layout.argtypes = [SP, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                      ctypes.POINTER(I64), ctypes.POINTER(I64)]
+        L.fab_workspace_bytes.restype = I
+        L.fab_workspace_bytes.argtypes = [SP, I, I, I, ctypes.POINTER(SZ)]
+        L.fab_forward_lse.restype = I
+        L.fab_forward_lse.argtypes = [SP, P, P, P, P, ctypes.c_float, I, P, P, P, SZ, P]
+        L.fab_backward.restype = I
+        L.fab_backward.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, P, SZ, P]
+        L.fab_strerror.restype = ctypes.c_char_p
+        L.fab_strerror.argtypes = [I]
+        L.fab_last_error.restype = ctypes.c_char_p
+        L.fab_last_error.argtypes = []
+        L.fab_version.restype = I
+        L.fab_version.argtypes = []
+        L.fab_profile_enable.restype = I
+        L.fab_profile_enable.argtypes = [I]
+        L.fab_profile_reset.restype = I
+        L.fab_profile_reset.argtypes = []
+        L.fab_profile_read.restype = I
+        L.fab_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(I64)]
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != FAB_OK:
+        raise FabError(rc, lib().fab_last_error().decode() or lib().fab_strerror(rc).decode())
+
+
+@dataclass(frozen=True)
+class Shape:
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    M: int
+    DK: int
+    DV: int
+
+    def c(self):
+        return FabShape(self.B, self.H, self.Hkv, self.N, self.M, self.DK, self.DV)
+
+
+def shape_of(q, k, v):
+    B, H, N, DK = q.shape
+    Bk, Hkv, M, DKk = k.shape
+    DV = v.shape[-1]
+    return Shape(B, H, Hkv, N, M, DK, DV)
+
+
+def blob_layout(shape: Shape):
+    """(off_q, off_k, off_v, total_floats) of the packed [dQ | dK | dV] blob."""
+    o = [ctypes.c_int64() for _ in range(4)]
+    _check(lib().fab_blob_layout(ctypes.byref(shape.c()), *[ctypes.byref(x) for x in o]))
+    return tuple(x.value for x in o)
+
+
+def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fab_workspace_bytes(ctypes.byref(shape.c()), MODES[mode], int(bool(has_mask)),
+                                     int(bool(have_o_lse)), ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mask_arg(mask):
+    if mask is None:
+        return None
+    import torch
+    if mask.dtype == torch.float16:
+        mask = mask.view(torch.int16)
+    if mask.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("mask must hold f16 bit patterns (float16, int16 or uint16)")
+    return mask
+
+
+def _check_tensor(t, name, shape, device):
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device):
+    import torch
+    n = workspace_bytes(shape, mode, has_mask, have_o_lse)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None):
+    """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v."""
+    import torch
+    s = shape_of(q, k, v)
+    dev = q.device
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev)
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev)
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev)
+    mask = _mask_arg(mask)
+    if O is None:
+        O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev)
+    else:
+        nbytes = ws.numel() * ws.element_size()
+    _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                 float(scale), MODES[mode], _ptr(O), _ptr(lse), _ptr(ws), nbytes,
+                                 _stream_handle(stream)))
+    return O, lse
+
+
+def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=None, ws=None,
+             stream=None):
+    """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v)."""
+    import torch
+    s = shape_of(q, k, v)
+    dev = q.device
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev)
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev)
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev)
+    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), dev)
+    mask = _mask_arg(mask)
+    total = blob_layout(s)[3]
+    if blob is None:
+        blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev)
+    else:
+        nbytes = ws.numel() * ws.element_size()
+    _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
+                              float(scale), MODES[mode], _ptr(O), _ptr(lse), _ptr(blob),
+                              _ptr(ws), nbytes, _stream_handle(stream)))
+    return blob
+
+
+def unpack(blob, shape: Shape):
+    """Views dq (B,H,N,DK), dk (B,Hkv,M,DK), dv (B,Hkv,M,DV) into the blob at the padded offsets."""
+    s = shape
+    _, off_k, off_v, _ = blob_layout(s)
+    nq, nk, nv = s.DK * s.N * s.H * s.B, s.DK * s.M * s.Hkv * s.B, s.DV * s.M * s.Hkv * s.B
+    dq = blob[0:nq].view(s.B, s.H, s.N, s.DK)
+    dk = blob[off_k:off_k + nk].view(s.B, s.Hkv, s.M, s.DK)
+    dv = blob[off_v:off_v + nv].view(s.B, s.Hkv, s.M, s.DV)
+    return dq, dk, dv
+
+
+def profile_enable(on=True):
+    """Bracket every kernel launch with HIP events (measurement only)."""
+    _check(lib().fab_profile_enable(int(bool(on))))
+
+
+def profile_reset():
+    _check(lib().fab_profile_reset())
+
+
+def profile_read():
+    """{kernel: (total_ms, launches)} since the last reset (waits for the events)."""
+    out = {}
+    for name in KERNELS:
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        _check(lib().fab_profile_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,388 @@
+// fab_api.cpp -- the C ABI of libfab (see include/fab.h): argument
+// validation, result-blob layout, workspace carving and the launch sequence.
+// No HIP call is made before every argument has been checked, so the
+// validation paths run on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fab.h"
+#include "fab_launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int kMaxHeadDim = 192;
+constexpr size_t kWsAlign = 256;
+
+int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+    fab::Dims d;
+    int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
+    // workspace offsets (bytes) and total
+    size_t ws_map, ws_lse, ws_O, ws_delta, ws_pk, ws_pv, ws_bytes;
+    bool gqa;
+};
+
+// Shape checks: the asserts of "Function ggml_flash_attn_back" restated for the
+// ggmlR layouts (q [DK,N,H,B], k [DK,M,Hkv,B], v [DV,M,Hkv,B], d [DV,H,N,B]),
+// plus the limits of these kernels.
+int check_shape(const fab_shape *s, Plan *pl)
+{
+    if (!s) return fail(FAB_E_INVAL, "shape is NULL");
+    if (s->B < 0 || s->N < 0 || s->M < 0)
+        return fail(FAB_E_INVAL, "B, N and M must be >= 0 (got B=%lld N=%lld M=%lld)",
+                    (long long)s->B, (long long)s->N, (long long)s->M);
+    if (s->H < 1 || s->Hkv < 1 || s->DK < 1 || s->DV < 1)
+        return fail(FAB_E_INVAL, "H, Hkv, DK and DV must be >= 1");
+    if (s->H % s->Hkv != 0)
+        return fail(FAB_E_INVAL, "H (%lld) must be a multiple of Hkv (%lld)", (long long)s->H,
+                    (long long)s->Hkv);
+    if (s->DK > kMaxHeadDim || s->DV > kMaxHeadDim)
+        return fail(FAB_E_UNSUPPORTED, "head dims above %d are not supported (DK=%lld DV=%lld)",
+                    kMaxHeadDim, (long long)s->DK, (long long)s->DV);
+    // element counts, computed with overflow guards
+    const double fq = (double)s->DK * s->N * s->H * s->B;
+    const double fk = (double)s->DK * s->M * s->H * s->B;  // per-head dK partials bound nk
+    const double fv = (double)s->DV * s->M * s->H * s->B;
+    const double fo = (double)s->DV * s->N * s->H * s->B;
+    const double fm = (double)s->M * s->N;
+    if (fq > kMaxElems || fk > kMaxElems || fv > kMaxElems || fo > kMaxElems || fm > kMaxElems)
+        return fail(FAB_E_UNSUPPORTED, "a tensor exceeds 2^31-1 elements");
+    pl->d = fab::Dims{(int)s->B, (int)s->H, (int)s->Hkv, (int)s->N, (int)s->M, (int)s->DK, (int)s->DV};
+    pl->nq = s->DK * s->N * s->H * s->B;
+    pl->nk = s->DK * s->M * s->Hkv * s->B;
+    pl->nv = s->DV * s->M * s->Hkv * s->B;
+    pl->nO = s->DV * s->H * s->N * s->B;
+    pl->nrow = s->N * s->H * s->B;
+    pl->off_k = pad4(pl->nq);
+    pl->off_v = pl->off_k + pad4(pl->nk);
+    pl->total = pl->off_v + pad4(pl->nv);
+    if ((double)pl->total > kMaxElems) return fail(FAB_E_UNSUPPORTED, "result blob exceeds 2^31-1 floats");
+    pl->gqa = s->H > s->Hkv;
+    return FAB_OK;
+}
+
+void plan_workspace(Plan *pl, int has_mask, int have_o_lse)
+{
+    const fab::Dims &d = pl->d;
+    size_t off = 0;
+    const int64_t nqb = (d.N + 31) / 32, nkb = (d.M + 31) / 32;
+    pl->ws_map = off;
+    if (has_mask) off = align_up(off + (size_t)(nqb * nkb));
+    pl->ws_lse = off;
+    pl->ws_O = off;
+    if (!have_o_lse) {
+        off = align_up(off + sizeof(float) * (size_t)pl->nrow);
+        pl->ws_O = off;
+        off = align_up(off + sizeof(float) * (size_t)pl->nO);
+    }
+    pl->ws_delta = off;
+    off = align_up(off + sizeof(float) * (size_t)pl->nrow);
+    pl->ws_pk = off;
+    pl->ws_pv = off;
+    if (pl->gqa) {
+        off = align_up(off + sizeof(float) * (size_t)d.DK * d.M * d.H * d.B);
+        pl->ws_pv = off;
+        off = align_up(off + sizeof(float) * (size_t)d.DV * d.M * d.H * d.B);
+    }
+    pl->ws_bytes = off;
+}
+
+int check_mode(int mode)
+{
+    if (mode != FAB_MODE_F32 && mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "unknown mode %d", mode);
+    return FAB_OK;
+}
+
+int check_ptr(const void *p, int64_t elems, const char *name)
+{
+    if (elems == 0) return FAB_OK;
+    if (!p) return fail(FAB_E_INVAL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(FAB_E_ALIGN, "%s is not 16-byte aligned", name);
+    return FAB_OK;
+}
+
+int check_ws(const void *ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0) return FAB_OK;
+    if (!ws) return fail(FAB_E_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1)) != 0)
+        return fail(FAB_E_ALIGN, "workspace is not %zu-byte aligned", kWsAlign);
+    if (ws_bytes < need) return fail(FAB_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return FAB_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(FAB_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FAB_TRY(x)                 \
+    do {                           \
+        const int rc__ = (x);      \
+        if (rc__ != FAB_OK) return rc__; \
+    } while (0)
+
+#define FAB_HIP(call, what)                        \
+    do {                                           \
+        const hipError_t e__ = (call);             \
+        if (e__ != hipSuccess) return hip_fail(e__, what); \
+    } while (0)
+
+// ---------------------------------------------------------------- measurement hooks
+enum Kid { kMap = 0, kFwd, kPrep, kBwd, kRed, kNumKid };
+const char *const kKidNames[kNumKid] = {"block_map", "forward", "prep", "backward", "gqa_reduce"};
+
+struct ProfRec {
+    int kid;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event()
+{
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+    int kid;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    ProfScope(int k, hipStream_t st) : kid(k), s(st)
+    {
+        if (!g_prof_on) return;
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        a = prof_event();
+        b = prof_event();
+        if (a) (void)hipEventRecord(a, s);
+    }
+    ~ProfScope()
+    {
+        if (!a || !b) return;
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof_recs.push_back(ProfRec{kid, a, b});
+    }
+};
+
+#define FAB_LAUNCH(kid, call, what)             \
+    do {                                        \
+        ProfScope ps__(kid, s);                 \
+        FAB_HIP(call, what);                    \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int fab_profile_enable(int on)
+{
+    g_err[0] = 0;
+    g_prof_on = on != 0;
+    return FAB_OK;
+}
+
+int fab_profile_reset(void)
+{
+    g_err[0] = 0;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (ProfRec &r : g_prof_recs) {
+        (void)hipEventSynchronize(r.b);
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_recs.clear();
+    return FAB_OK;
+}
+
+int fab_profile_read(const char *kernel, double *total_ms, int64_t *launches)
+{
+    g_err[0] = 0;
+    if (!kernel || !total_ms || !launches) return fail(FAB_E_INVAL, "NULL argument");
+    int kid = -1;
+    for (int i = 0; i < kNumKid; ++i)
+        if (std::strcmp(kernel, kKidNames[i]) == 0) kid = i;
+    if (kid < 0) return fail(FAB_E_INVAL, "unknown kernel name '%s'", kernel);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double sum = 0.0;
+    int64_t n = 0;
+    for (ProfRec &r : g_prof_recs) {
+        if (r.kid != kid) continue;
+        FAB_HIP(hipEventSynchronize(r.b), "event sync");
+        float ms = 0.f;
+        FAB_HIP(hipEventElapsedTime(&ms, r.a, r.b), "event elapsed time");
+        sum += ms;
+        ++n;
+    }
+    *total_ms = sum;
+    *launches = n;
+    return FAB_OK;
+}
+
+int fab_version(void) { return FAB_VERSION; }
+
+const char *fab_strerror(int status)
+{
+    switch (status) {
+    case FAB_OK: return "ok";
+    case FAB_E_INVAL: return "invalid argument";
+    case FAB_E_UNSUPPORTED: return "unsupported shape";
+    case FAB_E_WORKSPACE: return "workspace missing or too small";
+    case FAB_E_ALIGN: return "misaligned pointer";
+    case FAB_E_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *fab_last_error(void) { return g_err; }
+
+int fab_blob_layout(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int64_t *off_v,
+                    int64_t *total_floats)
+{
+    g_err[0] = 0;
+    Plan pl;
+    FAB_TRY(check_shape(shape, &pl));
+    if (off_q) *off_q = 0;
+    if (off_k) *off_k = pl.off_k;
+    if (off_v) *off_v = pl.off_v;
+    if (total_floats) *total_floats = pl.total;
+    return FAB_OK;
+}
+
+int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have_o_lse, size_t *bytes)
+{
+    g_err[0] = 0;
+    Plan pl;
+    FAB_TRY(check_shape(shape, &pl));
+    FAB_TRY(check_mode(mode));
+    if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
+    plan_workspace(&pl, has_mask != 0, have_o_lse != 0);
+    *bytes = pl.ws_bytes;
+    return FAB_OK;
+}
+
+int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, const float *v,
+                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
+                    size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    Plan pl;
+    FAB_TRY(check_shape(shape, &pl));
+    FAB_TRY(check_mode(mode));
+    if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
+    FAB_TRY(check_ptr(q, pl.nq, "q"));
+    FAB_TRY(check_ptr(k, pl.nk, "k"));
+    FAB_TRY(check_ptr(v, pl.nv, "v"));
+    FAB_TRY(check_ptr(O, pl.nO, "O"));
+    FAB_TRY(check_ptr(lse, pl.nrow, "lse"));
+    if (mask && !aligned16(mask)) return fail(FAB_E_ALIGN, "mask is not 16-byte aligned");
+    const bool use_mask = mask && (int64_t)pl.d.M * pl.d.N > 0;
+    plan_workspace(&pl, use_mask, 1);
+    const size_t need = use_mask ? pl.ws_map + (size_t)((pl.d.N + 31) / 32) * ((pl.d.M + 31) / 32) : 0;
+    FAB_TRY(check_ws(ws, ws_bytes, need));
+    if (pl.nrow == 0) return FAB_OK;  // no query rows: nothing to write
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    uint8_t *map = use_mask ? reinterpret_cast<uint8_t *>(wsb + pl.ws_map) : nullptr;
+    if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mask, map, pl.d, s), "block map launch");
+    FAB_LAUNCH(kFwd, fab::launch_forward(q, k, v, use_mask ? mask : nullptr, map, scale, mode == FAB_MODE_BF16,
+                                         O, lse, pl.d, s),
+               "forward launch");
+    return FAB_OK;
+}
+
+int fab_backward(const fab_shape *shape, const float *q, const float *k, const float *v,
+                 const uint16_t *mask, const float *d, float scale, int mode, const float *O,
+                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    Plan pl;
+    FAB_TRY(check_shape(shape, &pl));
+    FAB_TRY(check_mode(mode));
+    if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
+    if ((O == nullptr) != (lse == nullptr))
+        return fail(FAB_E_INVAL, "O and lse must be given together or both be NULL");
+    const bool have = O != nullptr;
+    FAB_TRY(check_ptr(q, pl.nq, "q"));
+    FAB_TRY(check_ptr(k, pl.nk, "k"));
+    FAB_TRY(check_ptr(v, pl.nv, "v"));
+    FAB_TRY(check_ptr(d, pl.nO, "d"));
+    if (have) {
+        FAB_TRY(check_ptr(O, pl.nO, "O"));
+        FAB_TRY(check_ptr(lse, pl.nrow, "lse"));
+    }
+    FAB_TRY(check_ptr(blob, pl.total, "blob"));
+    if (mask && !aligned16(mask)) return fail(FAB_E_ALIGN, "mask is not 16-byte aligned");
+    const bool use_mask = mask && (int64_t)pl.d.M * pl.d.N > 0;
+    plan_workspace(&pl, use_mask, have);
+    const bool empty = pl.d.B == 0 || pl.d.N == 0 || pl.d.M == 0;
+    FAB_TRY(check_ws(ws, ws_bytes, empty ? 0 : pl.ws_bytes));
+    if (pl.total == 0) return FAB_OK;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (empty) {
+        // no queries (dK = dV = 0) or no keys (every row all-masked: dQ = 0)
+        FAB_HIP(fab::launch_zero(blob, pl.total, s), "zero blob");
+        return FAB_OK;
+    }
+    char *wsb = static_cast<char *>(ws);
+    uint8_t *map = use_mask ? reinterpret_cast<uint8_t *>(wsb + pl.ws_map) : nullptr;
+    const uint16_t *mk = use_mask ? mask : nullptr;
+    const int bf16 = mode == FAB_MODE_BF16;
+    if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
+    const float *Ou = O, *lseu = lse;
+    if (!have) {
+        float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
+        float *lw = reinterpret_cast<float *>(wsb + pl.ws_lse);
+        FAB_LAUNCH(kFwd, fab::launch_forward(q, k, v, mk, map, scale, bf16, Ow, lw, pl.d, s), "forward launch");
+        Ou = Ow;
+        lseu = lw;
+    }
+    float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
+    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.nq, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
+               "prep launch");
+    float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
+    float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
+    FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, mk, map, lseu, delta, scale, bf16, blob, dk, dv, pl.gqa ? 1 : 0,
+                                          pl.d, s),
+               "backward launch");
+    if (pl.gqa) {
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, pl.d.DK, pl.d, s), "dK reduce launch");
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dv, blob + pl.off_v, pl.d.DV, pl.d, s), "dV reduce launch");
+    }
+    return FAB_OK;
+}
+
+}  // extern "C"

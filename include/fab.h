@@ -1,0 +1,149 @@
+/*
+ * fab.h -- C ABI of libfab: the exact (flash) attention backward on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the one PowerInfer's "Function ggml_flash_attn_back"
+ * constructs and the ggmlR test file "tests/testthat/test-flash-attn-back.R"
+ * exercises: given q, k, v, an optional additive f16 mask and the upstream
+ * gradient d of the attention output, return the gradients of sum(d * attn)
+ * with respect to q, k and v, packed into one f32 buffer.  The backward
+ * formulas are those of the labml "Flash Attention" page, section "Backward
+ * pass" (dV = P^T dO, dP = dO V^T, D = rowsum(dO o O), dS = P o (dP - D),
+ * dQ = scale dS K, dK = scale dS^T Q); the forward and its running max/sum
+ * are that page's "Forward pass" and "Flash Attention Optimization" sections.
+ *
+ * Tensor conventions (ggml ne order, ne0 fastest; every tensor contiguous f32,
+ * as in the ggmlR test file's header comment of `attn_ref`):
+ *     q    [DK, N,   H,   B]   element (c,n,h,b) at c + DK*(n + N*(h + H*b))
+ *     k    [DK, M,   Hkv, B]   element (c,m,g,b) at c + DK*(m + M*(g + Hkv*b))
+ *     v    [DV, M,   Hkv, B]   element (c,m,g,b) at c + DV*(m + M*(g + Hkv*b))
+ *     d, O [DV, H,   N,   B]   element (c,h,n,b) at c + DV*(h + H*(n + N*b))
+ *     mask [M,  N]  f16 bits   element (m,n)     at m + M*n, shared by all h, b
+ *     lse  [N,  H,   B]        element (n,h,b)   at n + N*(h + H*b)
+ * Query head h reads key/value head g = h / (H/Hkv) (grouped-query attention;
+ * H must be a multiple of Hkv).  Scores are scale*(q.k) + mask[m,n]: the scale
+ * multiplies first, then the mask is added.  A query row whose scores are all
+ * -inf is all-masked: its output row, its LSE (-inf) and its dQ row are zero
+ * and it contributes nothing to dK and dV.  The mask may hold finite values
+ * and -inf; +inf and NaN entries are outside the contract.
+ *
+ * Result blob (f32), the layout of "Function ggml_flash_attn_back" and the
+ * ggmlR test's `fab_grads` unpacker: [dQ | pad | dK | pad | dV | pad] with
+ *     off_q = 0, off_k = pad4(nq), off_v = off_k + pad4(nk), total = off_v + pad4(nv)
+ * in floats, where nq, nk, nv are the element counts of q, k, v and
+ * pad4(x) = ceil(x/4)*4 (16-byte alignment).  Every float of the blob is
+ * written; the pads are zero.
+ *
+ * Ownership and threading: the caller allocates and owns every buffer (inputs,
+ * outputs, workspace).  The library never allocates, frees or synchronises
+ * device memory; it only enqueues kernels on the caller's stream and keeps no
+ * per-call state, so calls on different streams with separate workspaces may
+ * run concurrently.
+ *
+ * Errors: every entry point validates all arguments before touching the
+ * device.  On any error nothing is enqueued and no output byte is written; the
+ * return value is a negative fab_status and fab_last_error() describes it
+ * (thread-local).  FAB_E_HIP reports a failed kernel launch; faults inside a
+ * kernel surface at the caller's next synchronisation of the stream.
+ */
+#ifndef FAB_H
+#define FAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FAB_VERSION 100  /* 1.0.0 */
+
+/* Problem extents.  B, N, M >= 0 (zero gives an empty problem); H, Hkv, DK,
+ * DV >= 1; H % Hkv == 0; DK, DV <= 192; every tensor below 2^31 elements. */
+typedef struct fab_shape {
+    int64_t B, H, Hkv, N, M, DK, DV;
+} fab_shape;
+
+/* Arithmetic mode of the dense contractions.
+ *   FAB_MODE_F32 : f32 operands on the f32 matrix cores (f32 accumulation).
+ *   FAB_MODE_BF16: q, k, v, d and the intermediate P and dS are rounded to
+ *                  bf16 (round-to-nearest-even) as matrix-core operands; all
+ *                  accumulation, the softmax statistics, D and the scale stay f32. */
+typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
+
+typedef enum fab_status {
+    FAB_OK = 0,
+    FAB_E_INVAL = -1,        /* bad shape, NULL pointer, bad scale or mode */
+    FAB_E_UNSUPPORTED = -2,  /* valid but outside what the kernels handle (DK/DV > 192, size) */
+    FAB_E_WORKSPACE = -3,    /* workspace missing or smaller than fab_workspace_bytes() */
+    FAB_E_ALIGN = -4,        /* a pointer is not 16-byte aligned (workspace: 256-byte) */
+    FAB_E_HIP = -5           /* a HIP launch or runtime call failed */
+} fab_status;
+
+/* Host only.  Blob offsets and total length, in floats (see above).
+ * Returns FAB_OK or FAB_E_INVAL. */
+int fab_blob_layout(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int64_t *off_v,
+                    int64_t *total_floats);
+
+/* Host only.  Workspace bytes that fab_forward_lse (have_o_lse ignored) or
+ * fab_backward need for this shape, mode and mask presence.  have_o_lse != 0
+ * means the caller will pass O and lse to fab_backward.  *bytes is written on
+ * FAB_OK. */
+int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have_o_lse,
+                        size_t *bytes);
+
+/* Forward with row log-sum-exp (labml "Flash Attention": "Forward pass" and the
+ * running max/sum of "Flash Attention Optimization").
+ *   q, k, v   device, f32, layouts above (read only)
+ *   mask      device f16 bits [M,N] or NULL for no mask (read only)
+ *   scale     finite f32 softmax scale
+ *   mode      fab_mode
+ *   O         device f32 [DV,H,N,B] (written): softmax(scale*q.k + mask) v
+ *   lse       device f32 [N,H,B] (written): natural-log log-sum-exp of the row's
+ *             scores, -inf for an all-masked row
+ *   ws        device workspace of ws_bytes >= fab_workspace_bytes(.., have_o_lse=1)
+ *   stream    hipStream_t of the caller (NULL = default stream) */
+int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, const float *v,
+                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* The attention backward ("Function ggml_flash_attn_back"; ggmlR
+ * `fab_grads`): gradients of sum(d * attn(q,k,v)) packed into blob.
+ *   q, k, v, mask, scale, mode  as for fab_forward_lse
+ *   d         device f32 [DV,H,N,B]: upstream gradient of the attention output
+ *   O, lse    either both NULL (the forward is recomputed internally, the
+ *             pages' semantics) or both given: the output and row LSE of the
+ *             same forward (as written by fab_forward_lse); exactly one NULL
+ *             is FAB_E_INVAL
+ *   blob      device f32, total_floats of fab_blob_layout (written in full)
+ *   ws        device workspace, ws_bytes >= fab_workspace_bytes(.., have_o_lse)
+ *   stream    hipStream_t of the caller */
+int fab_backward(const fab_shape *shape, const float *q, const float *k, const float *v,
+                 const uint16_t *mask, const float *d, float scale, int mode, const float *O,
+                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement hooks (they compute nothing).  While enabled, every kernel
+ * launch made by fab_forward_lse and fab_backward is bracketed by a pair of
+ * HIP events recorded on the caller's stream.  fab_profile_read waits for the
+ * recorded events of one kernel -- "block_map", "forward", "prep", "backward"
+ * or "gqa_reduce" -- and returns their summed duration in milliseconds and the
+ * number of launches since the last fab_profile_reset.  The events are created
+ * by the library on first use and kept for reuse; only one thread should use
+ * the hooks at a time.  Returns FAB_OK, FAB_E_INVAL (unknown kernel name or
+ * NULL output) or FAB_E_HIP. */
+int fab_profile_enable(int on);
+int fab_profile_reset(void);
+int fab_profile_read(const char *kernel, double *total_ms, int64_t *launches);
+
+/* Static text for a status code. */
+const char *fab_strerror(int status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *fab_last_error(void);
+/* FAB_VERSION of the library. */
+int fab_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAB_H */

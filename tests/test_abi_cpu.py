@@ -1,0 +1,110 @@
+"""CPU-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/fab.h declares, computes the blob layout of "Function
+ggml_flash_attn_back" / the ggmlR unpacker, and rejects bad arguments before any
+device work (the ggmlR test file's principle that unsupported input must be
+refused rather than answered wrongly)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_backward_fab_amd as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fab.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fab_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fab.lib()
+    declared = header_functions()
+    assert set(declared) == set(fab.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.fab_version() == 100
+
+
+def test_strerror_covers_every_status():
+    L = fab.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.fab_strerror(code).decode() not in ("", "unknown status")
+    assert L.fab_strerror(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("shape", [
+    fab.Shape(2, 4, 2, 2, 4, 3, 5), fab.Shape(1, 2, 1, 3, 5, 3, 5), fab.Shape(1, 1, 1, 1, 1, 1, 1),
+    fab.Shape(1, 32, 8, 2048, 2048, 128, 128), fab.Shape(4, 16, 16, 512, 4096, 192, 128),
+    fab.Shape(0, 2, 1, 3, 5, 3, 5), fab.Shape(1, 2, 1, 0, 5, 3, 5)])
+def test_blob_layout_matches_the_pages_padding(shape):
+    s = shape
+    nq, nk, nv = s.DK * s.N * s.H * s.B, s.DK * s.M * s.Hkv * s.B, s.DV * s.M * s.Hkv * s.B
+    pad = lambda n: int(math.ceil(n * 4 / 16) * 16 / 4)
+    assert fab.blob_layout(s) == (0, pad(nq), pad(nq) + pad(nk), pad(nq) + pad(nk) + pad(nv))
+
+
+def test_workspace_grows_with_what_must_be_recomputed():
+    s = fab.Shape(1, 8, 2, 300, 400, 64, 64)
+    base = fab.workspace_bytes(s, "bf16", False, True)
+    assert fab.workspace_bytes(s, "bf16", True, True) > base      # mask block map
+    assert fab.workspace_bytes(s, "bf16", False, False) > base    # internal O and LSE
+    mha = fab.Shape(1, 8, 8, 300, 400, 64, 64)
+    assert fab.workspace_bytes(mha, "bf16", False, True) < base  # no grouped-query partials
+
+
+FAKE = 1 << 20   # a 256-byte aligned address that is never dereferenced: every call below fails validation
+
+
+def call_bwd(shape, q=FAKE, k=FAKE, v=FAKE, mask=None, d=FAKE, scale=0.5, mode=0, O=None, lse=None,
+             blob=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    L = fab.lib()
+    return L.fab_backward(ctypes.byref(fab.FabShape(*shape)), P(q), P(k), P(v), P(mask), P(d),
+                          float(scale), mode, P(O), P(lse), P(blob), P(ws), ws_bytes, None)
+
+
+GOOD = (1, 4, 2, 8, 8, 16, 16)
+
+
+@pytest.mark.parametrize("shape,kw,code", [
+    ((1, 3, 2, 8, 8, 16, 16), {}, fab.FAB_E_INVAL),          # H % Hkv != 0
+    ((1, 4, 2, -1, 8, 16, 16), {}, fab.FAB_E_INVAL),         # negative N
+    ((1, 0, 1, 8, 8, 16, 16), {}, fab.FAB_E_INVAL),          # no heads
+    ((1, 4, 2, 8, 8, 0, 16), {}, fab.FAB_E_INVAL),           # DK = 0
+    ((1, 4, 2, 8, 8, 256, 16), {}, fab.FAB_E_UNSUPPORTED),   # head dim above the kernels' range
+    ((1 << 20, 64, 64, 1024, 1024, 128, 128), {}, fab.FAB_E_UNSUPPORTED),  # beyond 2^31 elements
+    (GOOD, {"mode": 7}, fab.FAB_E_INVAL),
+    (GOOD, {"scale": float("nan")}, fab.FAB_E_INVAL),
+    (GOOD, {"scale": float("inf")}, fab.FAB_E_INVAL),
+    (GOOD, {"q": None}, fab.FAB_E_INVAL),
+    (GOOD, {"d": None}, fab.FAB_E_INVAL),
+    (GOOD, {"blob": None}, fab.FAB_E_INVAL),
+    (GOOD, {"O": FAKE}, fab.FAB_E_INVAL),                    # O without lse
+    (GOOD, {"lse": FAKE}, fab.FAB_E_INVAL),                  # lse without O
+    (GOOD, {"k": FAKE + 4}, fab.FAB_E_ALIGN),
+    (GOOD, {"mask": FAKE + 2}, fab.FAB_E_ALIGN),
+    (GOOD, {"ws": FAKE + 16}, fab.FAB_E_ALIGN),
+    (GOOD, {"ws": None}, fab.FAB_E_WORKSPACE),
+    (GOOD, {"ws_bytes": 16}, fab.FAB_E_WORKSPACE),
+])
+def test_backward_rejects_bad_arguments_before_device_work(shape, kw, code):
+    assert call_bwd(shape, **kw) == code
+    assert fab.lib().fab_last_error().decode() != ""
+
+
+def test_forward_rejects_bad_arguments():
+    L = fab.lib()
+    P = ctypes.c_void_p
+    sh = fab.FabShape(1, 4, 2, 8, 8, 16, 16)
+    rc = L.fab_forward_lse(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), None, 0.5, 0, None, P(FAKE),
+                           P(FAKE), 1 << 30, None)
+    assert rc == fab.FAB_E_INVAL   # O is NULL
+    rc = L.fab_forward_lse(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0.5, 0, P(FAKE),
+                           P(FAKE), None, 0, None)
+    assert rc == fab.FAB_E_WORKSPACE   # a mask needs its block map workspace
+    assert L.fab_blob_layout(None, None, None, None, None) == fab.FAB_E_INVAL

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 CPU oracle.
+
+Bar, per gradient tensor over the unpadded slice: max|gpu - oracle| / max|oracle|
+<= 1e-4 in f32 mode and <= 2e-2 in bf16 mode; blob pads exactly 0; no NaN/inf;
+the exact-zero sets (all-masked query rows, keys no query attends to) exactly 0.
+Small problems are compared element by element against the full oracle; the
+five workloads at full size are compared on sampled rows and keys the oracle
+computes one by one, and through sums that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fab_inputs as fi
+from fab_inputs import Shape, make_qkvd, random_mask, causal_mask, padding64_mask, F16_NEG_INF
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    return torch, torch.device("cuda:0")
+
+
+def fabmod():
+    import exact_attention_backward_fab_amd as fab
+    fab.lib()
+    return fab
+
+
+def to_dev(torch, dev, a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def rel_err(got, ref, den=None):
+    """max|got - ref| / max|ref|; den overrides the denominator (used when ref is
+    identically zero by cancellation, e.g. a single key, where a relative error is
+    undefined and the scale of the other gradients is used instead)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.max(np.abs(got - ref)) if ref.size else 0.0
+    if den is None:
+        den = np.max(np.abs(ref)) if ref.size else 0.0
+    return err / den if den > 0 else err
+
+
+def structural_zeros(s, mask):
+    """Boolean masks of the entries that are zero by structure, not by cancellation:
+    dQ rows of all-masked query rows (every score -inf), and dK/dV rows of keys
+    that no query attends to."""
+    dead_rows = np.zeros(s.N, bool)
+    dead_keys = np.zeros(s.M, bool) if s.N > 0 else np.ones(s.M, bool)
+    if mask is not None and s.N > 0 and s.M > 0:
+        inf = mask == F16_NEG_INF
+        dead_rows = inf.all(axis=1)
+        dead_keys = inf.all(axis=0)
+    return dead_rows, dead_keys
+
+
+def run_gpu(torch, dev, s, q, k, v, d, mask, scale, mode, with_o_lse=False):
+    fab = fabmod()
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    tm = to_dev(torch, dev, mask)
+    fs = fab.Shape(*s.astuple())
+    O = lse = None
+    if with_o_lse:
+        O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode=mode)
+    total = fab.blob_layout(fs)[3]
+    blob = torch.full((total + 64,), float("nan"), dtype=torch.float32, device=dev)  # guard band after
+    fab.backward(t[0], t[1], t[2], t[3], scale, mask=tm, mode=mode, O=O, lse=lse, blob=blob[:total]
+                 if total else blob[:4])
+    torch.cuda.synchronize()
+    out = blob.cpu().numpy()
+    assert np.all(np.isnan(out[total:])), "write past the end of the blob"
+    return out[:total]
+
+
+def check_blob(s, blob, ref, mode, tag="", mask=None):
+    """ref: dict with dq, dk, dv (oracle, f64)."""
+    fab = fabmod()
+    _, off_k, off_v, total = fab.blob_layout(fab.Shape(*s.astuple()))
+    nq, nk, nv = ref["dq"].size, ref["dk"].size, ref["dv"].size
+    assert np.all(np.isfinite(blob)), f"{tag}: non-finite values in the blob"
+    assert np.all(blob[nq:off_k] == 0) and np.all(blob[off_k + nk:off_v] == 0) and \
+        np.all(blob[off_v + nv:total] == 0), f"{tag}: pads not zero"
+    scale_all = max(float(np.max(np.abs(ref[n]))) if ref[n].size else 0.0 for n in ("dq", "dk", "dv"))
+    dead_rows, dead_keys = structural_zeros(s, mask)
+    errs = {}
+    for name, lo, n in (("dq", 0, nq), ("dk", off_k, nk), ("dv", off_v, nv)):
+        got = blob[lo:lo + n].reshape(ref[name].shape)
+        den = None if (ref[name].size and np.max(np.abs(ref[name])) > 0) else scale_all
+        errs[name] = rel_err(got, ref[name], den)
+        # zeros by structure are exact zeros in the GPU result too
+        z = got[:, :, dead_rows, :] if name == "dq" else got[:, :, dead_keys, :]
+        assert np.all(z == 0), f"{tag}: {name} non-zero where it is zero by structure"
+        assert np.all(ref[name][:, :, dead_rows if name == "dq" else dead_keys, :] == 0)
+    for name, e in errs.items():
+        assert e <= TOL[mode], f"{tag}: {name} max-rel error {e:.3e} > {TOL[mode]} ({errs})"
+    return errs
+
+
+def oracle_full(s, q, k, v, d, mask, scale):
+    from oracle import oracle as orc
+    return orc.backward(s, q, k, v, mask, d, scale)
+
+
+# ---------------------------------------------------------------- small, full oracle
+
+SMALL = [
+    # name, shape, mask kind, seed
+    ("p3_single_head", Shape(1, 1, 1, 3, 5, 4, 4), None, 11),
+    ("p3_causal", Shape(1, 1, 1, 3, 4, 4, 4), "causal", 12),
+    ("p3_gqa_batch", Shape(2, 4, 2, 2, 3, 4, 4), None, 13),
+    ("p3_packing", Shape(2, 4, 2, 2, 4, 3, 5), None, 31),
+    ("odd_pad_mask", Shape(1, 2, 1, 37, 29, 3, 5), "random", 41),
+    ("ragged_d64_random", Shape(2, 4, 2, 200, 300, 64, 64), "random", 42),
+    ("ragged_d128_causal_gqa", Shape(1, 4, 1, 333, 333, 128, 128), "causal", 43),
+    ("d192_128_padding", Shape(1, 2, 2, 130, 260, 192, 128), "padding", 44),
+    ("d40_72_nomask", Shape(1, 3, 1, 70, 90, 40, 72), None, 45),
+    ("d192_192_random", Shape(1, 2, 1, 65, 97, 192, 192), "random", 46),
+    ("one_key", Shape(1, 2, 1, 17, 1, 16, 16), None, 47),
+    ("one_query", Shape(1, 2, 2, 1, 130, 64, 64), "random", 48),
+    ("workload1", fi.WORKLOADS[1].shape, None, 1),
+]
+
+
+def small_mask(kind, s, seed):
+    if kind is None:
+        return None
+    if kind == "causal":
+        return causal_mask(s.N, s.M)
+    if kind == "padding":
+        m = np.zeros((s.N, s.M), np.uint16)
+        m[:, (3 * s.M) // 4:] = F16_NEG_INF
+        m[::7, :] = F16_NEG_INF
+        return m
+    return random_mask(s.N, s.M, seed, p_inf=0.3, full_rows=2, full_cols=3)
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+@pytest.mark.parametrize("name,s,mkind,seed", SMALL, ids=[c[0] for c in SMALL])
+def test_small_against_full_oracle(torch_dev, name, s, mkind, seed, mode):
+    torch, dev = torch_dev
+    print(f"[parity] {name} {mode} {s}", flush=True)
+    q, k, v, d = make_qkvd(s, seed)
+    mask = small_mask(mkind, s, seed)
+    scale = float(np.float32(1.0 / math.sqrt(s.DK)))
+    ref = oracle_full(s, q, k, v, d, mask, scale)
+    blob = run_gpu(torch, dev, s, q, k, v, d, mask, scale, mode)
+    check_blob(s, blob, ref, mode, tag=f"{name}/{mode}", mask=mask)
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_forward_output_and_lse(torch_dev, mode):
+    torch, dev = torch_dev
+    fab = fabmod()
+    from oracle import oracle as orc
+    s = Shape(2, 4, 2, 150, 170, 64, 96)
+    q, k, v, _ = make_qkvd(s, 61)
+    mask = random_mask(s.N, s.M, 61, p_inf=0.3, full_rows=2, full_cols=2)
+    scale = 0.125
+    O_ref, lse_ref = orc.forward(s, q, k, v, mask, scale)
+    O, lse = fab.forward_lse(to_dev(torch, dev, q), to_dev(torch, dev, k), to_dev(torch, dev, v), scale,
+                             mask=to_dev(torch, dev, mask), mode=mode)
+    O, lse = O.cpu().numpy(), lse.cpu().numpy()
+    assert rel_err(O, O_ref) <= TOL[mode]
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isneginf(lse), ~fin)
+    assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= (1e-5 if mode == "f32" else 2e-2)
+    dead = ~fin   # (B,H,N)
+    for b in range(s.B):
+        for h in range(s.H):
+            assert np.all(O[b, dead[b, h], h, :] == 0)
+
+
+def test_route_agreement_supplied_vs_recomputed_forward(torch_dev):
+    # the ggmlR test's "two routes agree to 1e-5" check, for O/LSE supplied by the
+    # caller vs recomputed inside the backward
+    torch, dev = torch_dev
+    s = Shape(1, 4, 2, 190, 210, 64, 64)
+    q, k, v, d = make_qkvd(s, 71)
+    mask = random_mask(s.N, s.M, 71, p_inf=0.2, full_rows=1, full_cols=1)
+    a = run_gpu(torch, dev, s, q, k, v, d, mask, 0.125, "f32", with_o_lse=False)
+    b = run_gpu(torch, dev, s, q, k, v, d, mask, 0.125, "f32", with_o_lse=True)
+    assert rel_err(a, b) <= 1e-5
+
+
+def test_d_ones_closed_form_on_gpu(torch_dev):
+    # d = ones: every component of dV[:, m] equals the summed attention weight of key m
+    torch, dev = torch_dev
+    s = Shape(2, 4, 2, 96, 128, 32, 48)
+    q, k, v, _ = make_qkvd(s, 32)
+    d = np.ones(s.d_shape, np.float32)
+    blob = run_gpu(torch, dev, s, q, k, v, d, None, 1 / math.sqrt(s.DK), "f32")
+    fab = fabmod()
+    _, off_k, off_v, _ = fab.blob_layout(fab.Shape(*s.astuple()))
+    dv = blob[off_v:off_v + s.DV * s.M * s.Hkv * s.B].reshape(s.v_shape)
+    assert np.max(np.abs(dv - dv[..., :1])) <= 1e-5 * np.max(np.abs(dv))
+    rk2 = s.H // s.Hkv
+    assert np.allclose(dv[..., 0].sum(axis=2), rk2 * s.N, rtol=1e-4)
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_all_masked_everything_gives_zero_blob(torch_dev, mode):
+    torch, dev = torch_dev
+    s = Shape(1, 2, 1, 40, 70, 32, 32)
+    q, k, v, d = make_qkvd(s, 81)
+    mask = np.full((s.N, s.M), F16_NEG_INF, np.uint16)
+    blob = run_gpu(torch, dev, s, q, k, v, d, mask, 0.2, mode)
+    assert np.all(blob == 0)
+
+
+@pytest.mark.parametrize("s", [Shape(1, 2, 1, 0, 5, 8, 8), Shape(1, 2, 1, 5, 0, 8, 8),
+                               Shape(0, 2, 1, 5, 5, 8, 8)], ids=["N0", "M0", "B0"])
+def test_empty_extents(torch_dev, s):
+    torch, dev = torch_dev
+    q, k, v, d = make_qkvd(s, 3)
+    blob = run_gpu(torch, dev, s, q, k, v, d, None, 0.3, "f32")
+    assert np.all(blob == 0)
+
+
+# ---------------------------------------------------------------- the five workloads at full size
+
+_cache = {}
+
+
+def workload(wid):
+    if wid not in _cache:
+        _cache[wid] = fi.workload_inputs(wid)
+    return _cache[wid]
+
+
+def sample_ids(s, wid, rng):
+    """Rows (n + N*(h + H*b)) and keys (m + M*(g + Hkv*b)) the oracle evaluates one by one."""
+    R = s.B * s.H * s.N
+    rows = list(rng.choice(R, 24, replace=False)) + [0, R - 1]
+    if wid in (3, 4):
+        # causal: a key is seen by the queries at or after it; keys near the end keep
+        # the oracle cheap, plus a few spread ones for the smaller workload
+        lo = s.M - (256 if wid == 4 else 1024)
+        keys = []
+        for gb in rng.choice(s.Hkv * s.B, 3, replace=False):
+            for m in rng.choice(np.arange(lo, s.M), 4, replace=False):
+                keys.append(int(m + s.M * gb))
+        if wid == 3:
+            keys.append(int(5 + s.M * 1))
+    else:
+        keys = []
+        for gb in rng.choice(s.Hkv * s.B, 3, replace=False):
+            for m in rng.choice(s.M, 5, replace=False):
+                keys.append(int(m + s.M * gb))
+        keys.append(int(s.M - 1))   # beyond the padding cut for workload 5: exactly zero
+    return np.array(rows, dtype=np.int64), np.array(keys, dtype=np.int64)
+
+
+WL_CASES = [(1, "f32"), (2, "f32"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (5, "f32"), (5, "bf16")]
+
+
+@pytest.mark.parametrize("wid,mode", WL_CASES, ids=[f"w{w}-{m}" for w, m in WL_CASES])
+def test_workload_full_size(torch_dev, wid, mode):
+    torch, dev = torch_dev
+    from oracle import oracle as orc
+    s, q, k, v, d, mask, scale = workload(wid)
+    print(f"[parity] workload {wid} {mode} {s}", flush=True)
+    fab = fabmod()
+    fs = fab.Shape(*s.astuple())
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    tm = to_dev(torch, dev, mask)
+    # the benchmark's configuration: O and LSE from the forward, then the backward
+    O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode=mode)
+    blob = fab.backward(t[0], t[1], t[2], t[3], scale, mask=tm, mode=mode, O=O, lse=lse)
+    torch.cuda.synchronize()
+    blob = blob.cpu().numpy()
+    _, off_k, off_v, total = fab.blob_layout(fs)
+    nq, nk, nv = q.size, k.size, v.size
+    assert np.all(np.isfinite(blob))
+    assert np.all(blob[nq:off_k] == 0) and np.all(blob[off_k + nk:off_v] == 0) and np.all(blob[off_v + nv:] == 0)
+    dq = blob[:nq].reshape(s.q_shape)
+    dk = blob[off_k:off_k + nk].reshape(s.k_shape)
+    dv = blob[off_v:off_v + nv].reshape(s.v_shape)
+    tol = TOL[mode]
+
+    dead_rows, dead_keys = structural_zeros(s, mask)
+    assert np.all(dq[:, :, dead_rows, :] == 0)
+    assert np.all(dk[:, :, dead_keys, :] == 0) and np.all(dv[:, :, dead_keys, :] == 0)
+    if wid in (1, 2):
+        ref = orc.backward(s, q, k, v, mask, d, scale)
+        for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            e = rel_err(got, ref[name])
+            print(f"  {name} max-rel {e:.3e}", flush=True)
+            assert e <= tol, name
+        return
+
+    rng = np.random.default_rng(100 + wid)
+    rows, keys = sample_ids(s, wid, rng)
+    rdq, rdk, rdv = orc.backward_sampled(s, q, k, v, mask, d, scale, rows, keys)
+    gdq = np.stack([dq[r // (s.N * s.H), (r // s.N) % s.H, r % s.N] for r in rows])
+    gdk = np.stack([dk[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
+    gdv = np.stack([dv[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
+    for name, got, ref in (("dq", gdq, rdq), ("dk", gdk, rdk), ("dv", gdv, rdv)):
+        e = rel_err(got, ref)
+        print(f"  sampled {name} max-rel {e:.3e}", flush=True)
+        assert e <= tol, name
+
+    # sums that hold at any size: a common shift of all keys leaves every softmax row
+    # unchanged, so sum_m dK[:, m] = 0; and sum_m dV[:, m] = sum of d over the live
+    # query rows of the group
+    live = None
+    if mask is not None:
+        live = np.array([np.any(mask[n] != F16_NEG_INF) for n in range(s.N)])
+    rk2 = s.H // s.Hkv
+    dk_sum = dk.astype(np.float64).sum(axis=2)
+    dk_abs = np.abs(dk.astype(np.float64)).sum(axis=2)
+    assert np.max(np.abs(dk_sum) / np.maximum(dk_abs, 1e-30)) <= tol
+    d64 = d.astype(np.float64)
+    if live is not None:
+        d64 = d64 * live[None, :, None, None]
+    expect = d64.sum(axis=1).reshape(s.B, s.Hkv, rk2, s.DV).sum(axis=2)
+    got = dv.astype(np.float64).sum(axis=2)
+    assert np.max(np.abs(got - expect)) <= tol * np.max(np.abs(dv.astype(np.float64)).sum(axis=2))
+    if wid == 5:
+        # keys past the padding cut and all-masked query rows are exactly zero
+        assert np.all(dk[:, :, 3072:] == 0) and np.all(dv[:, :, 3072:] == 0)
+        assert np.all(dq[:, :, ::64, :] == 0)
