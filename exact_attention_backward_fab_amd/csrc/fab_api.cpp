@@ -39,7 +39,8 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_lse, ws_O, ws_delta, ws_pk, ws_pv, ws_bytes;
+    size_t ws_map, ws_lse, ws_O, ws_delta, ws_o16, ws_pk, ws_pv, ws_bytes;
+    int dvp;  // padded value head dim of the kernels
     bool gqa;
 };
 
@@ -79,10 +80,13 @@ int check_shape(const fab_shape *s, Plan *pl)
     pl->total = pl->off_v + pad4(pl->nv);
     if ((double)pl->total > kMaxElems) return fail(FAB_E_UNSUPPORTED, "result blob exceeds 2^31-1 floats");
     pl->gqa = s->H > s->Hkv;
+    fab::HeadDims hd;
+    if (!fab::pick_head_dims((int)s->DK, (int)s->DV, &hd)) return fail(FAB_E_UNSUPPORTED, "head dims");
+    pl->dvp = hd.dv;
     return FAB_OK;
 }
 
-void plan_workspace(Plan *pl, int has_mask, int have_o_lse)
+void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
 {
     const fab::Dims &d = pl->d;
     size_t off = 0;
@@ -98,6 +102,8 @@ void plan_workspace(Plan *pl, int has_mask, int have_o_lse)
     }
     pl->ws_delta = off;
     off = align_up(off + sizeof(float) * (size_t)pl->nrow);
+    pl->ws_o16 = off;
+    if (mode == FAB_MODE_BF16) off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);  // bf16 d
     pl->ws_pk = off;
     pl->ws_pv = off;
     if (pl->gqa) {
@@ -287,7 +293,7 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     FAB_TRY(check_shape(shape, &pl));
     FAB_TRY(check_mode(mode));
     if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
-    plan_workspace(&pl, has_mask != 0, have_o_lse != 0);
+    plan_workspace(&pl, mode, has_mask != 0, have_o_lse != 0);
     *bytes = pl.ws_bytes;
     return FAB_OK;
 }
@@ -308,7 +314,7 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     FAB_TRY(check_ptr(lse, pl.nrow, "lse"));
     if (mask && !aligned16(mask)) return fail(FAB_E_ALIGN, "mask is not 16-byte aligned");
     const bool use_mask = mask && (int64_t)pl.d.M * pl.d.N > 0;
-    plan_workspace(&pl, use_mask, 1);
+    plan_workspace(&pl, mode, use_mask, 1);
     const size_t need = use_mask ? pl.ws_map + (size_t)((pl.d.N + 31) / 32) * ((pl.d.M + 31) / 32) : 0;
     FAB_TRY(check_ws(ws, ws_bytes, need));
     if (pl.nrow == 0) return FAB_OK;  // no query rows: nothing to write
@@ -346,7 +352,7 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     FAB_TRY(check_ptr(blob, pl.total, "blob"));
     if (mask && !aligned16(mask)) return fail(FAB_E_ALIGN, "mask is not 16-byte aligned");
     const bool use_mask = mask && (int64_t)pl.d.M * pl.d.N > 0;
-    plan_workspace(&pl, use_mask, have);
+    plan_workspace(&pl, mode, use_mask, have);
     const bool empty = pl.d.B == 0 || pl.d.N == 0 || pl.d.M == 0;
     FAB_TRY(check_ws(ws, ws_bytes, empty ? 0 : pl.ws_bytes));
     if (pl.total == 0) return FAB_OK;
@@ -371,12 +377,14 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
         lseu = lw;
     }
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
-    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.nq, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
+    __bf16 *dO16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
+    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, dO16, pl.dvp, pl.off_k, pl.nk, pl.off_v, pl.nv,
+                                       pl.total, pl.d, s),
                "prep launch");
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
-    FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, mk, map, lseu, delta, scale, bf16, blob, dk, dv, pl.gqa ? 1 : 0,
-                                          pl.d, s),
+    FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, dO16, mk, map, lseu, delta, scale, bf16, blob, dk, dv,
+                                          pl.gqa ? 1 : 0, pl.d, s),
                "backward launch");
     if (pl.gqa) {
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, pl.d.DK, pl.d, s), "dK reduce launch");

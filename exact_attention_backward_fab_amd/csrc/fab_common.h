@@ -17,8 +17,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Block-map classes of a 32x32 (query x key) block of the additive mask.
-enum : uint8_t { kBlockSkip = 0, kBlockFree = 1, kBlockMixed = 2 };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Block map of the additive mask, one byte per 32x32 (query x key) block:
+// bits 0-1 the block class, bit 2 set when every entry of the block equals the
+// causal rule (0 where key <= query, -inf elsewhere).
+enum : uint8_t { kBlockSkip = 0, kBlockFree = 1, kBlockMixed = 2, kBlockCausalBit = 4 };
+// Classes of a kernel tile (a rectangle of map blocks).
+enum : int { kTileSkip = 0, kTileFree = 1, kTileMixed = 2, kTileCausal = 3 };
 constexpr int kMapTile = 32;
 
 // ---------------------------------------------------------------- MFMA
@@ -66,6 +73,101 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4 &x)
     return r;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j addresses 4 consecutive 16-bit elements; lane i then receives, in
+// slot k, element (i & 3) of the 4 read by lane 4k + (i >> 2).  When lane j of
+// the group points at row r0 + (j >> 2), column c0 + 4 (j & 3) of a row-major
+// matrix X, lane i receives X[r0 + k][c0 + i] for k = 0..3: four consecutive
+// rows of one column, the operand shape of a matrix-core B (or A) fragment.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16 *p)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Matrix-core operand of 8 bf16 for the lane's column c0 + (l & 31) of a
+// row-major LDS matrix X (leading dimension ld): rows r0..r0+3 in slots 0-3 and
+// r0+dr..r0+dr+3 in slots 4-7.
+__device__ __forceinline__ bf16x8 lds_col8(const __bf16 *X, int ld, int r0, int dr, int c0, int lane)
+{
+    const int j = lane & 15, grp = (lane >> 4) & 1;
+    const __bf16 *p = X + (r0 + (j >> 2)) * ld + c0 + 16 * grp + 4 * (j & 3);
+    const bf16x4 lo = lds_read_tr16(p);
+    const bf16x4 hi = lds_read_tr16(p + dr * ld);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- buffer access
+// Raw buffer resources: accesses past num_bytes read as zero and writes or
+// atomics past it are dropped by the hardware, so tiles that run over the end
+// of a (batch, head) slice need no bounds checks.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, num_bytes, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ void buf_atomic_add_f32(rsrc_t r, uint32_t byte_off, float v)
+{
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS tile layouts
+// Row-major bf16 tiles in LDS.  Rows of 128 elements (256 bytes) use an XOR
+// swizzle of their 16-byte chunks, chunk' = chunk ^ (4 (row & 3) + ((row >> 2) & 3)),
+// which keeps both access patterns of these tiles free of bank conflicts: 16
+// consecutive rows reading the same chunk (row-per-lane 16-byte reads), and 4
+// consecutive rows x 4 consecutive chunks (transposing reads).  Other widths
+// pad each row by 16 bytes instead.
+template <int D>
+struct RowTile {
+    static constexpr bool kSwizzle = (D == 128);
+    static constexpr int kLd = kSwizzle ? D : D + 8;  // elements per row
+    // element offset of (row, col); col is a multiple of 4
+    __device__ static __forceinline__ int off(int row, int col)
+    {
+        if constexpr (kSwizzle) {
+            const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+            return row * kLd + ((((col >> 3) ^ sw)) << 3) + (col & 7);
+        } else {
+            return row * kLd + col;
+        }
+    }
+};
+
+// Matrix-core operand of 8 bf16 for the lane's column c0 + (lane & 31) of a
+// row-major LDS tile: rows r0..r0+3 in slots 0-3, rows r0+dr..r0+dr+3 in slots 4-7.
+template <typename Layout>
+__device__ __forceinline__ bf16x8 tile_col8(const __bf16 *X, int r0, int dr, int c0, int lane)
+{
+    const int j = lane & 15, grp = (lane >> 4) & 1;
+    const int col = c0 + 16 * grp + 4 * (j & 3);
+    const bf16x4 lo = lds_read_tr16(X + Layout::off(r0 + (j >> 2), col));
+    const bf16x4 hi = lds_read_tr16(X + Layout::off(r0 + dr + (j >> 2), col));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// dS^T tile [key][query] with BR = 32 queries per row (64 bytes): chunk' = chunk ^ ((row >> 2) & 3).
+struct StTile {
+    static constexpr int kLd = 32;
+    __device__ static __forceinline__ int off(int row, int col)
+    {
+        return row * kLd + ((((col >> 3) ^ ((row >> 2) & 3))) << 3) + (col & 7);
+    }
+};
+
 // ---------------------------------------------------------------- loads
 // Four consecutive floats row[c..c+3] of a row of length D; entries at or past
 // D read as 0.  vec: D % 4 == 0 and the row start is 16-byte aligned.
@@ -96,5 +198,27 @@ __device__ __forceinline__ float group_sum(float x, int width)
 
 __device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// Class of a kernel tile made of nq x nk map blocks starting at (qb0, kb0):
+// SKIP if every block is all -inf, FREE if every block is all zero, CAUSAL if
+// every block follows the causal rule exactly, MIXED otherwise.  A NULL map
+// (no mask) is FREE.
+__device__ __forceinline__ int tile_class(const uint8_t *map, int nqb, int nkb, int qb0, int nq,
+                                          int kb0, int nk)
+{
+    if (!map) return kTileFree;
+    bool all_skip = true, all_free = true, all_causal = true;
+    const int qe = min(qb0 + nq, nqb), ke = min(kb0 + nk, nkb);
+    for (int i = qb0; i < qe; ++i)
+        for (int j = kb0; j < ke; ++j) {
+            const uint8_t c = map[i * nkb + j];
+            all_skip = all_skip && ((c & 3) == kBlockSkip);
+            all_free = all_free && ((c & 3) == kBlockFree);
+            all_causal = all_causal && ((c & kBlockCausalBit) != 0);
+        }
+    if (all_skip) return kTileSkip;
+    if (all_free) return kTileFree;
+    return all_causal ? kTileCausal : kTileMixed;
+}
 
 }  // namespace fab

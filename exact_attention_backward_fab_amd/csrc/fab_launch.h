@@ -11,9 +11,39 @@ struct Dims {
     int B, H, Hkv, N, M, DK, DV;
 };
 
-// Padded head dimensions the kernels are instantiated for.
-int padded_dim(int d);                 // 32, 64, 128 or 192; 0 if unsupported
-bool bwd_supported(int dkp, int dvp, int bf16);
+// Padded head dimensions (DKP, DVP) the kernels are instantiated for; a shape
+// uses the first pair that covers both of its head dims.
+struct HeadDims {
+    int dk, dv;
+};
+constexpr HeadDims kHeadDims[] = {{32, 32}, {64, 64}, {128, 128}, {192, 128}, {192, 192}};
+
+inline bool pick_head_dims(int DK, int DV, HeadDims *out)
+{
+    for (const HeadDims &h : kHeadDims)
+        if (DK <= h.dk && DV <= h.dv) {
+            *out = h;
+            return true;
+        }
+    return false;
+}
+
+// Calls FN<DKP, DVP, BF16>(ARGS, STREAM) for the instantiated pair HD and
+// returns its result.
+#define FAB_DISPATCH_HEAD_DIMS(FN, ARGS, STREAM, HD, BF)                                           \
+    do {                                                                                          \
+        if ((HD).dk == 32 && (HD).dv == 32)                                                       \
+            return (BF) ? FN<32, 32, true>(ARGS, STREAM) : FN<32, 32, false>(ARGS, STREAM);       \
+        if ((HD).dk == 64 && (HD).dv == 64)                                                       \
+            return (BF) ? FN<64, 64, true>(ARGS, STREAM) : FN<64, 64, false>(ARGS, STREAM);       \
+        if ((HD).dk == 128 && (HD).dv == 128)                                                     \
+            return (BF) ? FN<128, 128, true>(ARGS, STREAM) : FN<128, 128, false>(ARGS, STREAM);   \
+        if ((HD).dk == 192 && (HD).dv == 128)                                                     \
+            return (BF) ? FN<192, 128, true>(ARGS, STREAM) : FN<192, 128, false>(ARGS, STREAM);   \
+        if ((HD).dk == 192 && (HD).dv == 192)                                                     \
+            return (BF) ? FN<192, 192, true>(ARGS, STREAM) : FN<192, 192, false>(ARGS, STREAM);   \
+        return hipErrorInvalidValue;                                                              \
+    } while (0)
 
 // Block map of the additive mask: u8 [ceil(N/32)][ceil(M/32)].
 hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, hipStream_t s);
@@ -23,17 +53,19 @@ hipError_t launch_forward(const float *q, const float *k, const float *v, const 
                           const uint8_t *map, float scale, int bf16, float *O, float *lse,
                           const Dims &d, hipStream_t s);
 
-// Delta = rowsum(d o O) [N,H,B]; zero the dQ slice [0, nq) and the blob pads.
-hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, int64_t nq,
-                       int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total,
+// Delta = rowsum(d o O) [N,H,B]; zero the dQ slice [0, off_k) and the blob
+// pads; when dO16 is given, also write d as bf16 [B][H][N][dvp] (zero-padded).
+hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, __bf16 *dO16,
+                       int dvp, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total,
                        const Dims &d, hipStream_t s);
 
-// KV-block-outer backward: dV, dK per key tile (stored into dk/dv with
+// Key-block-outer backward: dV, dK per key tile (stored into dk/dv with
 // per-query-head layout when part_heads != 0), dQ by f32 atomics into dq.
+// bf16 mode reads dO from dO16 (see launch_prep); f32 mode from dO.
 hipError_t launch_backward(const float *q, const float *k, const float *v, const float *dO,
-                           const uint16_t *mask, const uint8_t *map, const float *lse,
-                           const float *delta, float scale, int bf16, float *dq, float *dk,
-                           float *dv, int part_heads, const Dims &d, hipStream_t s);
+                           const __bf16 *dO16, const uint16_t *mask, const uint8_t *map,
+                           const float *lse, const float *delta, float scale, int bf16, float *dq,
+                           float *dk, float *dv, int part_heads, const Dims &d, hipStream_t s);
 
 // dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] for one of dK / dV.
 hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s);
