@@ -35,7 +35,7 @@ FAB_E_HIP = -5
 EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
            "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
            "fab_strerror", "fab_last_error", "fab_version")
-KERNELS = ("block_map", "forward", "prep", "backward", "gqa_reduce")
+KERNELS = ("block_map", "forward", "prep", "pack", "backward", "dq", "gqa_reduce")
 
 
 class FabShape(ctypes.Structure):

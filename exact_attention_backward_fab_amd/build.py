@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libfab.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fab_aux.hip", "fab_fwd.hip", "fab_bwd.hip", "fab_api.cpp"]
+SOURCES = ["fab_aux.hip", "fab_fwd.hip", "fab_bwd.hip", "fab_qouter.hip", "fab_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-munsafe-fp-atomics",

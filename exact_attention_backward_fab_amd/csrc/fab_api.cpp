@@ -39,8 +39,9 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_lse, ws_O, ws_delta, ws_o16, ws_pk, ws_pv, ws_bytes;
-    int dvp;  // padded value head dim of the kernels
+    size_t ws_map, ws_lse, ws_O, ws_delta, ws_o16, ws_k16, ws_v16, ws_pk, ws_pv, ws_bytes;
+    int dkp, dvp;  // padded head dims of the kernels
+    int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
 };
 
@@ -82,7 +83,9 @@ int check_shape(const fab_shape *s, Plan *pl)
     pl->gqa = s->H > s->Hkv;
     fab::HeadDims hd;
     if (!fab::pick_head_dims((int)s->DK, (int)s->DV, &hd)) return fail(FAB_E_UNSUPPORTED, "head dims");
+    pl->dkp = hd.dk;
     pl->dvp = hd.dv;
+    pl->mp = (int)((s->M + fab::kPackRows - 1) / fab::kPackRows * fab::kPackRows);
     return FAB_OK;
 }
 
@@ -103,7 +106,16 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     pl->ws_delta = off;
     off = align_up(off + sizeof(float) * (size_t)pl->nrow);
     pl->ws_o16 = off;
-    if (mode == FAB_MODE_BF16) off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);  // bf16 d
+    pl->ws_k16 = off;
+    pl->ws_v16 = off;
+    if (mode == FAB_MODE_BF16) {
+        const size_t kvrows = (size_t)pl->mp * d.Hkv * d.B;
+        off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);  // bf16 d
+        pl->ws_k16 = off;
+        off = align_up(off + 2 * kvrows * pl->dkp);             // bf16 K
+        pl->ws_v16 = off;
+        off = align_up(off + 2 * kvrows * pl->dvp);             // bf16 V
+    }
     pl->ws_pk = off;
     pl->ws_pv = off;
     if (pl->gqa) {
@@ -156,8 +168,8 @@ int hip_fail(hipError_t e, const char *what)
     } while (0)
 
 // ---------------------------------------------------------------- measurement hooks
-enum Kid { kMap = 0, kFwd, kPrep, kBwd, kRed, kNumKid };
-const char *const kKidNames[kNumKid] = {"block_map", "forward", "prep", "backward", "gqa_reduce"};
+enum Kid { kMap = 0, kFwd, kPrep, kBwd, kRed, kPack, kDq, kNumKid };
+const char *const kKidNames[kNumKid] = {"block_map", "forward", "prep", "backward", "gqa_reduce", "pack", "dq"};
 
 struct ProfRec {
     int kid;
@@ -378,14 +390,29 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     }
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
     __bf16 *dO16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
-    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, dO16, pl.dvp, pl.off_k, pl.nk, pl.off_v, pl.nv,
-                                       pl.total, pl.d, s),
+    // bf16: dQ is written once by the query-block-outer kernel (only its pad is
+    // zeroed); f32: dQ is accumulated by atomics into a zeroed slice
+    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, dO16, pl.dvp, bf16 ? pl.nq : 0, pl.off_k, pl.nk,
+                                       pl.off_v, pl.nv, pl.total, pl.d, s),
                "prep launch");
+    __bf16 *k16 = nullptr, *v16 = nullptr;
+    if (bf16) {
+        k16 = reinterpret_cast<__bf16 *>(wsb + pl.ws_k16);
+        v16 = reinterpret_cast<__bf16 *>(wsb + pl.ws_v16);
+        const int64_t heads = (int64_t)pl.d.Hkv * pl.d.B;
+        FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(k, k16, heads, pl.d.M, pl.mp, pl.d.DK, pl.dkp, s),
+                   "K pack launch");
+        FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(v, v16, heads, pl.d.M, pl.mp, pl.d.DV, pl.dvp, s),
+                   "V pack launch");
+    }
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, dO16, mk, map, lseu, delta, scale, bf16, blob, dk, dv,
                                           pl.gqa ? 1 : 0, pl.d, s),
                "backward launch");
+    if (bf16)
+        FAB_LAUNCH(kDq, fab::launch_dq(q, k16, v16, dO16, mk, map, lseu, delta, scale, blob, pl.mp, pl.d, s),
+                   "dQ launch");
     if (pl.gqa) {
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, pl.d.DK, pl.d, s), "dK reduce launch");
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dv, blob + pl.off_v, pl.d.DV, pl.d, s), "dV reduce launch");

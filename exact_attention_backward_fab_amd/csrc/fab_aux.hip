@@ -65,7 +65,7 @@ struct PrepArgs {
     const float *dO, *O;
     float *delta, *blob;
     __bf16 *dO16;                     // bf16 copy [B][H][N][DVP], or NULL
-    int64_t zero_end;                 // zero blob[0, zero_end): the dQ slice and its pad
+    int64_t zero_lo, zero_hi;         // zero blob[zero_lo, zero_hi): the dQ slice (or its pad)
     int64_t pad1_lo, pad1_hi, pad2_lo, pad2_hi;
     int rows, DV, DVP, N, H, lpr_log2, vec;
 };
@@ -95,10 +95,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
         acc = group_sum(acc, lpr);
         if (sub == 0) a.delta[n + a.N * (h + a.H * b)] = acc;
     }
-    // zero the dQ slice (and its pad) for the atomics, and the two other pads
-    const int64_t n4 = a.zero_end / 4;
+    // zero the dQ slice for the atomics (or only its pad), and the two other pads
+    const int64_t z4 = (a.zero_lo + 3) / 4, n4 = a.zero_hi / 4;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t j = gtid; j < n4; j += nthr) reinterpret_cast<f32x4 *>(a.blob)[j] = z;
+    for (int64_t j = z4 + gtid; j < n4; j += nthr) reinterpret_cast<f32x4 *>(a.blob)[j] = z;
+    if (gtid < 4 && a.zero_lo + gtid < 4 * z4 && a.zero_lo + gtid < a.zero_hi) a.blob[a.zero_lo + gtid] = 0.f;
     if (gtid < 4) {
         if (a.pad1_lo + gtid < a.pad1_hi) a.blob[a.pad1_lo + gtid] = 0.f;
         if (a.pad2_lo + gtid < a.pad2_hi) a.blob[a.pad2_lo + gtid] = 0.f;
@@ -143,12 +144,13 @@ hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, h
 }
 
 hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, __bf16 *dO16,
-                       int dvp, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total,
-                       const Dims &d, hipStream_t s)
+                       int dvp, int64_t zero_lo, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
+                       int64_t total, const Dims &d, hipStream_t s)
 {
     PrepArgs a;
     a.dO = dO; a.O = O; a.delta = delta; a.blob = blob; a.dO16 = dO16;
-    a.zero_end = off_k;  // off_k = pad4(nq), a multiple of 4
+    a.zero_lo = zero_lo;
+    a.zero_hi = off_k;  // off_k = pad4(nq), a multiple of 4
     a.pad1_lo = off_k + nk; a.pad1_hi = off_v;
     a.pad2_lo = off_v + nv; a.pad2_hi = total;
     a.rows = d.B * d.N * d.H;
@@ -157,7 +159,7 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
     int lpr = 1, lg = 0;
     while (lpr * 4 < a.DVP && lpr < 64) { lpr *= 2; ++lg; }
     a.lpr_log2 = lg;
-    const int64_t work = std::max<int64_t>((int64_t)a.rows * lpr, off_k / 4);
+    const int64_t work = std::max<int64_t>((int64_t)a.rows * lpr, (off_k - zero_lo) / 4);
     int grid = (int)std::min<int64_t>((work + 255) / 256, 4096);
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), 0, s, a);

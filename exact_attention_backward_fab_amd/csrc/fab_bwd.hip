@@ -6,17 +6,19 @@
 // query tile it recomputes S = scale Q K^T (+ mask) and P = exp(S - LSE) from
 // the row log-sum-exp of the forward, then forms, as in the labml "Flash
 // Attention" page ("Backward pass"):
-//     dV += P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dK += scale dS^T Q,
-//     dQ += scale dS K   (f32 atomics into the result blob: every key block
-//                         of the head adds its share)
-// with D = rowsum(dO o O) from the prep kernel.  All five products run on the
+//     dV += P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dK += scale dS^T Q
+// with D = rowsum(dO o O) from the prep kernel.  The products run on the
 // matrix cores: bf16 operands with f32 accumulation (v_mfma_f32_32x32x16_bf16)
 // or f32 operands (v_mfma_f32_32x32x2_f32).
 //
+// dQ = scale dS K: in bf16 mode a separate query-block-outer kernel
+// (fab_qouter.hip) recomputes S and dP by query blocks and writes each dQ row
+// once; in f32 mode this kernel adds every key block's share with f32 atomics
+// into the result blob.
+//
 // Wave layout: wave w owns keys 32w..32w+31 of the block.  S and dP come out of
 // the matrix core with one key per lane (the C layout, see fab_common.h), which
-// is exactly the A-operand layout of P^T and dS^T for dV and dK; only dQ needs
-// dS transposed, which goes through LDS.
+// is exactly the A-operand layout of P^T and dS^T for dV and dK.
 #include <algorithm>
 
 #include "fab_common.h"
@@ -47,8 +49,6 @@ struct B16Cfg {
     static constexpr int QCN = BR * DKP / 4, OCN = BR * DVP / 8;   // 16-byte chunks of a Q / dO tile
     static constexpr int QCH = (QCN + NT - 1) / NT;   // f32x4 chunks of a Q tile per thread
     static constexpr int OCH = (OCN + NT - 1) / NT;   // 16-byte chunks of a bf16 dO tile per thread
-    static constexpr int ND = DKP / 32;               // 32-wide dQ tiles along the head dim
-    static constexpr int MAXT = (ND + W - 1) / W;     // dQ tiles per wave
     static constexpr int LIST = 2048;                 // live query tiles listed at a time
 };
 
@@ -61,7 +61,7 @@ struct B16Tile {
 
 // Per-(batch, head) views of the query-side tensors.
 struct B16Head {
-    rsrc_t q, o, lse, del, dq;
+    rsrc_t q, o, lse, del;
     const float *qp;   // plain pointer to Q for the head-dim-padded (checked) loads
 };
 
@@ -123,12 +123,12 @@ __device__ __forceinline__ void b16_store(const B16Tile<DKP, DVP> &t, __bf16 *sQ
     }
 }
 
-// One query tile against the key block: S, dP, P, dS, dS^T to LDS, dV and dK.
+// One query tile against the key block: S, dP, P, dS, dV and dK.
 // The causal rule is applied as "query >= thr" (thr = INT_MIN when the tile
 // is not causal); masked adds the additive mask values read from memory.
 template <int DKP, int DVP>
 __device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, const __bf16 *Ob, const float *sLb,
-                                         const float *sDb, __bf16 *St, const __bf16 *sK, const bf16x8 *vf,
+                                         const float *sDb, const __bf16 *sK, const bf16x8 *vf,
                                          f32x16 *dkacc, f32x16 *dvacc, int q0, int thr, bool masked, int mykey,
                                          float kbias, float sl2, int w, int lane)
 {
@@ -199,12 +199,7 @@ __device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, con
         }
     }
 
-    // ---- dS^T to LDS ([key][query]) for dQ, and the bf16 A operands of dV, dK
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v4 = {pacc[4 * r4], pacc[4 * r4 + 1], pacc[4 * r4 + 2], pacc[4 * r4 + 3]};
-        *reinterpret_cast<bf16x4 *>(&St[StTile::off(32 * w + l32, 8 * r4 + 4 * half)]) = to_bf16x4(v4);
-    }
+    // ---- the bf16 A operands of dV and dK
     bf16x8 pa[2], da[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -254,7 +249,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(16))) __bf16 sK[BC * QL::kLd];         // K block, row-major
     __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BR * QL::kLd];      // Q tiles (double buffer)
     __shared__ __attribute__((aligned(16))) __bf16 sO[2][BR * OL::kLd];      // dO tiles
-    __shared__ __attribute__((aligned(16))) __bf16 sSt[2][BC * StTile::kLd]; // dS^T: [key][query]
     __shared__ __attribute__((aligned(16))) float sL[2][BR];                 // LSE (log2 units)
     __shared__ __attribute__((aligned(16))) float sD[2][BR];                 // D
     __shared__ int sList[C::LIST];                                           // live tiles: 4*index + class
@@ -277,12 +271,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     hd.o = make_rsrc(p.dO16 + hrow * DVP, (uint32_t)(p.N * DVP) * 2u);
     hd.lse = make_rsrc(p.lse + hrow, (uint32_t)p.N * 4u);
     hd.del = make_rsrc(p.delta + hrow, (uint32_t)p.N * 4u);
-    hd.dq = make_rsrc(p.dq + hrow * p.DK, (uint32_t)(p.N * p.DK) * 4u);
     const int nqt = (p.N + BR - 1) / BR;
     const float sl2 = p.scale * kLog2e;
 
-    // ---- the key block: bf16 rows in LDS (B operand of S = Q K^T and of
-    // dQ = dS K), and the B operand of dP = dO V^T in registers (lane = key)
+    // ---- the key block: bf16 rows in LDS (B operand of S = Q K^T), and the B
+    // operand of dP = dO V^T in registers (lane = key)
     for (int c = tid; c < BC * (DKP / 4); c += NT) {
         const int r = c / (DKP / 4), col = 4 * (c % (DKP / 4));
         const int key = key0 + r;
@@ -309,27 +302,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     for (int seg = 0; seg < nqt; seg += C::LIST) {
         // ---- ordered list of the live query tiles of this segment (block map)
-        if (tid == 0) sCount[W] = 0;
-        __syncthreads();
-        for (int c0 = seg; c0 < min(seg + C::LIST, nqt); c0 += NT) {
-            const int it = c0 + tid;
-            int cls = kTileSkip;
-            if (it < min(seg + C::LIST, nqt))
-                cls = tile_class(p.map, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile, key0 / kMapTile,
-                                 BC / kMapTile);
-            const bool live = cls != kTileSkip;
-            const uint64_t ball = __ballot(live);
-            const int before = __popcll(ball & ((1ull << lane) - 1ull));
-            if (lane == 0) sCount[w] = __popcll(ball);
-            __syncthreads();
-            int base = sCount[W];
-            for (int v = 0; v < w; ++v) base += sCount[v];
-            if (live) sList[base + before] = 4 * it + cls;
-            __syncthreads();
-            if (tid == 0) sCount[W] += sCount[0] + sCount[1] + sCount[2] + sCount[3];
-            __syncthreads();
-        }
-        const int count = sCount[W];
+        const int count = build_live_list<W>(sList, sCount, seg, min(seg + C::LIST, nqt), tid, lane, w, [&](int it) {
+            return tile_class(p.map, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile, key0 / kMapTile,
+                              BC / kMapTile);
+        });
         if (count == 0) continue;
 
         // ---- first live tile into buffer 0
@@ -351,46 +327,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             B16Tile<DKP, DVP> nt;
             b16_load<DKP, DVP, EXACT>(nt, hd, (more ? (sList[li + 1] >> 2) : it) * BR, p.N, p.DK, p.vecK, tid);
 
-            __bf16 *St = sSt[buf];
-            b16_step<DKP, DVP>(p, sQ[buf], sO[buf], sL[buf], sD[buf], St, sK, vf, dkacc, dvacc, q0,
+            b16_step<DKP, DVP>(p, sQ[buf], sO[buf], sL[buf], sD[buf], sK, vf, dkacc, dvacc, q0,
                                cls == kTileCausal ? mykey : INT_MIN, cls == kTileMixed, mykey, kbias, sl2, w, lane);
             if (more) b16_store<DKP, DVP>(nt, sQ[buf ^ 1], sO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], tid);
-            __syncthreads();  // dS^T of every wave visible; next tile staged
-
-            // ---- dQ = scale dS K for this wave's 32-query x 32-dim tiles; rows past N
-            // are dropped by the buffer bounds
-            {
-                f32x16 acc[C::MAXT];
-#pragma unroll
-                for (int x = 0; x < C::MAXT; ++x) acc[x] = zero16();
-                bf16x8 a[BC / 16];
-#pragma unroll
-                for (int t = 0; t < BC / 16; ++t) a[t] = tile_col8<StTile>(St, 16 * t + 8 * half, 4, 0, lane);
-#pragma unroll
-                for (int x = 0; x < C::MAXT; ++x) {
-                    const int dt = w + W * x;
-                    if (dt < C::ND) {
-                        bf16x8 bk[BC / 16];
-#pragma unroll
-                        for (int t = 0; t < BC / 16; ++t) bk[t] = tile_col8<QL>(sK, 16 * t + 8 * half, 4, dt * 32, lane);
-#pragma unroll
-                        for (int t = 0; t < BC / 16; ++t) acc[x] = mfma_bf16(a[t], bk[t], acc[x]);
-                    }
-                }
-#pragma unroll
-                for (int x = 0; x < C::MAXT; ++x) {
-                    const int col = (w + W * x) * 32 + l32;
-                    if (w + W * x < C::ND && (EXACT || col < p.DK)) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            buf_atomic_add_f32(hd.dq, (uint32_t)((q0 + crow(r, half)) * p.DK + col) * 4u,
-                                               acc[x][r] * p.scale);
-                    }
-                }
-            }
+            __syncthreads();  // next tile staged; every wave is done with this one
             buf ^= 1;
         }
-        __syncthreads();  // the list is rebuilt for the next segment
     }
 
     // ---- store dK (scaled) and dV of this key block

@@ -125,25 +125,32 @@ __device__ __forceinline__ void buf_atomic_add_f32(rsrc_t r, uint32_t byte_off, 
 }
 
 // ---------------------------------------------------------------- LDS tile layouts
-// Row-major bf16 tiles in LDS.  Rows of 128 elements (256 bytes) use an XOR
-// swizzle of their 16-byte chunks, chunk' = chunk ^ (4 (row & 3) + ((row >> 2) & 3)),
-// which keeps both access patterns of these tiles free of bank conflicts: 16
-// consecutive rows reading the same chunk (row-per-lane 16-byte reads), and 4
-// consecutive rows x 4 consecutive chunks (transposing reads).  Other widths
-// pad each row by 16 bytes instead.
+// Row-major bf16 tiles of D columns, stored without padding; the 16-byte chunks
+// of each row are permuted by an XOR with a function of (row mod 16), chosen so
+// that the two access patterns on these tiles hit distinct LDS banks: 16
+// consecutive rows reading the same chunk (one row per lane, 16-byte reads) and
+// 4 consecutive rows x 4 consecutive chunks (transposing reads).  The same
+// permutation is applied by the bf16 pack kernels to rows in global memory, so
+// a tile can be copied linearly from global memory into LDS.
+//   D = 128 (16 chunks):      chunk ^ (4 (row & 3) + ((row >> 2) & 3))
+//   D = 64, 192 (8k chunks):  within each group of 8: chunk ^ f((row >> 1) & 7),
+//                             f(x) = 4 (x & 1) + (x >> 1)
+//   D = 32 (4 chunks):        chunk ^ ((row >> 2) & 3)
+__host__ __device__ __forceinline__ int swz_chunk(int row, int chunk, int nchunks)
+{
+    if (nchunks == 16) return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    if (nchunks == 4) return chunk ^ ((row >> 2) & 3);
+    const int x = (row >> 1) & 7;
+    return (chunk & ~7) | ((chunk & 7) ^ (((x & 1) << 2) | (x >> 1)));
+}
+
 template <int D>
 struct RowTile {
-    static constexpr bool kSwizzle = (D == 128);
-    static constexpr int kLd = kSwizzle ? D : D + 8;  // elements per row
+    static constexpr int kLd = D;   // elements per row
     // element offset of (row, col); col is a multiple of 4
     __device__ static __forceinline__ int off(int row, int col)
     {
-        if constexpr (kSwizzle) {
-            const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
-            return row * kLd + ((((col >> 3) ^ sw)) << 3) + (col & 7);
-        } else {
-            return row * kLd + col;
-        }
+        return row * kLd + (swz_chunk(row, col >> 3, D / 8) << 3) + (col & 7);
     }
 };
 
@@ -219,6 +226,41 @@ __device__ __forceinline__ int tile_class(const uint8_t *map, int nqb, int nkb, 
     if (all_skip) return kTileSkip;
     if (all_free) return kTileFree;
     return all_causal ? kTileCausal : kTileMixed;
+}
+
+// Ordered list of the live (not SKIP) tiles lo..hi-1 of a work-group of W waves:
+// sList[i] = 4 * tile + class for the i-th live tile; returns their number.
+// class_of(tile) gives a tile's class.  sCount holds W + 1 ints.  Every thread
+// of the work-group must call it; it synchronises the work-group on entry, so
+// a previous list may be read up to the call.
+template <int W, typename ClassOf>
+__device__ __forceinline__ int build_live_list(int *sList, int *sCount, int lo, int hi, int tid, int lane, int w,
+                                               ClassOf class_of)
+{
+    constexpr int NT = 64 * W;
+    __syncthreads();
+    if (tid == 0) sCount[W] = 0;
+    __syncthreads();
+    for (int c0 = lo; c0 < hi; c0 += NT) {
+        const int it = c0 + tid;
+        const int cls = it < hi ? class_of(it) : (int)kTileSkip;
+        const bool live = cls != kTileSkip;
+        const uint64_t ball = __ballot(live);
+        const int before = __popcll(ball & ((1ull << lane) - 1ull));
+        if (lane == 0) sCount[w] = __popcll(ball);
+        __syncthreads();
+        int base = sCount[W];
+        for (int v = 0; v < w; ++v) base += sCount[v];
+        if (live) sList[base + before] = 4 * it + cls;
+        __syncthreads();
+        if (tid == 0) {
+            int t = sCount[W];
+            for (int v = 0; v < W; ++v) t += sCount[v];
+            sCount[W] = t;
+        }
+        __syncthreads();
+    }
+    return sCount[W];
 }
 
 }  // namespace fab

@@ -1,5 +1,6 @@
 // fab_launch.h -- host-side launch interface between the C ABI (fab_api.cpp)
-// and the kernels (fab_kernels.hip).  Internal to libfab.
+// and the kernels (fab_aux.hip, fab_fwd.hip, fab_bwd.hip, fab_qouter.hip).
+// Internal to libfab.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,19 +54,35 @@ hipError_t launch_forward(const float *q, const float *k, const float *v, const 
                           const uint8_t *map, float scale, int bf16, float *O, float *lse,
                           const Dims &d, hipStream_t s);
 
-// Delta = rowsum(d o O) [N,H,B]; zero the dQ slice [0, off_k) and the blob
-// pads; when dO16 is given, also write d as bf16 [B][H][N][dvp] (zero-padded).
+// Delta = rowsum(d o O) [N,H,B]; zero blob[zero_lo, off_k) (the dQ slice when
+// it is accumulated by atomics, else only its pad) and the other blob pads;
+// when dO16 is given, also write d as bf16 [B][H][N][dvp] (zero-padded).
 hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, __bf16 *dO16,
-                       int dvp, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total,
-                       const Dims &d, hipStream_t s);
+                       int dvp, int64_t zero_lo, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
+                       int64_t total, const Dims &d, hipStream_t s);
+
+// Rows of the bf16 K / V copies are padded per head to a multiple of this.
+constexpr int kPackRows = 64;
+
+// f32 [heads][M][D] -> bf16 [heads][Mp][DP]: 16-byte chunks of row m permuted
+// by swz_chunk(m, ., DP/8) (fab_common.h); rows >= M and columns >= D zero.
+hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
+                                 hipStream_t s);
 
 // Key-block-outer backward: dV, dK per key tile (stored into dk/dv with
-// per-query-head layout when part_heads != 0), dQ by f32 atomics into dq.
-// bf16 mode reads dO from dO16 (see launch_prep); f32 mode from dO.
+// per-query-head layout when part_heads != 0).  f32 mode also adds dQ by f32
+// atomics into dq (zeroed beforehand); bf16 mode leaves dQ to launch_dq and
+// reads dO from dO16 (see launch_prep).
 hipError_t launch_backward(const float *q, const float *k, const float *v, const float *dO,
                            const __bf16 *dO16, const uint16_t *mask, const uint8_t *map,
                            const float *lse, const float *delta, float scale, int bf16, float *dq,
                            float *dk, float *dv, int part_heads, const Dims &d, hipStream_t s);
+
+// Query-block-outer dQ (bf16 mode): dq [DK,N,H,B] = scale dS K, every element
+// written once.  k16 / v16 from launch_pack_rows_bf16 with Mp rows per head.
+hipError_t launch_dq(const float *q, const __bf16 *k16, const __bf16 *v16, const __bf16 *dO16, const uint16_t *mask,
+                     const uint8_t *map, const float *lse, const float *delta, float scale, float *dq, int Mp,
+                     const Dims &d, hipStream_t s);
 
 // dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] for one of dK / dV.
 hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s);
