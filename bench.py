@@ -5,15 +5,17 @@
 
 A step is one pass of the whole path over one batch of resident inputs: one
 fab_backward call with O and LSE left to the library (the op's own semantics:
-mask block map, forward with row LSE, D = rowsum(dO o O), the key-block-outer
-backward with dQ atomics, the grouped-query reduction and the blob packing).
-`value` counts the work that pass must do: forward 2*N*M*(DK+DV)*H*B plus the
-backward 10*N*M*(DK+DV)/2*H*B, each halved under a causal mask.  The same line
-also reports the backward alone (O and LSE supplied by a prior forward, the
-usual training convention) and the forward alone, and a `roofline` object for
-the dominant kernel (the backward kernel), timed with HIP events on the stream
-it is launched on.  `cpu_baseline` times the f64 CPU oracle on a bounded sample
-of the same workload on this host's cores.
+mask block map, bf16 copies of K and V, forward with row LSE, D = rowsum(dO o
+O), the key-block-outer dK/dV kernel, the query-block-outer dQ kernel, the
+grouped-query reduction and the blob packing).  `value` counts the work that
+pass must do: forward 2*N*M*(DK+DV)*H*B plus the backward 10*N*M*(DK+DV)/2*H*B,
+each halved under a causal mask.  The same line also reports the backward
+alone (O and LSE supplied by a prior forward, the usual training convention)
+and the forward alone, every kernel's time per step with its algorithmic
+rate (TFLOP/s for the matrix-core kernels, GB/s for the memory-bound ones),
+and a `roofline` object for the dominant kernel, all timed with HIP events on
+the stream the kernels are launched on.  `cpu_baseline` times the f64 CPU
+oracle on a bounded sample of the same workload on this host's cores.
 
 Prints exactly one JSON line.
 """
@@ -47,6 +49,36 @@ def bwd_flops(s, causal):
     return f / 2 if causal else f
 
 
+def kernel_work(s, causal, mode):
+    """Algorithmic work of one launch-set of each kernel in a step: (amount,
+    unit), flops for the matrix-core kernels and bytes for the memory-bound
+    ones.  A causal mask halves the (query, key) pairs the contractions visit."""
+    half = 0.5 if causal else 1.0
+    pairs = float(s.N) * s.M * s.H * s.B * half
+    bf16 = mode == "bf16"
+    rows = float(s.N) * s.H * s.B
+    # padded head dims of the bf16 copies: the first instantiated pair covering (DK, DV)
+    dkp, dvp = next((a, b) for a, b in ((32, 32), (64, 64), (128, 128), (192, 128), (192, 192))
+                    if s.DK <= a and s.DV <= b)
+    mp = (s.M + 63) // 64 * 64
+    w = {
+        # S = Q K^T and O = P V
+        "forward": (2.0 * pairs * (s.DK + s.DV), "flop"),
+        # bf16: S, dP, dV, dK; f32: also dQ (atomics)
+        "backward": (2.0 * pairs * ((2 * s.DK + 2 * s.DV) if bf16 else (3 * s.DK + 2 * s.DV)), "flop"),
+        # S, dP, dQ
+        "dq": (2.0 * pairs * (2 * s.DK + s.DV), "flop"),
+        "block_map": (2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32), "byte"),
+        # read d and O, write D (+ bf16 d; f32 mode also zeroes the dQ slice)
+        "prep": (rows * (8.0 * s.DV + 4.0) + (rows * dvp * 2.0 if bf16 else rows * s.DK * 4.0), "byte"),
+        # read K, V in f32, write the bf16 copies
+        "pack": (s.Hkv * s.B * (4.0 * s.M * (s.DK + s.DV) + 2.0 * mp * (dkp + dvp)), "byte"),
+        # read per-query-head partials, write per-group sums
+        "gqa_reduce": (4.0 * s.M * (s.DK + s.DV) * s.B * (s.H + s.Hkv), "byte"),
+    }
+    return w
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,44 +105,55 @@ def time_loop(torch, fn, steps, warmup, stream):
     return a.elapsed_time(b) / steps
 
 
-def cpu_baseline(wid, s, q, k, v, d, mask, scale, causal, budget_s):
-    """The oracle, as it stands, on the first key/value group of the workload
-    (all H/Hkv query heads of group 0, batch 0, full N and M)."""
+def cpu_baseline(s, q, k, v, d, mask, scale, causal, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload: whole
+    key/value groups (b, g) with all their H/Hkv query heads, as many as fit the
+    time budget (all of them when they do), else the first queries of group 0.
+    Counted like `value`: forward plus backward flops of the (query, key) pairs
+    attended."""
     from oracle import oracle as orc
     rk2 = s.H // s.Hkv
-    sub = fi.Shape(1, rk2, 1, s.N, s.M, s.DK, s.DV)
-    qs = np.ascontiguousarray(q[:1, :rk2])
-    ks = np.ascontiguousarray(k[:1, :1])
-    vs = np.ascontiguousarray(v[:1, :1])
-    ds = np.ascontiguousarray(d[:1, :, :rk2])
-    # shrink the query range if one group would exceed the time budget (small
-    # calibration run first)
     cores = orc.default_threads()
-    n_keep = s.N
+
+    def group(b, g, n_keep):
+        sub = fi.Shape(1, rk2, 1, n_keep, s.M, s.DK, s.DV)
+        args = (np.ascontiguousarray(q[b:b + 1, g * rk2:(g + 1) * rk2, :n_keep]),
+                np.ascontiguousarray(k[b:b + 1, g:g + 1]), np.ascontiguousarray(v[b:b + 1, g:g + 1]),
+                None if mask is None else np.ascontiguousarray(mask[:n_keep]),
+                np.ascontiguousarray(d[b:b + 1, :n_keep, g * rk2:(g + 1) * rk2]))
+        return sub, args
+
+    # calibration on the first 64 queries of group 0
+    n_cal = min(s.N, 64)
+    sub, a = group(0, 0, n_cal)
     t0 = time.perf_counter()
-    cal = fi.Shape(1, rk2, 1, min(s.N, 64), s.M, s.DK, s.DV)
-    orc.backward(cal, np.ascontiguousarray(qs[:, :, :cal.N]), ks, vs,
-                 None if mask is None else np.ascontiguousarray(mask[:cal.N]),
-                 np.ascontiguousarray(ds[:, :cal.N]), scale)
-    per_row = (time.perf_counter() - t0) / cal.N
-    if per_row * s.N > budget_s:
-        n_keep = max(64, int(budget_s / per_row))
-    sub = fi.Shape(1, rk2, 1, n_keep, s.M, s.DK, s.DV)
-    msub = None if mask is None else np.ascontiguousarray(mask[:n_keep])
+    orc.backward(sub, a[0], a[1], a[2], a[3], a[4], scale)
+    per_row = (time.perf_counter() - t0) / n_cal
+    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
+    per_group = per_row * s.N
+    if per_group <= budget_s:
+        units = units[:max(1, min(len(units), int(budget_s / per_group)))]
+        n_keep = s.N
+    else:
+        units = units[:1]
+        n_keep = max(64, min(s.N, int(budget_s / per_row)))
     t0 = time.perf_counter()
-    orc.backward(sub, np.ascontiguousarray(qs[:, :, :n_keep]), ks, vs, msub,
-                 np.ascontiguousarray(ds[:, :n_keep]), scale)
+    for b, g in units:
+        sub, a = group(b, g, n_keep)
+        orc.backward(sub, a[0], a[1], a[2], a[3], a[4], scale)
     dt = time.perf_counter() - t0
-    # work counted like the metric: rows x keys actually attended
     if causal:
         pairs = sum(min(n + 1, s.M) for n in range(n_keep))
     else:
         pairs = n_keep * s.M
-    flops = 10.0 * pairs * (s.DK + s.DV) / 2.0 * rk2
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    pairs *= rk2 * len(units)
+    flops = pairs * (2.0 * (s.DK + s.DV) + 5.0 * (s.DK + s.DV))
+    what = (f"{len(units)} of {len(units) if n_keep < s.N else s.B * s.Hkv} key/value groups" if n_keep == s.N
+            else f"key/value group 0, queries 0..{n_keep - 1} of {s.N}")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"key/value group 0 of batch 0 ({rk2} query heads), queries 0..{n_keep - 1} of "
-                      f"{s.N}, all {s.M} keys, f64 forward + backward"}
+            "sample": f"{what} ({rk2} query heads each, all {s.M} keys); f64 forward + backward, "
+                      f"counted as the forward plus the backward flops of the attended pairs"}
 
 
 def main():
@@ -166,9 +209,35 @@ def main():
 
     F_f, F_b = fwd_flops(s, causal), bwd_flops(s, causal)
     peak = PEAK_TFLOPS[mode]
-    bwd_kernel_ms = prof["backward"][0] / max(prof["backward"][1], 1)
-    kern_tflops = F_b / (bwd_kernel_ms * 1e-3) / 1e12
-    split = {k: round(v[0] / max(args.steps, 1), 4) for k, v in prof.items() if v[1]}
+    work = kernel_work(s, causal, mode)
+    kernels = {}
+    for name, (tot_ms, launches) in prof.items():
+        if not launches:
+            continue
+        ms = tot_ms / args.steps                       # per step (all launches of the kernel)
+        amount, kind = work[name]
+        if kind == "flop":
+            rate = amount / (ms * 1e-3) / 1e12
+            kernels[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
+                             "achieved": round(rate, 2), "unit": "TFLOP/s", "frac": round(rate / peak, 4)}
+        else:
+            rate = amount / (ms * 1e-3) / 1e9
+            kernels[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
+                             "achieved": round(rate, 1), "unit": "GB/s", "frac": round(rate / HBM_GBS, 4)}
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dom_launch_ms = prof[dom][0] / prof[dom][1]
+    dom_amount, dom_kind = work[dom]
+    per_launch = dom_amount / max(prof[dom][1] // args.steps, 1)
+    if dom_kind == "flop":
+        ach = per_launch / (dom_launch_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "per_launch_flops": per_launch,
+                "avg_launch_ms": round(dom_launch_ms, 5)}
+    else:
+        ach = per_launch / (dom_launch_ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_GBS, 4), "traffic": None, "per_launch_bytes": per_launch,
+                "avg_launch_ms": round(dom_launch_ms, 5)}
 
     out = {
         "metric": METRIC,
@@ -192,14 +261,11 @@ def main():
                           "flops_counted": F_b},
         "forward_only": {"ms": round(ms_fwd, 4), "tflops": round(F_f / (ms_fwd * 1e-3) / 1e12, 3),
                          "frac_of_peak": round(F_f / (ms_fwd * 1e-3) / 1e12 / peak, 4)},
-        "kernel_ms_per_step": split,
-        "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(kern_tflops, 3),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(kern_tflops / peak, 4),
-                     "traffic": None, "per_launch_flops": F_b, "avg_launch_ms": round(bwd_kernel_ms, 5)},
+        "kernels": kernels,
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, s, q, k, v, d, mask, scale, causal,
-                                           args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline(s, q, k, v, d, mask, scale, causal, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
 
 

@@ -39,7 +39,7 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_lse, ws_O, ws_delta, ws_o16, ws_k16, ws_v16, ws_pk, ws_pv, ws_bytes;
+    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_o16, ws_pk, ws_pv, ws_bytes;
     int dkp, dvp;  // padded head dims of the kernels
     int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
@@ -89,6 +89,14 @@ int check_shape(const fab_shape *s, Plan *pl)
     return FAB_OK;
 }
 
+// Workspace carving (256-byte aligned sub-buffers, in this order):
+//   map        u8 block map of the mask                       (mask given)
+//   k16, v16   bf16 K / V rows, Mp per head, swizzled chunks   (bf16 mode)
+//   lse, O     forward recompute                               (O, lse not given)
+//   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward)
+//   o16        bf16 dO [B][H][N][DVP]                          (backward, bf16 mode)
+//   pk, pv     per-query-head dK / dV partials                 (backward, H > Hkv)
+// ws_fwd is the end of the part the forward alone uses.
 void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
 {
     const fab::Dims &d = pl->d;
@@ -96,6 +104,15 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     const int64_t nqb = (d.N + 31) / 32, nkb = (d.M + 31) / 32;
     pl->ws_map = off;
     if (has_mask) off = align_up(off + (size_t)(nqb * nkb));
+    pl->ws_k16 = off;
+    pl->ws_v16 = off;
+    if (mode == FAB_MODE_BF16) {
+        const size_t kvrows = (size_t)pl->mp * d.Hkv * d.B;
+        off = align_up(off + 2 * kvrows * pl->dkp);
+        pl->ws_v16 = off;
+        off = align_up(off + 2 * kvrows * pl->dvp);
+    }
+    pl->ws_fwd = off;
     pl->ws_lse = off;
     pl->ws_O = off;
     if (!have_o_lse) {
@@ -106,16 +123,7 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     pl->ws_delta = off;
     off = align_up(off + sizeof(float) * (size_t)pl->nrow);
     pl->ws_o16 = off;
-    pl->ws_k16 = off;
-    pl->ws_v16 = off;
-    if (mode == FAB_MODE_BF16) {
-        const size_t kvrows = (size_t)pl->mp * d.Hkv * d.B;
-        off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);  // bf16 d
-        pl->ws_k16 = off;
-        off = align_up(off + 2 * kvrows * pl->dkp);             // bf16 K
-        pl->ws_v16 = off;
-        off = align_up(off + 2 * kvrows * pl->dvp);             // bf16 V
-    }
+    if (mode == FAB_MODE_BF16) off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);
     pl->ws_pk = off;
     pl->ws_pv = off;
     if (pl->gqa) {
@@ -219,6 +227,27 @@ struct ProfScope {
         ProfScope ps__(kid, s);                 \
         FAB_HIP(call, what);                    \
     } while (0)
+
+// The bf16 copies of K and V (bf16 mode).
+int launch_pack(const Plan &pl, const float *k, const float *v, __bf16 *k16, __bf16 *v16, hipStream_t s)
+{
+    const int64_t heads = (int64_t)pl.d.Hkv * pl.d.B;
+    FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(k, k16, heads, pl.d.M, pl.mp, pl.d.DK, pl.dkp, s), "K pack launch");
+    FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(v, v16, heads, pl.d.M, pl.mp, pl.d.DV, pl.dvp, s), "V pack launch");
+    return FAB_OK;
+}
+
+int launch_fwd(const Plan &pl, int bf16, const float *q, const float *k, const float *v, const __bf16 *k16,
+               const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *O, float *lse,
+               hipStream_t s)
+{
+    if (bf16)
+        FAB_LAUNCH(kFwd, fab::launch_forward_bf16(q, k16, v16, mask, map, scale, O, lse, pl.mp, pl.d, s),
+                   "forward launch");
+    else
+        FAB_LAUNCH(kFwd, fab::launch_forward_f32(q, k, v, mask, map, scale, O, lse, pl.d, s), "forward launch");
+    return FAB_OK;
+}
 
 }  // namespace
 
@@ -327,17 +356,19 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     if (mask && !aligned16(mask)) return fail(FAB_E_ALIGN, "mask is not 16-byte aligned");
     const bool use_mask = mask && (int64_t)pl.d.M * pl.d.N > 0;
     plan_workspace(&pl, mode, use_mask, 1);
-    const size_t need = use_mask ? pl.ws_map + (size_t)((pl.d.N + 31) / 32) * ((pl.d.M + 31) / 32) : 0;
+    const size_t need = pl.nrow == 0 ? 0 : pl.ws_fwd;
     FAB_TRY(check_ws(ws, ws_bytes, need));
     if (pl.nrow == 0) return FAB_OK;  // no query rows: nothing to write
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *wsb = static_cast<char *>(ws);
     uint8_t *map = use_mask ? reinterpret_cast<uint8_t *>(wsb + pl.ws_map) : nullptr;
+    const int bf16 = mode == FAB_MODE_BF16;
+    __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
+    __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
     if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mask, map, pl.d, s), "block map launch");
-    FAB_LAUNCH(kFwd, fab::launch_forward(q, k, v, use_mask ? mask : nullptr, map, scale, mode == FAB_MODE_BF16,
-                                         O, lse, pl.d, s),
-               "forward launch");
+    if (bf16) FAB_TRY(launch_pack(pl, k, v, k16, v16, s));
+    FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, use_mask ? mask : nullptr, map, scale, O, lse, s));
     return FAB_OK;
 }
 
@@ -379,12 +410,15 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     uint8_t *map = use_mask ? reinterpret_cast<uint8_t *>(wsb + pl.ws_map) : nullptr;
     const uint16_t *mk = use_mask ? mask : nullptr;
     const int bf16 = mode == FAB_MODE_BF16;
+    __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
+    __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
     if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
+    if (bf16) FAB_TRY(launch_pack(pl, k, v, k16, v16, s));
     const float *Ou = O, *lseu = lse;
     if (!have) {
         float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
         float *lw = reinterpret_cast<float *>(wsb + pl.ws_lse);
-        FAB_LAUNCH(kFwd, fab::launch_forward(q, k, v, mk, map, scale, bf16, Ow, lw, pl.d, s), "forward launch");
+        FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, mk, map, scale, Ow, lw, s));
         Ou = Ow;
         lseu = lw;
     }
@@ -395,16 +429,6 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, dO16, pl.dvp, bf16 ? pl.nq : 0, pl.off_k, pl.nk,
                                        pl.off_v, pl.nv, pl.total, pl.d, s),
                "prep launch");
-    __bf16 *k16 = nullptr, *v16 = nullptr;
-    if (bf16) {
-        k16 = reinterpret_cast<__bf16 *>(wsb + pl.ws_k16);
-        v16 = reinterpret_cast<__bf16 *>(wsb + pl.ws_v16);
-        const int64_t heads = (int64_t)pl.d.Hkv * pl.d.B;
-        FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(k, k16, heads, pl.d.M, pl.mp, pl.d.DK, pl.dkp, s),
-                   "K pack launch");
-        FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(v, v16, heads, pl.d.M, pl.mp, pl.d.DV, pl.dvp, s),
-                   "V pack launch");
-    }
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, dO16, mk, map, lseu, delta, scale, bf16, blob, dk, dv,

@@ -1,7 +1,9 @@
-// fab_fwd.hip -- forward with row log-sum-exp (gfx950): O = softmax(scale*q.k
-// + mask) v and LSE = log sum exp, by query blocks with the running max and
-// running sum of the labml "Flash Attention" page ("Flash Attention
-// Optimization"); the dense products run on the matrix cores.
+// fab_fwd.hip -- f32-mode forward with row log-sum-exp (gfx950): O =
+// softmax(scale*q.k + mask) v and LSE = log sum exp, by query blocks with the
+// running max and running sum of the labml "Flash Attention" page ("Flash
+// Attention Optimization"); the dense products run on the f32 matrix cores
+// (v_mfma_f32_32x32x2_f32).  The bf16 forward is fwd_bf16_kernel in
+// fab_qouter.hip.
 #include <algorithm>
 
 #include "fab_common.h"
@@ -20,28 +22,24 @@ struct FwdArgs {
     float scale;
 };
 
-template <int DKP, int DVP, bool BF16>
+template <int DKP, int DVP>
 struct FwdCfg {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;
     static constexpr int BR = 32 * WAVES;  // queries per work-group (32 per wave)
     static constexpr int BC = 64;          // keys per step
-    static constexpr int PADE = BF16 ? 8 : 4;
-    static constexpr int LK = DKP + PADE;                        // sK row stride
-    static constexpr int LV = BF16 ? (BC + PADE) : (DVP + PADE);  // sVt (bf16) / sV (f32)
-    static constexpr int SV = BF16 ? DVP * LV : BC * LV;
-    using T = typename std::conditional<BF16, __bf16, float>::type;
+    static constexpr int LK = DKP + 4;     // sK row stride (floats)
+    static constexpr int LV = DVP + 4;     // sV row stride
 };
 
-template <int DKP, int DVP, bool BF16>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs p)
+template <int DKP, int DVP>
+__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p)
 {
-    using C = FwdCfg<DKP, DVP, BF16>;
-    using T = typename C::T;
+    using C = FwdCfg<DKP, DVP>;
     constexpr int BC = C::BC, BR = C::BR, NT = C::NT, LK = C::LK, LV = C::LV;
     constexpr int NKT = BC / 32;
-    __shared__ __attribute__((aligned(16))) T sK[BC * LK];
-    __shared__ __attribute__((aligned(16))) T sV[C::SV];
+    __shared__ __attribute__((aligned(16))) float sK[BC * LK];
+    __shared__ __attribute__((aligned(16))) float sV[BC * LV];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
     const int nqt = (p.N + BR - 1) / BR;
@@ -54,25 +52,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs p)
     const float *qrow = p.q + (size_t)p.DK * (nok ? (n + p.N * (h + p.H * b)) : 0);
 
     // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim)
-    constexpr int NQF = BF16 ? DKP / 16 : DKP / 2;
-    typename std::conditional<BF16, bf16x8, float>::type qf[NQF];
-    if constexpr (BF16) {
+    float qf[DKP / 2];
 #pragma unroll
-        for (int t = 0; t < DKP / 16; ++t) {
-            float x[8];
-            const f32x4 lo = nok ? load_row4(qrow, 16 * t + 8 * half, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
-            const f32x4 hi = nok ? load_row4(qrow, 16 * t + 8 * half + 4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
+    for (int t = 0; t < DKP / 2; t += 4) {
+        const f32x4 x = nok ? load_row4(qrow, half * (DKP / 2) + t, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { x[i] = lo[i]; x[4 + i] = hi[i]; }
-            qf[t] = to_bf16x8(x);
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < DKP / 2; t += 4) {
-            const f32x4 x = nok ? load_row4(qrow, half * (DKP / 2) + t, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qf[t + i] = x[i];
-        }
+        for (int i = 0; i < 4; ++i) qf[t + i] = x[i];
     }
 
     f32x16 oacc[DVP / 32];
@@ -88,48 +73,18 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs p)
                                    key0 / kMapTile, BC / kMapTile);
         if (cls == kTileSkip) continue;
         __syncthreads();
-        // ---- stage K (row-major) and V (bf16: transposed, keys in MFMA order)
-        if constexpr (BF16) {
-            for (int c = tid; c < BC * (DKP / 4); c += NT) {
-                const int r = c / (DKP / 4), c4 = c % (DKP / 4);
-                const int key = key0 + r;
-                const f32x4 x = key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK)
-                                          : f32x4{0, 0, 0, 0};
-                *reinterpret_cast<bf16x4 *>(&sK[r * LK + 4 * c4]) = to_bf16x4(x);
-            }
-            for (int c = tid; c < (BC / 8) * (DVP / 4); c += NT) {
-                const int kg = c / (DVP / 4), c4 = c % (DVP / 4);
-                f32x4 x[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int key = key0 + 8 * kg + i;
-                    x[i] = key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV)
-                                     : f32x4{0, 0, 0, 0};
-                }
-                // key index bits 2 and 3 swapped within each 16 (MFMA operand order)
-                const int base = 16 * (kg >> 1) + 4 * (kg & 1);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    bf16x4 lo, hi;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) { lo[i] = (__bf16)x[i][jj]; hi[i] = (__bf16)x[4 + i][jj]; }
-                    *reinterpret_cast<bf16x4 *>(&sV[(4 * c4 + jj) * LV + base]) = lo;
-                    *reinterpret_cast<bf16x4 *>(&sV[(4 * c4 + jj) * LV + base + 8]) = hi;
-                }
-            }
-        } else {
-            for (int c = tid; c < BC * (DKP / 4); c += NT) {
-                const int r = c / (DKP / 4), c4 = c % (DKP / 4);
-                const int key = key0 + r;
-                *reinterpret_cast<f32x4 *>(&sK[r * LK + 4 * c4]) =
-                    key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
-            }
-            for (int c = tid; c < BC * (DVP / 4); c += NT) {
-                const int r = c / (DVP / 4), c4 = c % (DVP / 4);
-                const int key = key0 + r;
-                *reinterpret_cast<f32x4 *>(&sV[r * LV + 4 * c4]) =
-                    key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV) : f32x4{0, 0, 0, 0};
-            }
+        // ---- stage K and V rows
+        for (int c = tid; c < BC * (DKP / 4); c += NT) {
+            const int r = c / (DKP / 4), c4 = c % (DKP / 4);
+            const int key = key0 + r;
+            *reinterpret_cast<f32x4 *>(&sK[r * LK + 4 * c4]) =
+                key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
+        }
+        for (int c = tid; c < BC * (DVP / 4); c += NT) {
+            const int r = c / (DVP / 4), c4 = c % (DVP / 4);
+            const int key = key0 + r;
+            *reinterpret_cast<f32x4 *>(&sV[r * LV + 4 * c4]) =
+                key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV) : f32x4{0, 0, 0, 0};
         }
         __syncthreads();
 
@@ -138,19 +93,11 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs p)
 #pragma unroll
         for (int kk = 0; kk < NKT; ++kk) {
             s[kk] = zero16();
-            if constexpr (BF16) {
 #pragma unroll
-                for (int t = 0; t < DKP / 16; ++t) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sK[(kk * 32 + l32) * LK + 16 * t + 8 * half]);
-                    s[kk] = mfma_bf16(a, qf[t], s[kk]);
-                }
-            } else {
+            for (int t = 0; t < DKP / 2; t += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sK[(kk * 32 + l32) * LK + half * (DKP / 2) + t]);
 #pragma unroll
-                for (int t = 0; t < DKP / 2; t += 4) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&sK[(kk * 32 + l32) * LK + half * (DKP / 2) + t]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[kk] = mfma_f32(a[i], qf[t + i], s[kk]);
-                }
+                for (int i = 0; i < 4; ++i) s[kk] = mfma_f32(a[i], qf[t + i], s[kk]);
             }
         }
         // ---- scale, mask, running max (log2 units)
@@ -190,22 +137,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs p)
         for (int dt = 0; dt < DVP / 32; ++dt) {
 #pragma unroll
             for (int kk = 0; kk < NKT; ++kk) {
-                if constexpr (BF16) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        float pv[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) pv[i] = s[kk][8 * u + i];
-                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                            &sV[(dt * 32 + l32) * LV + kk * 32 + 16 * u + 8 * half]);
-                        oacc[dt] = mfma_bf16(a, to_bf16x8(pv), oacc[dt]);
-                    }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const float a = sV[(kk * 32 + crow(u, half)) * LV + dt * 32 + l32];
-                        oacc[dt] = mfma_f32(a, s[kk][u], oacc[dt]);
-                    }
+                for (int u = 0; u < 16; ++u) {
+                    const float a = sV[(kk * 32 + crow(u, half)) * LV + dt * 32 + l32];
+                    oacc[dt] = mfma_f32(a, s[kk][u], oacc[dt]);
                 }
             }
         }
@@ -245,16 +180,20 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 template <int DKP, int DVP, bool BF16>
 hipError_t run_fwd(const FwdArgs &a, hipStream_t s)
 {
-    using C = FwdCfg<DKP, DVP, BF16>;
-    const int grid = ceil_div(a.N, C::BR) * a.H * a.B;
-    hipLaunchKernelGGL((fwd_kernel<DKP, DVP, BF16>), dim3(grid), dim3(C::NT), 0, s, a);
-    return hipGetLastError();
+    if constexpr (BF16) {
+        return hipErrorInvalidValue;
+    } else {
+        using C = FwdCfg<DKP, DVP>;
+        const int grid = ceil_div(a.N, C::BR) * a.H * a.B;
+        hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP>), dim3(grid), dim3(C::NT), 0, s, a);
+        return hipGetLastError();
+    }
 }
 }  // namespace
 
-hipError_t launch_forward(const float *q, const float *k, const float *v, const uint16_t *mask,
-                          const uint8_t *map, float scale, int bf16, float *O, float *lse,
-                          const Dims &d, hipStream_t s)
+hipError_t launch_forward_f32(const float *q, const float *k, const float *v, const uint16_t *mask,
+                              const uint8_t *map, float scale, float *O, float *lse, const Dims &d,
+                              hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
@@ -264,7 +203,7 @@ hipError_t launch_forward(const float *q, const float *k, const float *v, const 
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
-    FAB_DISPATCH_HEAD_DIMS(run_fwd, a, s, hd, bf16);
+    FAB_DISPATCH_HEAD_DIMS(run_fwd, a, s, hd, false);
 }
 
 }  // namespace fab

@@ -49,10 +49,15 @@ inline bool pick_head_dims(int DK, int DV, HeadDims *out)
 // Block map of the additive mask: u8 [ceil(N/32)][ceil(M/32)].
 hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, hipStream_t s);
 
-// Forward with row log-sum-exp (natural log, -inf for all-masked rows).
-hipError_t launch_forward(const float *q, const float *k, const float *v, const uint16_t *mask,
-                          const uint8_t *map, float scale, int bf16, float *O, float *lse,
-                          const Dims &d, hipStream_t s);
+// Forward with row log-sum-exp (natural log, -inf for all-masked rows): f32
+// operands, or bf16 operands read from the packed K / V (launch_pack_rows_bf16,
+// Mp rows per head).
+hipError_t launch_forward_f32(const float *q, const float *k, const float *v, const uint16_t *mask,
+                              const uint8_t *map, float scale, float *O, float *lse, const Dims &d,
+                              hipStream_t s);
+hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+                               const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
+                               hipStream_t s);
 
 // Delta = rowsum(d o O) [N,H,B]; zero blob[zero_lo, off_k) (the dQ slice when
 // it is accumulated by atomics, else only its pad) and the other blob pads;
