@@ -129,8 +129,8 @@ __device__ __forceinline__ void b16_store(const B16Tile<DKP, DVP> &t, __bf16 *sQ
 template <int DKP, int DVP>
 __device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, const __bf16 *Ob, const float *sLb,
                                          const float *sDb, const __bf16 *sK, const bf16x8 *vf,
-                                         f32x16 *dkacc, f32x16 *dvacc, int q0, int thr, bool masked, int mykey,
-                                         float kbias, float sl2, int w, int lane)
+                                         f32x16 *dkacc, f32x16 *dvacc, int q0, int thr, bool masked, bool fast,
+                                         int mykey, float kbias, float sl2, int w, int lane)
 {
     using C = B16Cfg<DKP, DVP>;
     using QL = typename C::QL;
@@ -171,11 +171,15 @@ __device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, con
         }
     }
 
-    // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32
+    // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a tile with
+    // every key visible (fast) folds the scale into the exponent
+    const float mul = fast ? sl2 : 1.f;
+    if (!fast) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float x = sacc[r] * sl2 + kbias;
-        sacc[r] = (q0 + crow(r, half) >= thr) ? x : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+            const float x = sacc[r] * sl2 + kbias;
+            sacc[r] = (q0 + crow(r, half) >= thr) ? x : -INFINITY;
+        }
     }
     if (masked) {
         const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
@@ -193,7 +197,7 @@ __device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, con
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int r = 4 * r4 + c;
-            const float P = fast_exp2(sacc[r] - lse4[c]);
+            const float P = fast_exp2(__builtin_fmaf(sacc[r], mul, -lse4[c]));
             sacc[r] = P;
             pacc[r] = P * (pacc[r] - del4[c]);
         }
@@ -328,7 +332,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             b16_load<DKP, DVP, EXACT>(nt, hd, (more ? (sList[li + 1] >> 2) : it) * BR, p.N, p.DK, p.vecK, tid);
 
             b16_step<DKP, DVP>(p, sQ[buf], sO[buf], sL[buf], sD[buf], sK, vf, dkacc, dvacc, q0,
-                               cls == kTileCausal ? mykey : INT_MIN, cls == kTileMixed, mykey, kbias, sl2, w, lane);
+                               cls == kTileCausal ? mykey : INT_MIN, cls == kTileMixed,
+                               cls == kTileFree && key0 + BC <= p.M, mykey, kbias, sl2, w, lane);
             if (more) b16_store<DKP, DVP>(nt, sQ[buf ^ 1], sO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], tid);
             __syncthreads();  // next tile staged; every wave is done with this one
             buf ^= 1;

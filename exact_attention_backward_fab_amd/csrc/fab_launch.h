@@ -69,8 +69,8 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
 // Rows of the bf16 K / V copies are padded per head to a multiple of this.
 constexpr int kPackRows = 64;
 
-// f32 [heads][M][D] -> bf16 [heads][Mp][DP]: 16-byte chunks of row m permuted
-// by swz_chunk(m, ., DP/8) (fab_common.h); rows >= M and columns >= D zero.
+// f32 [heads][M][D] -> bf16 [heads][Mp][DP] in 64-row tiles stored chunk column
+// by chunk column (fab_qouter.hip); rows >= M and columns >= D zero.
 hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
                                  hipStream_t s);
 

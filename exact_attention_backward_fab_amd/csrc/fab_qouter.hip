@@ -1,8 +1,8 @@
 // fab_qouter.hip -- bf16 row packing and the query-block-outer kernels (gfx950).
 //
-//   pack_rows_bf16_kernel  f32 rows [rows][D] -> bf16 rows [rows][DP] (zero-padded
-//                          columns), 16-byte chunks permuted by swz_chunk so that
-//                          a tile can be copied linearly into LDS
+//   pack_rows_bf16_kernel  f32 rows -> bf16 64-row tiles (zero-padded), stored so
+//                          that a tile is copied linearly into LDS and read there
+//                          without address arithmetic
 //   fwd_bf16_kernel        O = softmax(scale S + mask) V and the row LSE by query
 //                          blocks, with the running max and running sum of the
 //                          labml "Flash Attention" page ("Flash Attention
@@ -23,9 +23,23 @@
 
 namespace fab {
 
-// ============================================================== bf16 pack
-// src: heads of M rows of D floats; dst: heads of Mp >= M rows of DP bf16, rows
-// M..Mp-1 and columns D..DP-1 zero.
+// ============================================================== bf16 tiles
+// The bf16 copies of K and V are stored as tiles of 64 rows, each tile as its
+// 16-byte chunk columns one after the other: chunk c (head-dim columns 8c..8c+7)
+// of row r of a tile lies at byte c * 1024 + r * 16 of the tile.  One chunk column
+// is thus 1 KiB of contiguous memory, the unit the global -> LDS copies move.  In
+// LDS each chunk column gets 128 bytes of padding (stride kChunkL), so that
+//   * 16-byte row reads (matrix-core operands with one row per lane) are a
+//     contiguous 512-byte run per lane half, and
+//   * transposing 8-byte reads (ds_read_b64_tr_b16) of 4 rows x 4 chunk columns
+//     hit every LDS bank exactly twice,
+// and every address in a step is a per-lane base plus a compile-time offset.
+constexpr int kTR = 64;              // rows per tile
+constexpr int kChunkG = 1024;        // bytes per chunk column of a tile, global memory
+constexpr int kChunkL = 1152;        // ... in LDS
+
+// src: heads of M rows of D floats; dst: heads of Mp >= M rows (Mp a multiple of
+// 64) of DP bf16 in the tile layout above; rows >= M and columns >= D zero.
 __global__ __launch_bounds__(256) void pack_rows_bf16_kernel(const float *__restrict__ src, __bf16 *__restrict__ dst,
                                                              int64_t heads, int M, int Mp, int D, int DP, int vec)
 {
@@ -33,18 +47,21 @@ __global__ __launch_bounds__(256) void pack_rows_bf16_kernel(const float *__rest
     const int64_t total = heads * Mp * nch;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        const int64_t row = i / nch;                 // row of dst
-        const int ch = (int)(i - row * nch);
-        const int64_t hd = row / Mp;
-        const int m = (int)(row - hd * Mp);
+        // i enumerates (head, tile, chunk column, row in tile): consecutive threads
+        // write consecutive 16-byte chunks of the destination
+        const int64_t hd = i / ((int64_t)Mp * nch);
+        const int rem = (int)(i - hd * Mp * nch);
+        const int tile = rem / (kTR * nch), in = rem - tile * kTR * nch;
+        const int ch = in / kTR, r = in - ch * kTR;
+        const int m = tile * kTR + r;
         f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
         if (m < M) {
             const float *sr = src + (hd * M + m) * D;
             lo = load_row4(sr, 8 * ch, D, vec);
             hi = load_row4(sr, 8 * ch + 4, D, vec);
         }
-        __bf16 *dr = dst + row * DP + 8 * swz_chunk(m, ch, nch);
-        *reinterpret_cast<bf16x8 *>(dr) = __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8 *>(dst + 8 * i) =
+            __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
 
@@ -59,69 +76,134 @@ hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, i
     return hipGetLastError();
 }
 
-// ============================================================== dQ by query blocks
-struct DqArgs {
-    const float *q;                 // f32 [B,H,N,DK]
-    const __bf16 *k16, *v16;        // bf16 swizzled [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP], rows >= M zero
-    const __bf16 *dO16;             // bf16 [B,H,N,DVP]
-    const uint16_t *mask;
-    const uint8_t *map;
-    const float *lse, *delta;       // [N,H,B]
-    float *dq;                      // [DK,N,H,B] slice of the result blob
-    int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK;
-    float scale;
+// Work-group shape of the query-block-outer kernels: 4 waves, 32 queries each;
+// keys stream through LDS one 64-row tile (a step) at a time.
+constexpr int kQW = 4, kQNT = 64 * kQW, kQBQ = 32 * kQW, kQBK = kTR;
+constexpr int kQList = 512;   // live key steps listed at a time
+
+// LDS stages of the key stream (K and V tiles of one step each) and work-groups
+// per CU: two work-groups (two waves per SIMD, so that one wave's softmax
+// arithmetic overlaps the other's matrix-core work) when two stages of each fit
+// in half of the 160 KiB, else one; then as many stages as fit, at most 4.
+template <int DKP, int DVP>
+struct QStages {
+    static constexpr int kK = DKP / 8 * kChunkL;            // bytes of a K tile in LDS
+    static constexpr int kBytes = (DKP + DVP) / 8 * kChunkL;
+    static constexpr int kFixed = 4 * kQList + 256;
+    static constexpr int Occ = (2 * kBytes + kFixed <= 80 * 1024) ? 2 : 1;
+    static constexpr int kFit = (160 * 1024 / Occ - kFixed) / kBytes;
+    static constexpr int N = kFit > 4 ? 4 : kFit;
+    static_assert(N >= 2, "two LDS stages must fit");
 };
 
-// Work-group shape of the query-block-outer kernels: 4 waves, 32 queries each;
-// keys stream through LDS 64 at a time.
-constexpr int kQW = 4, kQNT = 64 * kQW, kQBQ = 32 * kQW, kQBK = 64;
-constexpr int kQList = 1024;   // live key steps listed at a time
+// Per-lane byte offsets inside an LDS tile (see the tile layout above):
+//   row operand   16 bytes of row l32 (+32 kk), chunk column 2t + half:
+//                 row_off + 512 kk + 2304 t
+//   transposed    rows 16u + 4 half + (j >> 2) (+32 kk, +8 for the upper 4 slots),
+//                 columns 32 dt + 16 grp + 4 (j & 3), j = lane & 15, grp = bit 4 of
+//                 the lane: tr_off + 4608 dt + 512 kk + 256 u (+128)
+__device__ __forceinline__ int tile_row_off(int lane) { return (lane >> 5) * kChunkL + (lane & 31) * 16; }
+__device__ __forceinline__ int tile_tr_off(int lane)
+{
+    const int j = lane & 15, grp = (lane >> 4) & 1, half = lane >> 5;
+    return (2 * grp + ((j & 3) >> 1)) * kChunkL + ((j >> 2) + 4 * half) * 16 + (j & 1) * 8;
+}
+__device__ __forceinline__ bf16x8 lds_row8(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x8 lds_tr8(const char *p)
+{
+    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16 *>(p));
+    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16 *>(p + 128));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
-// Streams the live key steps (block map) of one query block through two LDS
-// buffers: the bf16 K and V rows of step s+1 are copied from global memory
-// straight into LDS (buffer_load ... lds, 16 bytes per lane, consecutive lanes
-// to consecutive LDS addresses) while body(step, class, K tile, V tile) works on
-// step s.  Copies are issued per wave in 1 KiB blocks; a wave waits for its own
-// copies and the barrier publishes them to the work-group.
+// Work-group -> (query tile, head).  Consecutive work-groups are dealt round-robin
+// to the 8 XCDs; when the heads split evenly over the XCDs, each XCD gets a
+// contiguous range of heads (the heads of a key/value group share its K/V rows in
+// that XCD's L2) and walks it latest query tile first, heads fastest.
+struct QWork {
+    int qt, hb;
+};
+__device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB)
+{
+    QWork r;
+    if (HB % 8 == 0) {
+        const int xcd = bid % 8, j = bid / 8, per = HB / 8;
+        r.qt = nqt - 1 - j / per;
+        r.hb = xcd * per + j % per;
+    } else {
+        r.qt = nqt - 1 - bid / HB;
+        r.hb = bid % HB;
+    }
+    return r;
+}
+
+// One 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i
+// writes LDS bytes [la + 16 i, la + 16 i + 16); la must be wave-uniform.  Issued
+// as inline assembly so that the compiler does not make every later LDS read wait
+// for it; the caller orders it with explicit vmcnt waits and barriers.  m0 is not
+// used by the compiler in these kernels (the buffer copy is their only m0 user);
+// the copy reads m0 one wait state after it is written.
+__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t la, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(la), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// Waits until at most k * PER of this wave's vector-memory operations are in flight.
+template <int PER>
+__device__ __forceinline__ void wait_vm_steps(int k)
+{
+    static_assert(3 * PER <= 63, "vmcnt range");
+    if (k <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (k == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+    else if (k == 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * PER) : "memory");
+}
+
+// Streams the live key steps (block map) of one query block through the LDS
+// stages: the K and V tiles of later steps are copied from global memory straight
+// into LDS while body(step, class, K tile, V tile) works on the current one.  Each
+// wave copies a quarter of the chunk columns; before a step is used every wave
+// waits for its own copies of it (vmcnt) and a barrier publishes them; the same
+// barrier tells every wave that the stage about to be refilled has been consumed.
+// sKV is the stage array and kv_lds its LDS byte address.
 template <int DKP, int DVP, typename ClassOf, typename Body>
-__device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, __bf16 *sK, __bf16 *sV, int *sList,
+__device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const char *sKV, uint32_t kv_lds, int *sList,
                                                  int *sCount, int nks, int tid, int lane, int w, ClassOf class_of,
                                                  Body body)
 {
-    constexpr int KCH = kQBK * DKP / (8 * kQNT), VCH = kQBK * DVP / (8 * kQNT);   // copies per lane
-    static_assert(KCH * 8 * kQNT == kQBK * DKP && VCH * 8 * kQNT == kQBK * DVP, "tile copy split");
-    typedef __attribute__((address_space(3))) void lds_void;
+    using ST = QStages<DKP, DVP>;
+    constexpr int NS = ST::N;
+    constexpr int KCH = DKP / 8 / kQW, VCH = DVP / 8 / kQW;   // chunk columns copied per wave
+    static_assert(KCH * 8 * kQW == DKP && VCH * 8 * kQW == DVP, "tile copy split");
     auto issue = [&](int s, int bf) {
+        const uint32_t stg = kv_lds + (uint32_t)(bf * ST::kBytes);   // wave-uniform LDS byte address
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int blk = i * kQW + w;   // 1 KiB block of the tile
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)&sK[bf * kQBK * DKP + blk * 512], 16,
-                                                     (uint32_t)(s * kQBK * DKP) * 2u + (uint32_t)(blk * 64 + lane) * 16u,
-                                                     0, 0, 0);
+            const int c = i * kQW + w;
+            lds_copy16(rk, stg + c * kChunkL, (uint32_t)(s * DKP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-            const int blk = i * kQW + w;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)&sV[bf * kQBK * DVP + blk * 512], 16,
-                                                     (uint32_t)(s * kQBK * DVP) * 2u + (uint32_t)(blk * 64 + lane) * 16u,
-                                                     0, 0, 0);
+            const int c = i * kQW + w;
+            lds_copy16(rv, stg + ST::kK + c * kChunkL, (uint32_t)(s * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
     };
     for (int seg = 0; seg < nks; seg += kQList) {
         const int count = build_live_list<kQW>(sList, sCount, seg, min(seg + kQList, nks), tid, lane, w, class_of);
         if (count == 0) continue;
-        issue(sList[0] >> 2, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        int buf = 0;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < count) issue(sList[i] >> 2, i);
         for (int li = 0; li < count; ++li) {
+            wait_vm_steps<KCH + VCH>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
+            __syncthreads();                                          // ... for every wave; stage li-1 is free
+            if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
             const int e = sList[li];
-            if (li + 1 < count) issue(sList[li + 1] >> 2, buf ^ 1);
-            body(e >> 2, e & 3, (const __bf16 *)&sK[buf * kQBK * DKP], (const __bf16 *)&sV[buf * kQBK * DVP]);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of the next step landed
-            __syncthreads();                                   // every wave is done with this buffer
-            buf ^= 1;
+            const char *stg = sKV + (li % NS) * ST::kBytes;
+            body(e >> 2, e & 3, stg, stg + ST::kK);
         }
+        __syncthreads();   // every wave is done with the stages before they are refilled
     }
 }
 
@@ -139,25 +221,24 @@ __device__ __forceinline__ void load_q_operand(bf16x8 *qf, const float *qr, bool
     }
 }
 
-// S^T for one 32-key sub-tile (rows kk*32.. of the K tile): lane = query.
+// S^T for one 32-key sub-tile (rows 32 kk.. of the K tile at Kb): lane = query.
 template <int DKP>
-__device__ __forceinline__ f32x16 st_tile(const __bf16 *Kb, const bf16x8 *qf, int kk, int l32, int half)
+__device__ __forceinline__ f32x16 st_tile(const char *Kb, const bf16x8 *qf, int kk, int row_off)
 {
-    using KL = RowTile<DKP>;
     f32x16 acc = zero16();
     bf16x8 a[DKP / 16];
 #pragma unroll
-    for (int t = 0; t < DKP / 16; ++t)
-        a[t] = *reinterpret_cast<const bf16x8 *>(&Kb[KL::off(kk * 32 + l32, 16 * t + 8 * half)]);
+    for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Kb + row_off + 512 * kk + 2304 * t);
 #pragma unroll
     for (int t = 0; t < DKP / 16; ++t) acc = mfma_bf16(a[t], qf[t], acc);
     return acc;
 }
 
 // Scaled scores (log2 units) of a 64-key step for the lane's query: keys past
-// lim get -inf; MIXED steps add the mask row of the query.
+// lim get -inf; MIXED steps add the mask row of the query.  A lane's keys come in
+// runs of 4 (slots 4j..4j+3), read as one 8-byte load when vecM (M % 4 == 0).
 __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bool mixed, const uint16_t *mrow, int M,
-                                               float sl2, int half)
+                                               bool vecM, float sl2, int half)
 {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -167,18 +248,34 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
             st[kk][r] = (key0 + kk * 32 + crow(r, half) <= lim) ? x : -INFINITY;
         }
     if (mixed) {
+        uint16_t m[2][16];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                st[kk][r] += half_bits_to_float(mrow[min(key0 + kk * 32 + crow(r, half), M - 1)]) * kLog2e;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int k0 = key0 + kk * 32 + 8 * r4 + 4 * half;
+                if (vecM && k0 + 3 < M) {
+                    const uint2 x = *reinterpret_cast<const uint2 *>(mrow + k0);
+                    m[kk][4 * r4 + 0] = (uint16_t)(x.x & 0xFFFFu);
+                    m[kk][4 * r4 + 1] = (uint16_t)(x.x >> 16);
+                    m[kk][4 * r4 + 2] = (uint16_t)(x.y & 0xFFFFu);
+                    m[kk][4 * r4 + 3] = (uint16_t)(x.y >> 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m[kk][4 * r4 + i] = mrow[min(k0 + i, M - 1)];
+                }
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[kk][r] += half_bits_to_float(m[kk][r]) * kLog2e;
     }
 }
 
 // ============================================================== forward
 struct FwdArgs16 {
     const float *q;
-    const __bf16 *k16, *v16;        // bf16 swizzled [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP], rows >= M zero
+    const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
     float *O, *lse;                 // O [DV,H,N,B], lse [N,H,B]
@@ -187,19 +284,20 @@ struct FwdArgs16 {
 };
 
 template <int DKP, int DVP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs16 p)
+__global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
+__attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
 {
-    using VL = RowTile<DVP>;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kQBK * DKP];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kQBK * DVP];
+    __shared__ __attribute__((aligned(16))) char sKV[QStages<DKP, DVP>::N * QStages<DKP, DVP>::kBytes];
     __shared__ int sList[kQList];
     __shared__ int sCount[kQW + 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-    const int HB = p.H * p.B;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
+    const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
     const int nqt = (p.N + kQBQ - 1) / kQBQ;
-    const int qt = nqt - 1 - (int)(blockIdx.x / HB);  // latest queries first: most keys under a causal mask
-    const int hb = blockIdx.x % HB;
+    const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B);   // latest queries first (most keys if causal)
+    const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int q0 = qt * kQBQ;
     const int myq = q0 + 32 * w + l32;  // this lane's query (C-layout column of S^T and O^T)
@@ -214,47 +312,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     f32x16 oacc[DVP / 32];
 #pragma unroll
     for (int i = 0; i < DVP / 32; ++i) oacc[i] = zero16();
-    float m_run = -INFINITY, l_part = 0.f;   // running max (log2 units), this half's running sum
+    float m_run = -INFINITY, l_part = 0.f;   // reference max (log2 units), this half's running sum
     const float sl2 = p.scale * kLog2e;
     const uint16_t *mrow = p.mask + (size_t)p.M * min(myq, p.N - 1);
 
     stream_key_steps<DKP, DVP>(
-        rk, rv, sK, sV, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
+        rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
             return tile_class(p.map, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
                               kQBK / kMapTile);
         },
-        [&](int s, int cls, const __bf16 *Kb, const __bf16 *Vb) {
+        [&](int s, int cls, const char *Kb, const char *Vb) {
             const int key0 = s * kQBK;
             f32x16 st[2];
-            st[0] = st_tile<DKP>(Kb, qf, 0, l32, half);
-            st[1] = st_tile<DKP>(Kb, qf, 1, l32, half);
-            const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
-            scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, sl2, half);
+            st[0] = st_tile<DKP>(Kb, qf, 0, row_off);
+            st[1] = st_tile<DKP>(Kb, qf, 1, row_off);
+            // scores in log2 units = st * mul: a step with every key visible (FREE and
+            // inside M) keeps the raw products and folds the scale into the exponent
+            float mul = sl2;
+            if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f)) {
+                const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
+                scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                mul = 1.f;
+            }
 
-            // ---- running max and sum; the two lane halves hold the same query
-            float mloc = -INFINITY;
+            // ---- running max and sum; the two lane halves hold the same query.  The
+            // reference max m_run moves only when the step's max exceeds it by more
+            // than 8 (P <= 2^8 stays exact in f32 and bf16 relative terms; O = Õ / l
+            // and LSE = m_run + log2 l do not depend on which reference is used), so
+            // most steps skip rescaling the accumulators.
+            float mraw = -INFINITY;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, st[kk][r]);
-            mloc = swap_halves_max(mloc);
-            const float m_new = fmaxf(m_run, mloc);
+                for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, st[kk][r]);
+            const float mloc = swap_halves_max(mraw) * mul;
+            const bool grow = mloc > m_run + 8.f;   // m_run = -inf: any finite score
+            const float m_new = grow ? mloc : m_run;
+            if (__any(grow)) {
+                const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+                l_part *= alpha;
+#pragma unroll
+                for (int i = 0; i < DVP / 32; ++i) oacc[i] *= alpha;
+            }
+            m_run = m_new;
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // all -inf so far: P = 0
-            const float alpha = fast_exp2(m_run - m_use);
             float lsum = 0.f;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(st[kk][r] - m_use);
+                    const float e = fast_exp2(__builtin_fmaf(st[kk][r], mul, -m_use));
                     st[kk][r] = e;
                     lsum += e;
                 }
-            l_part = l_part * alpha + lsum;
-            m_run = m_new;
-#pragma unroll
-            for (int i = 0; i < DVP / 32; ++i) oacc[i] *= alpha;
+            l_part += lsum;
 
             // ---- O^T += V^T P^T: A = V^T by transposing reads (key rows 16u + 4*half
             // (+8) of the sub-tile), B = P^T (lane = query, keys in operand order)
@@ -269,7 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     bf16x8 av[DVP / 32];
 #pragma unroll
                     for (int dt = 0; dt < DVP / 32; ++dt)
-                        av[dt] = tile_col8<VL>(Vb, kk * 32 + 16 * u + 4 * half, 8, dt * 32, lane);
+                        av[dt] = lds_tr8(Vb + tr_off + 4608 * dt + 512 * kk + 256 * u);
 #pragma unroll
                     for (int dt = 0; dt < DVP / 32; ++dt) oacc[dt] = mfma_bf16(av[dt], pb, oacc[dt]);
                 }
@@ -301,21 +413,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// ============================================================== dQ by query blocks
+struct DqArgs {
+    const float *q;                 // f32 [B,H,N,DK]
+    const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
+    const __bf16 *dO16;             // bf16 [B,H,N,DVP]
+    const uint16_t *mask;
+    const uint8_t *map;
+    const float *lse, *delta;       // [N,H,B]
+    float *dq;                      // [DK,N,H,B] slice of the result blob
+    int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK;
+    float scale;
+};
+
 template <int DKP, int DVP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dq_bf16_kernel(DqArgs p)
+__global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
+__attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void dq_bf16_kernel(DqArgs p)
 {
-    using KL = RowTile<DKP>;
-    using VL = RowTile<DVP>;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kQBK * DKP];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kQBK * DVP];
+    __shared__ __attribute__((aligned(16))) char sKV[QStages<DKP, DVP>::N * QStages<DKP, DVP>::kBytes];
     __shared__ int sList[kQList];
     __shared__ int sCount[kQW + 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-    const int HB = p.H * p.B;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
+    const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
     const int nqt = (p.N + kQBQ - 1) / kQBQ;
-    const int qt = nqt - 1 - (int)(blockIdx.x / HB);  // latest queries first: most keys under a causal mask
-    const int hb = blockIdx.x % HB;
+    const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B);   // latest queries first (most keys if causal)
+    const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int q0 = qt * kQBQ;
     const int myq = q0 + 32 * w + l32;  // this lane's query (C-layout column of S^T and dP^T)
@@ -351,35 +476,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint16_t *mrow = p.mask + (size_t)p.M * min(myq, p.N - 1);
 
     stream_key_steps<DKP, DVP>(
-        rk, rv, sK, sV, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
+        rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
             return tile_class(p.map, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
                               kQBK / kMapTile);
         },
-        [&](int s, int cls, const __bf16 *Kb, const __bf16 *Vb) {
+        [&](int s, int cls, const char *Kb, const char *Vb) {
             const int key0 = s * kQBK;
             // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key sub-tiles (lane = query)
             f32x16 st[2], pt[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                st[kk] = st_tile<DKP>(Kb, qf, kk, l32, half);
+                st[kk] = st_tile<DKP>(Kb, qf, kk, row_off);
                 pt[kk] = zero16();
                 bf16x8 av[DVP / 16];
 #pragma unroll
-                for (int t = 0; t < DVP / 16; ++t)
-                    av[t] = *reinterpret_cast<const bf16x8 *>(&Vb[VL::off(kk * 32 + l32, 16 * t + 8 * half)]);
+                for (int t = 0; t < DVP / 16; ++t) av[t] = lds_row8(Vb + row_off + 512 * kk + 2304 * t);
 #pragma unroll
                 for (int t = 0; t < DVP / 16; ++t) pt[kk] = mfma_bf16(av[t], of[t], pt[kk]);
             }
 
-            // ---- P and dS; keys past M and (causal steps) keys after the query get -inf
-            const int lim = min(cls == kTileCausal ? myq : INT_MAX, p.M - 1);
-            scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, sl2, half);
+            // ---- P and dS; keys past M and (causal steps) keys after the query get -inf;
+            // a step with every key visible folds the scale into the exponent
+            float mul = sl2;
+            if (!(cls == kTileFree && key0 + kQBK <= p.M)) {
+                const int lim = min(cls == kTileCausal ? myq : INT_MAX, p.M - 1);
+                scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                mul = 1.f;
+            }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float P = fast_exp2(st[kk][r] - lse2);
+                    const float P = fast_exp2(__builtin_fmaf(st[kk][r], mul, -lse2));
                     pt[kk][r] = P * (pt[kk][r] - dl);
                 }
 
@@ -396,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     bf16x8 bk[DKP / 32];
 #pragma unroll
                     for (int dt = 0; dt < DKP / 32; ++dt)
-                        bk[dt] = tile_col8<KL>(Kb, kk * 32 + 16 * u + 4 * half, 8, dt * 32, lane);
+                        bk[dt] = lds_tr8(Kb + tr_off + 4608 * dt + 512 * kk + 256 * u);
 #pragma unroll
                     for (int dt = 0; dt < DKP / 32; ++dt) dqacc[dt] = mfma_bf16(da, bk[dt], dqacc[dt]);
                 }
