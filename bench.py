@@ -61,6 +61,7 @@ def kernel_work(s, causal, mode):
     dkp, dvp = next((a, b) for a, b in ((32, 32), (64, 64), (128, 128), (192, 128), (192, 192))
                     if s.DK <= a and s.DV <= b)
     mp = (s.M + 63) // 64 * 64
+    np_ = (s.N + 63) // 64 * 64
     w = {
         # S = Q K^T and O = P V
         "forward": (2.0 * pairs * (s.DK + s.DV), "flop"),
@@ -69,10 +70,13 @@ def kernel_work(s, causal, mode):
         # S, dP, dQ
         "dq": (2.0 * pairs * (2 * s.DK + s.DV), "flop"),
         "block_map": (2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32), "byte"),
-        # read d and O, write D (+ bf16 d; f32 mode also zeroes the dQ slice)
-        "prep": (rows * (8.0 * s.DV + 4.0) + (rows * dvp * 2.0 if bf16 else rows * s.DK * 4.0), "byte"),
-        # read K, V in f32, write the bf16 copies
-        "pack": (s.Hkv * s.B * (4.0 * s.M * (s.DK + s.DV) + 2.0 * mp * (dkp + dvp)), "byte"),
+        # bf16: read d, O and the LSE, write the bf16 dO tiles and the LSE/D blocks;
+        # f32: read d and O, write D and zero the dQ slice
+        "prep": ((rows * (8.0 * s.DV + 4.0) + s.H * s.B * (np_ * dvp * 2.0 + np_ / 64 * 512.0)) if bf16
+                 else rows * (8.0 * s.DV + 4.0) + rows * s.DK * 4.0, "byte"),
+        # read K, V (and Q) in f32, write the bf16 tiles
+        "pack": (s.Hkv * s.B * (4.0 * s.M * (s.DK + s.DV) + 2.0 * mp * (dkp + dvp))
+                 + s.H * s.B * (4.0 * s.N * s.DK + 2.0 * np_ * dkp), "byte"),
         # read per-query-head partials, write per-group sums
         "gqa_reduce": (4.0 * s.M * (s.DK + s.DV) * s.B * (s.H + s.Hkv), "byte"),
     }

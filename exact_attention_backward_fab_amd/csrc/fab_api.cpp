@@ -39,8 +39,9 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_o16, ws_pk, ws_pv, ws_bytes;
+    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_pk, ws_pv, ws_bytes;
     int dkp, dvp;  // padded head dims of the kernels
+    int np;        // query rows per head of the bf16 Q / dO tiles
     int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
 };
@@ -86,6 +87,7 @@ int check_shape(const fab_shape *s, Plan *pl)
     pl->dkp = hd.dk;
     pl->dvp = hd.dv;
     pl->mp = (int)((s->M + fab::kPackRows - 1) / fab::kPackRows * fab::kPackRows);
+    pl->np = (int)((s->N + fab::kPackRows - 1) / fab::kPackRows * fab::kPackRows);
     return FAB_OK;
 }
 
@@ -93,8 +95,9 @@ int check_shape(const fab_shape *s, Plan *pl)
 //   map        u8 block map of the mask                       (mask given)
 //   k16, v16   bf16 K / V rows, Mp per head, swizzled chunks   (bf16 mode)
 //   lse, O     forward recompute                               (O, lse not given)
-//   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward)
-//   o16        bf16 dO [B][H][N][DVP]                          (backward, bf16 mode)
+//   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward, f32 mode)
+//   q16, o16   bf16 Q / dO tiles, Np rows per head             (backward, bf16 mode)
+//   stats      LSE / D blocks [B][H][Np/64][128]               (backward, bf16 mode)
 //   pk, pv     per-query-head dK / dV partials                 (backward, H > Hkv)
 // ws_fwd is the end of the part the forward alone uses.
 void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
@@ -121,9 +124,18 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         off = align_up(off + sizeof(float) * (size_t)pl->nO);
     }
     pl->ws_delta = off;
-    off = align_up(off + sizeof(float) * (size_t)pl->nrow);
+    if (mode == FAB_MODE_F32) off = align_up(off + sizeof(float) * (size_t)pl->nrow);
+    pl->ws_q16 = off;
     pl->ws_o16 = off;
-    if (mode == FAB_MODE_BF16) off = align_up(off + 2 * (size_t)pl->nrow * pl->dvp);
+    pl->ws_stats = off;
+    if (mode == FAB_MODE_BF16) {
+        const size_t qrows = (size_t)pl->np * d.H * d.B;
+        off = align_up(off + 2 * qrows * pl->dkp);
+        pl->ws_o16 = off;
+        off = align_up(off + 2 * qrows * pl->dvp);
+        pl->ws_stats = off;
+        off = align_up(off + sizeof(float) * qrows / 64 * 128);
+    }
     pl->ws_pk = off;
     pl->ws_pv = off;
     if (pl->gqa) {
@@ -423,20 +435,34 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
         lseu = lw;
     }
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
-    __bf16 *dO16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
+    __bf16 *q16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_q16) : nullptr;
+    __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
+    float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
     // bf16: dQ is written once by the query-block-outer kernel (only its pad is
     // zeroed); f32: dQ is accumulated by atomics into a zeroed slice
-    FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, dO16, pl.dvp, bf16 ? pl.nq : 0, pl.off_k, pl.nk,
-                                       pl.off_v, pl.nv, pl.total, pl.d, s),
-               "prep launch");
+    if (bf16)
+        FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, Ou, lseu, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
+                                                pl.off_v, pl.nv, pl.total, pl.d, s),
+                   "prep launch");
+    else
+        FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
+                   "prep launch");
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
-    FAB_LAUNCH(kBwd, fab::launch_backward(q, k, v, d, dO16, mk, map, lseu, delta, scale, bf16, blob, dk, dv,
-                                          pl.gqa ? 1 : 0, pl.d, s),
-               "backward launch");
-    if (bf16)
-        FAB_LAUNCH(kDq, fab::launch_dq(q, k16, v16, dO16, mk, map, lseu, delta, scale, blob, pl.mp, pl.d, s),
+    if (bf16) {
+        FAB_LAUNCH(kPack,
+                   fab::launch_pack_rows_bf16(q, q16, (int64_t)pl.d.H * pl.d.B, pl.d.N, pl.np, pl.d.DK, pl.dkp, s),
+                   "Q pack launch");
+        FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, pl.gqa ? 1 : 0,
+                                                   pl.np, pl.mp, pl.d, s),
+                   "backward launch");
+        FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, pl.np, pl.mp, pl.d, s),
                    "dQ launch");
+    } else {
+        FAB_LAUNCH(kBwd, fab::launch_backward_f32(q, k, v, d, mk, map, lseu, delta, scale, blob, dk, dv,
+                                                  pl.gqa ? 1 : 0, pl.d, s),
+                   "backward launch");
+    }
     if (pl.gqa) {
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, pl.d.DK, pl.d, s), "dK reduce launch");
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dv, blob + pl.off_v, pl.d.DV, pl.d, s), "dV reduce launch");

@@ -23,12 +23,12 @@
 
 #include "fab_common.h"
 #include "fab_launch.h"
+#include "fab_tiles.h"
 
 namespace fab {
 
 struct BwdArgs {
     const float *q, *k, *v, *dO;
-    const __bf16 *dO16;               // bf16 mode: d as [B][H][N][DVP]
     const uint16_t *mask;
     const uint8_t *map;
     const float *lse, *delta;
@@ -39,264 +39,89 @@ struct BwdArgs {
 };
 
 // ============================================================== bf16 mode
+// Inputs are the bf16 tiles of fab_tiles.h: Q and dO per query head ([B,H,Np,*]),
+// K and V per key/value head ([B,Hkv,Mp,*]), and the per-query LSE/D blocks.  A
+// work-group owns 128 keys (32 per wave, one per lane in the C layout of S and
+// dP); its K and V rows are B operands held in registers.  The query tiles that
+// see the block stream through LDS 64 queries at a time: the Q tile, the dO tile
+// and the LSE/D block of a step are copied from global memory straight into LDS
+// (several stages ahead), and every product reads its LDS operand as a per-lane
+// base plus a constant offset.
+struct KvArgs {
+    const __bf16 *q16, *o16;          // bf16 tiles [B,H,Np,DKP] / [B,H,Np,DVP]
+    const float *stats;               // LSE/D blocks [B,H,Np/64][128]
+    const __bf16 *k16, *v16;          // bf16 tiles [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP]
+    const uint16_t *mask;
+    const uint8_t *map;
+    float *dk, *dv;
+    int B, H, Hkv, N, Np, M, Mp, DK, DV;
+    int part_heads, nqb, nkb;
+    float scale;
+};
+
+constexpr int kKW = 4, kKNT = 64 * kKW;
+constexpr int kKBC = 32 * kKW;   // keys per work-group
+constexpr int kKBR = kTR;        // queries per step
+constexpr int kKList = 512;      // live query steps listed at a time
+
+// LDS stages: the Q tile, the dO tile and the LSE/D block of one step each.
 template <int DKP, int DVP>
-struct B16Cfg {
-    static constexpr int W = 4, NT = 64 * W;
-    static constexpr int BC = 32 * W;   // keys per work-group (32 per wave)
-    static constexpr int BR = 32;       // queries per step
-    using QL = RowTile<DKP>;            // layout of Q tiles and of the K block
-    using OL = RowTile<DVP>;            // layout of dO tiles
-    static constexpr int QCN = BR * DKP / 4, OCN = BR * DVP / 8;   // 16-byte chunks of a Q / dO tile
-    static constexpr int QCH = (QCN + NT - 1) / NT;   // f32x4 chunks of a Q tile per thread
-    static constexpr int OCH = (OCN + NT - 1) / NT;   // 16-byte chunks of a bf16 dO tile per thread
-    static constexpr int LIST = 2048;                 // live query tiles listed at a time
+struct KStages {
+    static constexpr int kQ = DKP / 8 * kChunkL, kO = DVP / 8 * kChunkL, kS = kStatsTile * 4;
+    static constexpr int kBytes = kQ + kO + kS;
+    static constexpr int kFit = (160 * 1024 - 4 * kKList - 256) / kBytes;
+    static constexpr int N = kFit > 4 ? 4 : kFit;
+    static_assert(N >= 2, "two LDS stages must fit");
 };
 
 template <int DKP, int DVP>
-struct B16Tile {
-    u32x4 q[B16Cfg<DKP, DVP>::QCH];   // f32 Q (4 floats per chunk)
-    u32x4 o[B16Cfg<DKP, DVP>::OCH];   // bf16 dO (8 per chunk)
-    float lse, del;
-};
-
-// Per-(batch, head) views of the query-side tensors.
-struct B16Head {
-    rsrc_t q, o, lse, del;
-    const float *qp;   // plain pointer to Q for the head-dim-padded (checked) loads
-};
-
-// Global loads of query tile rows q0..q0+BR-1 into registers.  Rows at or past N
-// read as zero through the buffer bounds; EXACT (DK == DKP) needs no other
-// check, otherwise the Q columns past DK are zero-filled explicitly.
-template <int DKP, int DVP, bool EXACT>
-__device__ __forceinline__ void b16_load(B16Tile<DKP, DVP> &t, const B16Head &hd, int q0, int N, int DK,
-                                         int vecK, int tid)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_kernel(KvArgs p)
 {
-    using C = B16Cfg<DKP, DVP>;
-#pragma unroll
-    for (int i = 0; i < C::QCH; ++i) {
-        const int c = tid + C::NT * i;
-        if (C::QCN % C::NT != 0 && c >= C::QCN) break;
-        const int n = q0 + c / (DKP / 4), col = 4 * (c % (DKP / 4));
-        if constexpr (EXACT) {
-            t.q[i] = buf_load16(hd.q, (uint32_t)(n * DK + col) * 4u);
-        } else {
-            const f32x4 x = n < N ? load_row4(hd.qp + (size_t)n * DK, col, DK, vecK) : f32x4{0.f, 0.f, 0.f, 0.f};
-            t.q[i] = __builtin_bit_cast(u32x4, x);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::OCH; ++i) {
-        const int c = tid + C::NT * i;
-        if (C::OCN % C::NT != 0 && c >= C::OCN) break;
-        const int n = q0 + c / (DVP / 8), col = 8 * (c % (DVP / 8));
-        t.o[i] = buf_load16(hd.o, (uint32_t)(n * DVP + col) * 2u);
-    }
-    if (tid < C::BR) {
-        t.lse = buf_load_f32(hd.lse, (uint32_t)(q0 + tid) * 4u);   // 0 past N: harmless, Q = dO = 0 there
-        t.del = buf_load_f32(hd.del, (uint32_t)(q0 + tid) * 4u);
-    }
-}
+    using ST = KStages<DKP, DVP>;
+    constexpr int NS = ST::N;
+    constexpr int QCH = DKP / 8 / kKW, OCH = DVP / 8 / kKW;   // chunk columns copied per wave
+    static_assert(QCH * 8 * kKW == DKP && OCH * 8 * kKW == DVP, "tile copy split");
+    constexpr int PER = QCH + OCH + 1;                         // copies per wave and step
+    __shared__ __attribute__((aligned(16))) char sQO[NS * ST::kBytes];
+    __shared__ int sList[kKList];
+    __shared__ int sCount[kKW + 1];
 
-template <int DKP, int DVP>
-__device__ __forceinline__ void b16_store(const B16Tile<DKP, DVP> &t, __bf16 *sQ, __bf16 *sO, float *sL,
-                                          float *sD, int tid)
-{
-    using C = B16Cfg<DKP, DVP>;
-#pragma unroll
-    for (int i = 0; i < C::QCH; ++i) {
-        const int c = tid + C::NT * i;
-        if (C::QCN % C::NT != 0 && c >= C::QCN) break;
-        *reinterpret_cast<bf16x4 *>(&sQ[C::QL::off(c / (DKP / 4), 4 * (c % (DKP / 4)))]) =
-            to_bf16x4(__builtin_bit_cast(f32x4, t.q[i]));
-    }
-#pragma unroll
-    for (int i = 0; i < C::OCH; ++i) {
-        const int c = tid + C::NT * i;
-        if (C::OCN % C::NT != 0 && c >= C::OCN) break;
-        *reinterpret_cast<u32x4 *>(&sO[C::OL::off(c / (DVP / 8), 8 * (c % (DVP / 8)))]) = t.o[i];
-    }
-    if (tid < C::BR) {
-        // log2 units; an all-masked row (LSE = -inf) becomes +inf so that P = 0
-        sL[tid] = (t.lse == -INFINITY) ? INFINITY : t.lse * kLog2e;
-        sD[tid] = t.del;
-    }
-}
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
+    const uint32_t qo_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sQO;
 
-// One query tile against the key block: S, dP, P, dS, dV and dK.
-// The causal rule is applied as "query >= thr" (thr = INT_MIN when the tile
-// is not causal); masked adds the additive mask values read from memory.
-template <int DKP, int DVP>
-__device__ __forceinline__ void b16_step(const BwdArgs &p, const __bf16 *Qb, const __bf16 *Ob, const float *sLb,
-                                         const float *sDb, const __bf16 *sK, const bf16x8 *vf,
-                                         f32x16 *dkacc, f32x16 *dvacc, int q0, int thr, bool masked, bool fast,
-                                         int mykey, float kbias, float sl2, int w, int lane)
-{
-    using C = B16Cfg<DKP, DVP>;
-    using QL = typename C::QL;
-    using OL = typename C::OL;
-    const int half = lane >> 5, l32 = lane & 31;
-
-    // ---- S = Q K^T and dP = dO V^T (lane = key, rows = queries)
-    f32x16 sacc = zero16(), pacc = zero16();
-#pragma unroll
-    for (int t0 = 0; t0 < DKP / 16; t0 += 8) {
-        constexpr int T = DKP / 16 < 8 ? DKP / 16 : 8;
-        bf16x8 bk[T], a[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t >= DKP / 16) break;
-            bk[t] = *reinterpret_cast<const bf16x8 *>(&sK[QL::off(32 * w + l32, 16 * (t0 + t) + 8 * half)]);
-            a[t] = *reinterpret_cast<const bf16x8 *>(&Qb[QL::off(l32, 16 * (t0 + t) + 8 * half)]);
-        }
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t >= DKP / 16) break;
-            sacc = mfma_bf16(a[t], bk[t], sacc);
-        }
-    }
-#pragma unroll
-    for (int t0 = 0; t0 < DVP / 16; t0 += 8) {
-        constexpr int T = DVP / 16 < 8 ? DVP / 16 : 8;
-        bf16x8 a[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t >= DVP / 16) break;
-            a[t] = *reinterpret_cast<const bf16x8 *>(&Ob[OL::off(l32, 16 * (t0 + t) + 8 * half)]);
-        }
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            if (t0 + t >= DVP / 16) break;
-            pacc = mfma_bf16(a[t], vf[t0 + t], pacc);
-        }
-    }
-
-    // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a tile with
-    // every key visible (fast) folds the scale into the exponent
-    const float mul = fast ? sl2 : 1.f;
-    if (!fast) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float x = sacc[r] * sl2 + kbias;
-            sacc[r] = (q0 + crow(r, half) >= thr) ? x : -INFINITY;
-        }
-    }
-    if (masked) {
-        const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int n = min(q0 + crow(r, half), p.N - 1);
-            sacc[r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
-        }
-    }
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const int qr = 8 * r4 + 4 * half;
-        const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&sLb[qr]);
-        const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&sDb[qr]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r = 4 * r4 + c;
-            const float P = fast_exp2(__builtin_fmaf(sacc[r], mul, -lse4[c]));
-            sacc[r] = P;
-            pacc[r] = P * (pacc[r] - del4[c]);
-        }
-    }
-
-    // ---- the bf16 A operands of dV and dK
-    bf16x8 pa[2], da[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        float pv[8], dv8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pv[i] = sacc[8 * u + i];
-            dv8[i] = pacc[8 * u + i];
-        }
-        pa[u] = to_bf16x8(pv);
-        da[u] = to_bf16x8(dv8);
-    }
-
-    // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys);
-    // query rows of slots 0-3 are 16u + 4*half + 0..3, slots 4-7 are 8 further
-    {
-        bf16x8 bo[DVP / 32][2];
-#pragma unroll
-        for (int dt = 0; dt < DVP / 32; ++dt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) bo[dt][u] = tile_col8<OL>(Ob, 16 * u + 4 * half, 8, dt * 32, lane);
-#pragma unroll
-        for (int dt = 0; dt < DVP / 32; ++dt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) dvacc[dt] = mfma_bf16(pa[u], bo[dt][u], dvacc[dt]);
-    }
-    {
-        bf16x8 bq[DKP / 32][2];
-#pragma unroll
-        for (int dt = 0; dt < DKP / 32; ++dt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) bq[dt][u] = tile_col8<QL>(Qb, 16 * u + 4 * half, 8, dt * 32, lane);
-#pragma unroll
-        for (int dt = 0; dt < DKP / 32; ++dt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) dkacc[dt] = mfma_bf16(da[u], bq[dt][u], dkacc[dt]);
-    }
-}
-
-template <int DKP, int DVP, bool EXACT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_kernel(BwdArgs p)
-{
-    using C = B16Cfg<DKP, DVP>;
-    using QL = typename C::QL;
-    using OL = typename C::OL;
-    constexpr int BC = C::BC, BR = C::BR, NT = C::NT, W = C::W;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[BC * QL::kLd];         // K block, row-major
-    __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BR * QL::kLd];      // Q tiles (double buffer)
-    __shared__ __attribute__((aligned(16))) __bf16 sO[2][BR * OL::kLd];      // dO tiles
-    __shared__ __attribute__((aligned(16))) float sL[2][BR];                 // LSE (log2 units)
-    __shared__ __attribute__((aligned(16))) float sD[2][BR];                 // D
-    __shared__ int sList[C::LIST];                                           // live tiles: 4*index + class
-    __shared__ int sCount[W + 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+    // ---- work-group -> (key block, head): first key blocks first (under a causal
+    // mask they see the most queries); heads dealt to the XCDs in contiguous ranges
     const int HB = p.H * p.B;
-    const int j = blockIdx.x / HB, hb = blockIdx.x % HB;  // key block slowest: heaviest first when causal
+    int kb, hb;
+    if (HB % 8 == 0) {
+        const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HB / 8;
+        kb = jj / per;
+        hb = xcd * per + jj % per;
+    } else {
+        kb = blockIdx.x / HB;
+        hb = blockIdx.x % HB;
+    }
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
-    const int key0 = j * BC;
+    const int key0 = kb * kKBC;
     const int mykey = key0 + 32 * w + l32;  // this lane's key in the C layout of S and dP
-    const bool keyok = mykey < p.M;
-    const float kbias = keyok ? 0.f : -INFINITY;  // keys past M never get weight
-    const float *kh = p.k + (size_t)p.DK * p.M * (g + p.Hkv * b);
-    const float *vh = p.v + (size_t)p.DV * p.M * (g + p.Hkv * b);
-    const size_t hrow = (size_t)p.N * (h + p.H * b);  // first row of this (batch, head)
-    B16Head hd;
-    hd.qp = p.q + hrow * p.DK;
-    hd.q = make_rsrc(hd.qp, (uint32_t)(p.N * p.DK) * 4u);
-    hd.o = make_rsrc(p.dO16 + hrow * DVP, (uint32_t)(p.N * DVP) * 2u);
-    hd.lse = make_rsrc(p.lse + hrow, (uint32_t)p.N * 4u);
-    hd.del = make_rsrc(p.delta + hrow, (uint32_t)p.N * 4u);
-    const int nqt = (p.N + BR - 1) / BR;
+    const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
     const float sl2 = p.scale * kLog2e;
 
-    // ---- the key block: bf16 rows in LDS (B operand of S = Q K^T), and the B
-    // operand of dP = dO V^T in registers (lane = key)
-    for (int c = tid; c < BC * (DKP / 4); c += NT) {
-        const int r = c / (DKP / 4), col = 4 * (c % (DKP / 4));
-        const int key = key0 + r;
-        const f32x4 x = key < p.M ? load_row4(kh + (size_t)p.DK * key, col, p.DK, p.vecK)
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<bf16x4 *>(&sK[QL::off(r, col)]) = to_bf16x4(x);
-    }
-    bf16x8 vf[DVP / 16];
+    // ---- this lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
+    bf16x8 kf[DKP / 16], vf[DVP / 16];
     {
-        const float *vr = vh + (size_t)p.DV * (keyok ? mykey : 0);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const __bf16 *kh = p.k16 + (size_t)(g + p.Hkv * b) * p.Mp * DKP;
+        const __bf16 *vh = p.v16 + (size_t)(g + p.Hkv * b) * p.Mp * DVP;
+        const bool in = mykey < p.Mp;
+        const bf16x8 z = {};
 #pragma unroll
-        for (int t = 0; t < DVP / 16; ++t) {
-            const f32x4 lo = keyok ? load_row4(vr, 16 * t + 8 * half, p.DV, p.vecV) : z;
-            const f32x4 hi = keyok ? load_row4(vr, 16 * t + 8 * half + 4, p.DV, p.vecV) : z;
-            vf[t] = __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int t = 0; t < DKP / 16; ++t)
+            kf[t] = in ? *reinterpret_cast<const bf16x8 *>(kh + tile_elem(mykey, 16 * t + 8 * half, DKP)) : z;
+#pragma unroll
+        for (int t = 0; t < DVP / 16; ++t)
+            vf[t] = in ? *reinterpret_cast<const bf16x8 *>(vh + tile_elem(mykey, 16 * t + 8 * half, DVP)) : z;
     }
     f32x16 dkacc[DKP / 32], dvacc[DVP / 32];
 #pragma unroll
@@ -304,40 +129,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
 
-    for (int seg = 0; seg < nqt; seg += C::LIST) {
-        // ---- ordered list of the live query tiles of this segment (block map)
-        const int count = build_live_list<W>(sList, sCount, seg, min(seg + C::LIST, nqt), tid, lane, w, [&](int it) {
-            return tile_class(p.map, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile, key0 / kMapTile,
-                              BC / kMapTile);
+    const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // first tile row of this head
+    const rsrc_t rq = make_rsrc(p.q16 + qhead * DKP, (uint32_t)(p.Np * DKP) * 2u);
+    const rsrc_t ro = make_rsrc(p.o16 + qhead * DVP, (uint32_t)(p.Np * DVP) * 2u);
+    const rsrc_t rs = make_rsrc(p.stats + qhead / 64 * kStatsTile, (uint32_t)(p.Np / 64 * kStatsTile) * 4u);
+
+    // copies of query step it into stage bf: Q and dO chunk columns split over the
+    // waves, lanes 0-7 of each wave copy a quarter of the LSE/D block
+    auto issue = [&](int it, int bf) {
+        const uint32_t stg = qo_lds + (uint32_t)(bf * ST::kBytes);
+#pragma unroll
+        for (int i = 0; i < QCH; ++i) {
+            const int c = i * kKW + w;
+            lds_copy16(rq, stg + c * kChunkL, (uint32_t)(it * DKP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
+        }
+#pragma unroll
+        for (int i = 0; i < OCH; ++i) {
+            const int c = i * kKW + w;
+            lds_copy16(ro, stg + ST::kQ + c * kChunkL, (uint32_t)(it * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
+        }
+        if (lane < 8)
+            lds_copy16(rs, stg + ST::kQ + ST::kO + w * 128,
+                       (uint32_t)(it * kStatsTile * 4 + w * 128) + (uint32_t)lane * 16u);
+    };
+
+    const int nqt = p.Np / kKBR;
+    for (int seg = 0; seg < nqt; seg += kKList) {
+        const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
+            return tile_class(p.map, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
+                              kKBC / kMapTile);
         });
         if (count == 0) continue;
-
-        // ---- first live tile into buffer 0
-        {
-            B16Tile<DKP, DVP> t;
-            b16_load<DKP, DVP, EXACT>(t, hd, (sList[0] >> 2) * BR, p.N, p.DK, p.vecK, tid);
-            b16_store<DKP, DVP>(t, sQ[0], sO[0], sL[0], sD[0], tid);
-        }
-        __syncthreads();
-
-        int buf = 0;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < count) issue(sList[i] >> 2, i);
         for (int li = 0; li < count; ++li) {
+            wait_vm_steps<PER>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
+            __syncthreads();                                    // ... for every wave; stage li-1 is free
+            if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
             const int e = sList[li];
             const int it = e >> 2, cls = e & 3;
-            const int q0 = it * BR;
-            const bool more = li + 1 < count;
-            // prefetch the next live tile into registers (the current one again when
-            // there is none); stored to the other buffer after this step's products
-            B16Tile<DKP, DVP> nt;
-            b16_load<DKP, DVP, EXACT>(nt, hd, (more ? (sList[li + 1] >> 2) : it) * BR, p.N, p.DK, p.vecK, tid);
+            const int q0 = it * kKBR;
+            const char *Qb = sQO + (li % NS) * ST::kBytes;
+            const char *Ob = Qb + ST::kQ;
+            const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
 
-            b16_step<DKP, DVP>(p, sQ[buf], sO[buf], sL[buf], sD[buf], sK, vf, dkacc, dvacc, q0,
-                               cls == kTileCausal ? mykey : INT_MIN, cls == kTileMixed,
-                               cls == kTileFree && key0 + BC <= p.M, mykey, kbias, sl2, w, lane);
-            if (more) b16_store<DKP, DVP>(nt, sQ[buf ^ 1], sO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], tid);
-            __syncthreads();  // next tile staged; every wave is done with this one
-            buf ^= 1;
+            // ---- S = Q K^T and dP = dO V^T for two 32-query sub-tiles (lane = key)
+            f32x16 sacc[2], pacc[2];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                sacc[qq] = zero16();
+                pacc[qq] = zero16();
+                bf16x8 a[DKP / 16];
+#pragma unroll
+                for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
+#pragma unroll
+                for (int t = 0; t < DKP / 16; ++t) sacc[qq] = mfma_bf16(a[t], kf[t], sacc[qq]);
+                bf16x8 o[DVP / 16];
+#pragma unroll
+                for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
+#pragma unroll
+                for (int t = 0; t < DVP / 16; ++t) pacc[qq] = mfma_bf16(o[t], vf[t], pacc[qq]);
+            }
+
+            // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
+            // every key visible folds the scale into the exponent
+            const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
+            const float mul = fast ? sl2 : 1.f;
+            if (!fast) {
+                const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = sacc[qq][r] * sl2 + kbias;
+                        sacc[qq][r] = (q0 + 32 * qq + crow(r, half) >= thr) ? x : -INFINITY;
+                    }
+                if (cls == kTileMixed) {
+                    const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int n = min(q0 + 32 * qq + crow(r, half), p.N - 1);
+                            sacc[qq][r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
+                        }
+                }
+            }
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int qr = 32 * qq + 8 * r4 + 4 * half;
+                    const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(Sb + qr);
+                    const f32x4 del4 = *reinterpret_cast<const f32x4 *>(Sb + 64 + qr);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * r4 + c;
+                        const float P = fast_exp2(__builtin_fmaf(sacc[qq][r], mul, -lse4[c]));
+                        sacc[qq][r] = P;
+                        pacc[qq][r] = P * (pacc[qq][r] - del4[c]);
+                    }
+                }
+
+            // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
+            // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float pv[8], dv8[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        pv[i] = sacc[qq][8 * u + i];
+                        dv8[i] = pacc[qq][8 * u + i];
+                    }
+                    const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
+                    bf16x8 bo[DVP / 32], bq[DKP / 32];
+#pragma unroll
+                    for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
+#pragma unroll
+                    for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa, bo[dt], dvacc[dt]);
+#pragma unroll
+                    for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
+#pragma unroll
+                    for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da, bq[dt], dkacc[dt]);
+                }
         }
+        __syncthreads();   // every wave is done with the stages before they are refilled
     }
 
     // ---- store dK (scaled) and dV of this key block
@@ -560,46 +479,67 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     }
 }
 
-// ============================================================== launcher
+// ============================================================== launchers
 namespace {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 template <int DKP, int DVP, bool BF16>
-hipError_t run_bwd(const BwdArgs &a, hipStream_t s)
+hipError_t run_bwd_f32(const BwdArgs &a, hipStream_t s)
 {
     if constexpr (BF16) {
-        using C = B16Cfg<DKP, DVP>;
-        const dim3 grid(ceil_div(a.M, C::BC) * a.H * a.B);
-        if (a.DK == DKP)
-            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, true>), grid, dim3(C::NT), 0, s, a);
-        else
-            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, false>), grid, dim3(C::NT), 0, s, a);
+        return hipErrorInvalidValue;
     } else {
         using C = F32Cfg<DKP, DVP>;
         hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
                            0, s, a);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+}
+
+template <int DKP, int DVP, bool BF16>
+hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
+{
+    if constexpr (!BF16) {
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT), 0, s, a);
+        return hipGetLastError();
+    }
 }
 }  // namespace
 
-hipError_t launch_backward(const float *q, const float *k, const float *v, const float *dO,
-                           const __bf16 *dO16, const uint16_t *mask, const uint8_t *map,
-                           const float *lse, const float *delta, float scale, int bf16, float *dq,
-                           float *dk, float *dv, int part_heads, const Dims &d, hipStream_t s)
+hipError_t launch_backward_f32(const float *q, const float *k, const float *v, const float *dO,
+                               const uint16_t *mask, const uint8_t *map, const float *lse, const float *delta,
+                               float scale, float *dq, float *dk, float *dv, int part_heads, const Dims &d,
+                               hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
-    if (bf16 && !dO16) return hipErrorInvalidValue;
     BwdArgs a;
-    a.q = q; a.k = k; a.v = v; a.dO = dO; a.dO16 = dO16; a.mask = mask; a.map = map;
+    a.q = q; a.k = k; a.v = v; a.dO = dO; a.mask = mask; a.map = map;
     a.lse = lse; a.delta = delta; a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
-    FAB_DISPATCH_HEAD_DIMS(run_bwd, a, s, hd, bf16);
+    FAB_DISPATCH_HEAD_DIMS(run_bwd_f32, a, s, hd, false);
+}
+
+hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
+                                const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
+                                float *dv, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s)
+{
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
+    KvArgs a;
+    a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
+    a.dk = dk; a.dv = dv;
+    a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
+    a.part_heads = part_heads;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.scale = scale;
+    FAB_DISPATCH_HEAD_DIMS(run_bwd_bf16, a, s, hd, true);
 }
 
 }  // namespace fab

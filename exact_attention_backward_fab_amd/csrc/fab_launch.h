@@ -59,35 +59,46 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
                                const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s);
 
-// Delta = rowsum(d o O) [N,H,B]; zero blob[zero_lo, off_k) (the dQ slice when
-// it is accumulated by atomics, else only its pad) and the other blob pads;
-// when dO16 is given, also write d as bf16 [B][H][N][dvp] (zero-padded).
-hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, __bf16 *dO16,
-                       int dvp, int64_t zero_lo, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
-                       int64_t total, const Dims &d, hipStream_t s);
+// f32 mode prep: Delta = rowsum(d o O) [N,H,B]; zero the dQ slice [0, off_k)
+// (the atomics target) and the other blob pads.
+hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, int64_t off_k, int64_t nk,
+                       int64_t off_v, int64_t nv, int64_t total, const Dims &d, hipStream_t s);
 
-// Rows of the bf16 K / V copies are padded per head to a multiple of this.
+// bf16 mode prep: D and the LSE/D blocks (stats, [B][H][Np/64][128]) from d, O and
+// lse, d as bf16 tiles [B][H][Np][dvp] (fab_tiles.h, zero-padded), and the pads
+// of the result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)).
+hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
+                            int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
+                            int64_t total, const Dims &d, hipStream_t s);
+
+// Rows of the bf16 tiles are padded per head to a multiple of this.
 constexpr int kPackRows = 64;
 
 // f32 [heads][M][D] -> bf16 [heads][Mp][DP] in 64-row tiles stored chunk column
-// by chunk column (fab_qouter.hip); rows >= M and columns >= D zero.
+// by chunk column (fab_tiles.h); rows >= M and columns >= D zero.
 hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
                                  hipStream_t s);
 
-// Key-block-outer backward: dV, dK per key tile (stored into dk/dv with
-// per-query-head layout when part_heads != 0).  f32 mode also adds dQ by f32
-// atomics into dq (zeroed beforehand); bf16 mode leaves dQ to launch_dq and
-// reads dO from dO16 (see launch_prep).
-hipError_t launch_backward(const float *q, const float *k, const float *v, const float *dO,
-                           const __bf16 *dO16, const uint16_t *mask, const uint8_t *map,
-                           const float *lse, const float *delta, float scale, int bf16, float *dq,
-                           float *dk, float *dv, int part_heads, const Dims &d, hipStream_t s);
+// Key-block-outer backward, f32 mode: dV, dK per key tile (stored into dk/dv with
+// per-query-head layout when part_heads != 0) and dQ by f32 atomics into dq
+// (zeroed beforehand).
+hipError_t launch_backward_f32(const float *q, const float *k, const float *v, const float *dO,
+                               const uint16_t *mask, const uint8_t *map, const float *lse, const float *delta,
+                               float scale, float *dq, float *dk, float *dv, int part_heads, const Dims &d,
+                               hipStream_t s);
+
+// Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
+// (launch_pack_rows_bf16 / launch_prep, Np rows per head), K, V (Mp rows per head)
+// and the LSE/D blocks; stored as in launch_backward_f32.
+hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
+                                const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
+                                float *dv, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
 
 // Query-block-outer dQ (bf16 mode): dq [DK,N,H,B] = scale dS K, every element
-// written once.  k16 / v16 from launch_pack_rows_bf16 with Mp rows per head.
-hipError_t launch_dq(const float *q, const __bf16 *k16, const __bf16 *v16, const __bf16 *dO16, const uint16_t *mask,
-                     const uint8_t *map, const float *lse, const float *delta, float scale, float *dq, int Mp,
-                     const Dims &d, hipStream_t s);
+// written once; inputs as for launch_backward_bf16.
+hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16, const __bf16 *v16,
+                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, int Np, int Mp, const Dims &d,
+                     hipStream_t s);
 
 // dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] for one of dK / dV.
 hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s);

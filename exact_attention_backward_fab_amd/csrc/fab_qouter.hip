@@ -1,8 +1,6 @@
-// fab_qouter.hip -- bf16 row packing and the query-block-outer kernels (gfx950).
+// fab_qouter.hip -- the query-block-outer kernels (gfx950), on the bf16 tiles of
+// fab_tiles.h.
 //
-//   pack_rows_bf16_kernel  f32 rows -> bf16 64-row tiles (zero-padded), stored so
-//                          that a tile is copied linearly into LDS and read there
-//                          without address arithmetic
 //   fwd_bf16_kernel        O = softmax(scale S + mask) V and the row LSE by query
 //                          blocks, with the running max and running sum of the
 //                          labml "Flash Attention" page ("Flash Attention
@@ -20,61 +18,9 @@
 
 #include "fab_common.h"
 #include "fab_launch.h"
+#include "fab_tiles.h"
 
 namespace fab {
-
-// ============================================================== bf16 tiles
-// The bf16 copies of K and V are stored as tiles of 64 rows, each tile as its
-// 16-byte chunk columns one after the other: chunk c (head-dim columns 8c..8c+7)
-// of row r of a tile lies at byte c * 1024 + r * 16 of the tile.  One chunk column
-// is thus 1 KiB of contiguous memory, the unit the global -> LDS copies move.  In
-// LDS each chunk column gets 128 bytes of padding (stride kChunkL), so that
-//   * 16-byte row reads (matrix-core operands with one row per lane) are a
-//     contiguous 512-byte run per lane half, and
-//   * transposing 8-byte reads (ds_read_b64_tr_b16) of 4 rows x 4 chunk columns
-//     hit every LDS bank exactly twice,
-// and every address in a step is a per-lane base plus a compile-time offset.
-constexpr int kTR = 64;              // rows per tile
-constexpr int kChunkG = 1024;        // bytes per chunk column of a tile, global memory
-constexpr int kChunkL = 1152;        // ... in LDS
-
-// src: heads of M rows of D floats; dst: heads of Mp >= M rows (Mp a multiple of
-// 64) of DP bf16 in the tile layout above; rows >= M and columns >= D zero.
-__global__ __launch_bounds__(256) void pack_rows_bf16_kernel(const float *__restrict__ src, __bf16 *__restrict__ dst,
-                                                             int64_t heads, int M, int Mp, int D, int DP, int vec)
-{
-    const int nch = DP / 8;
-    const int64_t total = heads * Mp * nch;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        // i enumerates (head, tile, chunk column, row in tile): consecutive threads
-        // write consecutive 16-byte chunks of the destination
-        const int64_t hd = i / ((int64_t)Mp * nch);
-        const int rem = (int)(i - hd * Mp * nch);
-        const int tile = rem / (kTR * nch), in = rem - tile * kTR * nch;
-        const int ch = in / kTR, r = in - ch * kTR;
-        const int m = tile * kTR + r;
-        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-        if (m < M) {
-            const float *sr = src + (hd * M + m) * D;
-            lo = load_row4(sr, 8 * ch, D, vec);
-            hi = load_row4(sr, 8 * ch + 4, D, vec);
-        }
-        *reinterpret_cast<bf16x8 *>(dst + 8 * i) =
-            __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-}
-
-hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
-                                 hipStream_t s)
-{
-    const int64_t work = heads * Mp * (DP / 8);
-    if (work == 0) return hipSuccess;
-    const int grid = (int)std::min<int64_t>((work + 255) / 256, 16384);
-    hipLaunchKernelGGL(pack_rows_bf16_kernel, dim3(grid), dim3(256), 0, s, src, dst, heads, M, Mp, D, DP,
-                       (int)(D % 4 == 0));
-    return hipGetLastError();
-}
 
 // Work-group shape of the query-block-outer kernels: 4 waves, 32 queries each;
 // keys stream through LDS one 64-row tile (a step) at a time.
@@ -96,26 +42,6 @@ struct QStages {
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-// Per-lane byte offsets inside an LDS tile (see the tile layout above):
-//   row operand   16 bytes of row l32 (+32 kk), chunk column 2t + half:
-//                 row_off + 512 kk + 2304 t
-//   transposed    rows 16u + 4 half + (j >> 2) (+32 kk, +8 for the upper 4 slots),
-//                 columns 32 dt + 16 grp + 4 (j & 3), j = lane & 15, grp = bit 4 of
-//                 the lane: tr_off + 4608 dt + 512 kk + 256 u (+128)
-__device__ __forceinline__ int tile_row_off(int lane) { return (lane >> 5) * kChunkL + (lane & 31) * 16; }
-__device__ __forceinline__ int tile_tr_off(int lane)
-{
-    const int j = lane & 15, grp = (lane >> 4) & 1, half = lane >> 5;
-    return (2 * grp + ((j & 3) >> 1)) * kChunkL + ((j >> 2) + 4 * half) * 16 + (j & 1) * 8;
-}
-__device__ __forceinline__ bf16x8 lds_row8(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ __forceinline__ bf16x8 lds_tr8(const char *p)
-{
-    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const __bf16 *>(p));
-    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const __bf16 *>(p + 128));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Work-group -> (query tile, head).  Consecutive work-groups are dealt round-robin
 // to the 8 XCDs; when the heads split evenly over the XCDs, each XCD gets a
 // contiguous range of heads (the heads of a key/value group share its K/V rows in
@@ -135,29 +61,6 @@ __device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB)
         r.hb = bid % HB;
     }
     return r;
-}
-
-// One 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i
-// writes LDS bytes [la + 16 i, la + 16 i + 16); la must be wave-uniform.  Issued
-// as inline assembly so that the compiler does not make every later LDS read wait
-// for it; the caller orders it with explicit vmcnt waits and barriers.  m0 is not
-// used by the compiler in these kernels (the buffer copy is their only m0 user);
-// the copy reads m0 one wait state after it is written.
-__device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t la, uint32_t voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(la), "v"(voff), "s"(r) : "memory", "m0");
-}
-
-// Waits until at most k * PER of this wave's vector-memory operations are in flight.
-template <int PER>
-__device__ __forceinline__ void wait_vm_steps(int k)
-{
-    static_assert(3 * PER <= 63, "vmcnt range");
-    if (k <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (k == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
-    else if (k == 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * PER) : "memory");
 }
 
 // Streams the live key steps (block map) of one query block through the LDS
@@ -415,14 +318,13 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 
 // ============================================================== dQ by query blocks
 struct DqArgs {
-    const float *q;                 // f32 [B,H,N,DK]
-    const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
-    const __bf16 *dO16;             // bf16 [B,H,N,DVP]
+    const __bf16 *q16, *o16;        // bf16 tiles [B,H,Np,DKP] / [B,H,Np,DVP], rows >= N zero
+    const float *stats;             // LSE/D blocks [B,H,Np/64][128]
+    const __bf16 *k16, *v16;        // bf16 tiles [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP], rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
-    const float *lse, *delta;       // [N,H,B]
     float *dq;                      // [DK,N,H,B] slice of the result blob
-    int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK;
+    int B, H, Hkv, N, Np, M, Mp, DK, DV, nqb, nkb;
     float scale;
 };
 
@@ -451,21 +353,26 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const rsrc_t rv = make_rsrc(p.v16 + kvrow * DVP, (uint32_t)(p.Mp * DVP) * 2u);
 
     // ---- this lane's query: LSE (log2 units, +inf when all-masked or past N), D,
-    // and the B operands Q^T and dO^T of S^T = K Q^T and dP^T = V dO^T
+    // and the B operands Q^T and dO^T of S^T = K Q^T and dP^T = V dO^T (rows past
+    // the padded extent Np read as zero with no weight)
     float lse2 = INFINITY, dl = 0.f;
-    if (qok) {
-        const float L = p.lse[hrow + myq];
-        lse2 = (L == -INFINITY) ? INFINITY : L * kLog2e;
-        dl = p.delta[hrow + myq];
-    }
     bf16x8 qf[DKP / 16], of[DVP / 16];
-    load_q_operand<DKP>(qf, p.q + (hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half);
     {
-        const __bf16 *orow = p.dO16 + (hrow + (qok ? myq : 0)) * DVP;
+        const bool in = myq < p.Np;
+        const size_t qhead = (size_t)(h + p.H * b) * p.Np;
+        const __bf16 *qh16 = p.q16 + qhead * DKP;
+        const __bf16 *oh16 = p.o16 + qhead * DVP;
+        const bf16x8 z = {};
 #pragma unroll
-        for (int t = 0; t < DVP / 16; ++t) {
-            const u32x4 x = qok ? *reinterpret_cast<const u32x4 *>(orow + 16 * t + 8 * half) : u32x4{0u, 0u, 0u, 0u};
-            of[t] = __builtin_bit_cast(bf16x8, x);
+        for (int t = 0; t < DKP / 16; ++t)
+            qf[t] = in ? *reinterpret_cast<const bf16x8 *>(qh16 + tile_elem(myq, 16 * t + 8 * half, DKP)) : z;
+#pragma unroll
+        for (int t = 0; t < DVP / 16; ++t)
+            of[t] = in ? *reinterpret_cast<const bf16x8 *>(oh16 + tile_elem(myq, 16 * t + 8 * half, DVP)) : z;
+        if (in) {
+            const float *st = p.stats + (qhead / 64 + myq / 64) * kStatsTile + (myq & 63);
+            lse2 = st[0];
+            dl = st[64];
         }
     }
 
@@ -586,18 +493,17 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
 }
 
-hipError_t launch_dq(const float *q, const __bf16 *k16, const __bf16 *v16, const __bf16 *dO16, const uint16_t *mask,
-                     const uint8_t *map, const float *lse, const float *delta, float scale, float *dq, int Mp,
-                     const Dims &d, hipStream_t s)
+hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16, const __bf16 *v16,
+                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, int Np, int Mp, const Dims &d,
+                     hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
     DqArgs a;
-    a.q = q; a.k16 = k16; a.v16 = v16; a.dO16 = dO16; a.mask = mask; a.map = map;
-    a.lse = lse; a.delta = delta; a.dq = dq;
-    a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
+    a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
+    a.dq = dq;
+    a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
-    a.vecK = (d.DK % 4 == 0);
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_dq, a, s, hd, true);
 }
