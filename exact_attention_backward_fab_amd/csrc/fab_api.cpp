@@ -240,12 +240,12 @@ struct ProfScope {
         FAB_HIP(call, what);                    \
     } while (0)
 
-// The bf16 copies of K and V (bf16 mode).
-int launch_pack(const Plan &pl, const float *k, const float *v, __bf16 *k16, __bf16 *v16, hipStream_t s)
+// The bf16 tiles of Q (when q16 is given), K and V (bf16 mode), one launch.
+int launch_pack(const Plan &pl, const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
+                __bf16 *v16, hipStream_t s)
 {
-    const int64_t heads = (int64_t)pl.d.Hkv * pl.d.B;
-    FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(k, k16, heads, pl.d.M, pl.mp, pl.d.DK, pl.dkp, s), "K pack launch");
-    FAB_LAUNCH(kPack, fab::launch_pack_rows_bf16(v, v16, heads, pl.d.M, pl.mp, pl.d.DV, pl.dvp, s), "V pack launch");
+    FAB_LAUNCH(kPack, fab::launch_pack_qkv(q16 ? q : nullptr, k, v, q16, k16, v16, pl.np, pl.mp, pl.d, s),
+               "pack launch");
     return FAB_OK;
 }
 
@@ -379,7 +379,7 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
     __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
     if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mask, map, pl.d, s), "block map launch");
-    if (bf16) FAB_TRY(launch_pack(pl, k, v, k16, v16, s));
+    if (bf16) FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, s));
     FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, use_mask ? mask : nullptr, map, scale, O, lse, s));
     return FAB_OK;
 }
@@ -424,8 +424,9 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     const int bf16 = mode == FAB_MODE_BF16;
     __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
     __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
+    __bf16 *q16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_q16) : nullptr;
     if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
-    if (bf16) FAB_TRY(launch_pack(pl, k, v, k16, v16, s));
+    if (bf16) FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, s));
     const float *Ou = O, *lseu = lse;
     if (!have) {
         float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
@@ -435,7 +436,6 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
         lseu = lw;
     }
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
-    __bf16 *q16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_q16) : nullptr;
     __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
     float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
     // bf16: dQ is written once by the query-block-outer kernel (only its pad is
@@ -450,9 +450,6 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     if (bf16) {
-        FAB_LAUNCH(kPack,
-                   fab::launch_pack_rows_bf16(q, q16, (int64_t)pl.d.H * pl.d.B, pl.d.N, pl.np, pl.d.DK, pl.dkp, s),
-                   "Q pack launch");
         FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, pl.gqa ? 1 : 0,
                                                    pl.np, pl.mp, pl.d, s),
                    "backward launch");

@@ -22,23 +22,41 @@
 namespace fab {
 
 // ============================================================== block map
-__global__ __launch_bounds__(64) void block_map_kernel(const uint16_t *__restrict__ mask,
-                                                       uint8_t *__restrict__ map, int N, int M,
-                                                       int nkb)
+// One wave per 32x32 block, 4 blocks per work-group: lane l reads row l/2 of the
+// block, columns 16 (l & 1)..+15 (two 16-byte loads when the row is aligned).
+__global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restrict__ mask,
+                                                        uint8_t *__restrict__ map, int N, int M,
+                                                        int nqb, int nkb)
 {
-    const int kb = blockIdx.x, qb = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nqb * nkb) return;   // whole waves: the votes below stay within one wave
+    const int qb = blk / nkb, kb = blk - qb * nkb;
+    const int lane = threadIdx.x & 63;
     const int n = qb * kMapTile + (lane >> 1);
     const int m0 = kb * kMapTile + (lane & 1) * 16;
     bool all_inf = true, all_zero = true, causal = true;
     if (n < N) {
         const uint16_t *row = mask + (size_t)n * M;
+        uint16_t x[16];
+        if ((M & 7) == 0 && m0 + 16 <= M) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(row + m0);
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(row + m0 + 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = (uint16_t)(a[i] & 0xFFFFu);
+                x[2 * i + 1] = (uint16_t)(a[i] >> 16);
+                x[8 + 2 * i] = (uint16_t)(b[i] & 0xFFFFu);
+                x[8 + 2 * i + 1] = (uint16_t)(b[i] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = m0 + i < M ? row[m0 + i] : (uint16_t)0xFC00u;
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = m0 + i;
             if (m < M) {
-                const uint16_t x = row[m];
-                const bool is_inf = x == 0xFC00u, is_zero = (x & 0x7FFFu) == 0;
+                const bool is_inf = x[i] == 0xFC00u, is_zero = (x[i] & 0x7FFFu) == 0;
                 all_inf = all_inf && is_inf;
                 all_zero = all_zero && is_zero;
                 causal = causal && (m <= n ? is_zero : is_inf);
@@ -107,118 +125,169 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 }
 
 // ============================================================== bf16 tiles
-// Row m of head hd = hh + H*bb of src starts at src + hh*sh + bb*sb + m*rs floats.
-struct PackArgs {
-    const float *src, *O;             // O: second input of the prep (rows like src), or NULL
-    const float *lse;                 // prep: row LSE [N,H,B] (natural log)
-    __bf16 *dst;                      // tiles [heads][Mp][DP]
-    float *stats;                     // prep: LSE/D blocks [heads][Mp/64][128]
-    float *blob;                      // prep: result blob whose pads are zeroed (work-group 0)
+// One packing job: heads of M rows of D floats -> bf16 tiles [heads][Mp][DP].  Row
+// m of head hd = hh + H*bb starts at src + hh*sh + bb*sb + m*rs floats.
+struct PackJob {
+    const float *src;
+    __bf16 *dst;
     int64_t sh, sb, rs;
-    int H, M, Mp, D, DP, vec;
+    int H, M, Mp, D, vec;
+    int tiles;                        // heads * Mp / 64: work-groups of this job
+};
+
+// Extra outputs of the bf16-mode prep (second input O, LSE/D blocks, blob pads).
+struct PrepExtra {
+    const float *O;                   // rows like the job's src
+    const float *lse;                 // row LSE [N,H,B] (natural log)
+    float *stats;                     // LSE/D blocks [heads][Mp/64][128]
+    float *blob;                      // result blob whose pads are zeroed (work-group 0)
     int64_t pad_lo[3], pad_hi[3];
 };
 
+// One 64-row tile of job j (tile index bt within the job), through LDS so that the
+// row reads and the tile writes are both contiguous.  With x (prep), also the
+// row dot products with O and the tile's LSE/D block.
 template <int DP>
-__global__ __launch_bounds__(256) void pack_tiles_kernel(PackArgs a)
+__device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepExtra *x)
 {
     constexpr int C4 = DP / 4;                        // 4-column groups per row
+    constexpr int IT = (64 * C4 + 255) / 256;         // per thread
     __shared__ __attribute__((aligned(16))) __bf16 tile[64 * DP];
     __shared__ float part[64][C4 + 1];
     const int tid = threadIdx.x;
-    const int ntile = a.Mp / 64;
-    const int hd = blockIdx.x / ntile, t = blockIdx.x - hd * ntile;
-    const int hh = hd % a.H, bb = hd / a.H;
-    const float *base = a.src + hh * a.sh + bb * a.sb;
-    const float *obase = a.O ? a.O + hh * a.sh + bb * a.sb : nullptr;
+    const int ntile = j.Mp / 64;
+    const int hd = bt / ntile, t = bt - hd * ntile;
+    const int hh = hd % j.H, bb = hd / j.H;
+    const float *base = j.src + hh * j.sh + bb * j.sb;
+    const float *obase = x ? x->O + hh * j.sh + bb * j.sb : nullptr;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    constexpr int IT = (64 * C4 + 255) / 256;         // 4-column groups per thread
     // all loads of the tile first (independent, so they are in flight together)
-    f32x4 x[IT], y[IT];
+    f32x4 xv[IT], yv[IT];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int idx = tid + 256 * i;
         const int r = idx / C4, col = 4 * (idx - r * C4);
         const int m = t * 64 + r;
-        const bool ok = idx < 64 * C4 && m < a.M;
-        x[i] = ok ? load_row4(base + m * a.rs, col, a.D, a.vec) : z;
-        y[i] = (ok && obase) ? load_row4(obase + m * a.rs, col, a.D, a.vec) : z;
+        const bool ok = idx < 64 * C4 && m < j.M;
+        xv[i] = ok ? load_row4(base + m * j.rs, col, j.D, j.vec) : z;
+        yv[i] = (ok && obase) ? load_row4(obase + m * j.rs, col, j.D, j.vec) : z;
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int idx = tid + 256 * i;
         if (idx >= 64 * C4) break;
         const int r = idx / C4, col = 4 * (idx - r * C4);
-        *reinterpret_cast<bf16x4 *>(&tile[((col >> 3) * 64 + r) * 8 + (col & 7)]) = to_bf16x4(x[i]);
-        if (obase) part[r][col >> 2] = x[i][0] * y[i][0] + x[i][1] * y[i][1] + x[i][2] * y[i][2] + x[i][3] * y[i][3];
+        *reinterpret_cast<bf16x4 *>(&tile[((col >> 3) * 64 + r) * 8 + (col & 7)]) = to_bf16x4(xv[i]);
+        if (obase) part[r][col >> 2] = xv[i][0] * yv[i][0] + xv[i][1] * yv[i][1] + xv[i][2] * yv[i][2] + xv[i][3] * yv[i][3];
     }
     __syncthreads();
-    bf16x8 *out = reinterpret_cast<bf16x8 *>(a.dst + ((size_t)hd * a.Mp + t * 64) * DP);
+    bf16x8 *out = reinterpret_cast<bf16x8 *>(j.dst + ((size_t)hd * j.Mp + t * 64) * DP);
     for (int i = tid; i < 8 * DP; i += 256) out[i] = reinterpret_cast<const bf16x8 *>(tile)[i];
-    if (obase && tid < 64) {
+    if (x && tid < 64) {
         const int m = t * 64 + tid;
         float dsum = 0.f;
         for (int c = 0; c < C4; ++c) dsum += part[tid][c];
-        float *st = a.stats + ((size_t)hd * ntile + t) * kStatsTile + tid;
+        float *st = x->stats + ((size_t)hd * ntile + t) * kStatsTile + tid;
         float lse2 = INFINITY;   // rows past M (padding) and all-masked rows: no weight
-        if (m < a.M) {
-            const float L = a.lse[(size_t)a.M * hd + m];
+        if (m < j.M) {
+            const float L = x->lse[(size_t)j.M * hd + m];
             if (L != -INFINITY) lse2 = L * kLog2e;
         }
         st[0] = lse2;
-        st[64] = m < a.M ? dsum : 0.f;
+        st[64] = m < j.M ? dsum : 0.f;
     }
-    if (a.blob && blockIdx.x == 0 && tid < 4)
+}
+
+// Up to three packing jobs in one launch (Q and K with DKP columns, V with DVP):
+// work-groups [0, t0) job 0, [t0, t0 + t1) job 1, the rest job 2.
+struct PackJobs {
+    PackJob j[3];
+};
+
+template <int DKP, int DVP>
+__global__ __launch_bounds__(256) void pack_qkv_kernel(PackJobs a)
+{
+    int bt = blockIdx.x;
+    if (bt < a.j[0].tiles) {
+        pack_tile<DKP>(a.j[0], bt, nullptr);
+        return;
+    }
+    bt -= a.j[0].tiles;
+    if (bt < a.j[1].tiles) {
+        pack_tile<DKP>(a.j[1], bt, nullptr);
+        return;
+    }
+    bt -= a.j[1].tiles;
+    pack_tile<DVP>(a.j[2], bt, nullptr);
+}
+
+template <int DVP>
+__global__ __launch_bounds__(256) void prep_tiles_kernel(PackJob j, PrepExtra x)
+{
+    pack_tile<DVP>(j, blockIdx.x, &x);
+    if (blockIdx.x == 0 && threadIdx.x < 4)
         for (int k = 0; k < 3; ++k)
-            if (a.pad_lo[k] + tid < a.pad_hi[k]) a.blob[a.pad_lo[k] + tid] = 0.f;
+            if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) x.blob[x.pad_lo[k] + threadIdx.x] = 0.f;
 }
 
 namespace {
-template <int DP>
-hipError_t run_pack(const PackArgs &a, int64_t heads, hipStream_t s)
+PackJob rows_job(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D)
 {
-    const int64_t grid = heads * (a.Mp / 64);
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_tiles_kernel<DP>, dim3((unsigned)grid), dim3(256), 0, s, a);
-    return hipGetLastError();
+    PackJob j = {};
+    j.src = src; j.dst = dst;
+    j.H = 1; j.sh = 0; j.sb = (int64_t)M * D; j.rs = D;   // heads are consecutive blocks of M rows
+    j.M = M; j.Mp = Mp; j.D = D; j.vec = (D % 4 == 0);
+    j.tiles = (int)(heads * (Mp / 64));
+    return j;
 }
-hipError_t dispatch_pack(const PackArgs &a, int64_t heads, hipStream_t s)
+
+template <int DKP, int DVP, bool BF16>
+hipError_t run_pack(const PackJobs &a, hipStream_t s)
 {
-    switch (a.DP) {
-    case 32: return run_pack<32>(a, heads, s);
-    case 64: return run_pack<64>(a, heads, s);
-    case 128: return run_pack<128>(a, heads, s);
-    case 192: return run_pack<192>(a, heads, s);
-    default: return hipErrorInvalidValue;
-    }
+    const int64_t grid = (int64_t)a.j[0].tiles + a.j[1].tiles + a.j[2].tiles;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((pack_qkv_kernel<DKP, DVP>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
-                                 hipStream_t s)
+hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+                           int Np, int Mp, const Dims &d, hipStream_t s)
 {
-    PackArgs a = {};
-    a.src = src; a.dst = dst;
-    a.sh = (int64_t)M * D; a.sb = 0; a.rs = D;   // heads are consecutive blocks of M rows
-    a.H = 1; a.M = M; a.Mp = Mp; a.D = D; a.DP = DP; a.vec = (D % 4 == 0);
-    // with H = 1 every head index hd maps to hh = 0, bb = hd: make sb the head stride
-    a.sb = a.sh; a.sh = 0;
-    return dispatch_pack(a, heads, s);
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
+    PackJobs a = {};
+    const int64_t qh = q ? (int64_t)d.H * d.B : 0, kh = (int64_t)d.Hkv * d.B;
+    a.j[0] = rows_job(q, q16, qh, d.N, Np, d.DK);
+    a.j[1] = rows_job(k, k16, kh, d.M, Mp, d.DK);
+    a.j[2] = rows_job(v, v16, kh, d.M, Mp, d.DV);
+    FAB_DISPATCH_HEAD_DIMS(run_pack, a, s, hd, true);
 }
 
 hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
                             int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
                             int64_t total, const Dims &d, hipStream_t s)
 {
-    PackArgs a = {};
-    a.src = dO; a.O = O; a.lse = lse; a.dst = dO16; a.stats = stats; a.blob = blob;
+    PackJob j = {};
+    j.src = dO; j.dst = dO16;
     // d, O [DV,H,N,B]: row n of head (h, b) at DV*(h + H*(n + N*b))
-    a.sh = d.DV; a.sb = (int64_t)d.DV * d.H * d.N; a.rs = (int64_t)d.DV * d.H;
-    a.H = d.H; a.M = d.N; a.Mp = Np; a.D = d.DV; a.DP = dvp; a.vec = (d.DV % 4 == 0);
-    a.pad_lo[0] = nq; a.pad_hi[0] = off_k;
-    a.pad_lo[1] = off_k + nk; a.pad_hi[1] = off_v;
-    a.pad_lo[2] = off_v + nv; a.pad_hi[2] = total;
-    return dispatch_pack(a, (int64_t)d.H * d.B, s);
+    j.H = d.H; j.sh = d.DV; j.sb = (int64_t)d.DV * d.H * d.N; j.rs = (int64_t)d.DV * d.H;
+    j.M = d.N; j.Mp = Np; j.D = d.DV; j.vec = (d.DV % 4 == 0);
+    j.tiles = d.H * d.B * (Np / 64);
+    PrepExtra x = {};
+    x.O = O; x.lse = lse; x.stats = stats; x.blob = blob;
+    x.pad_lo[0] = nq; x.pad_hi[0] = off_k;
+    x.pad_lo[1] = off_k + nk; x.pad_hi[1] = off_v;
+    x.pad_lo[2] = off_v + nv; x.pad_hi[2] = total;
+    if (j.tiles == 0) return hipSuccess;
+    switch (dvp) {
+    case 32: hipLaunchKernelGGL(prep_tiles_kernel<32>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
+    case 64: hipLaunchKernelGGL(prep_tiles_kernel<64>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
+    case 128: hipLaunchKernelGGL(prep_tiles_kernel<128>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
+    case 192: hipLaunchKernelGGL(prep_tiles_kernel<192>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // ============================================================== GQA reduce
@@ -254,7 +323,9 @@ hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, h
 {
     const int nqb = (d.N + kMapTile - 1) / kMapTile, nkb = (d.M + kMapTile - 1) / kMapTile;
     if (nqb == 0 || nkb == 0) return hipSuccess;
-    hipLaunchKernelGGL(block_map_kernel, dim3(nkb, nqb), dim3(64), 0, s, mask, map, d.N, d.M, nkb);
+    const int64_t blocks = (int64_t)nqb * nkb;
+    hipLaunchKernelGGL(block_map_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, s, mask, map, d.N, d.M,
+                       nqb, nkb);
     return hipGetLastError();
 }
 

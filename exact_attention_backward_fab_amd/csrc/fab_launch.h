@@ -50,8 +50,8 @@ inline bool pick_head_dims(int DK, int DV, HeadDims *out)
 hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, hipStream_t s);
 
 // Forward with row log-sum-exp (natural log, -inf for all-masked rows): f32
-// operands, or bf16 operands read from the packed K / V (launch_pack_rows_bf16,
-// Mp rows per head).
+// operands, or bf16 operands read from the packed K / V (launch_pack_qkv, Mp rows
+// per head).
 hipError_t launch_forward_f32(const float *q, const float *k, const float *v, const uint16_t *mask,
                               const uint8_t *map, float scale, float *O, float *lse, const Dims &d,
                               hipStream_t s);
@@ -74,10 +74,11 @@ hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, _
 // Rows of the bf16 tiles are padded per head to a multiple of this.
 constexpr int kPackRows = 64;
 
-// f32 [heads][M][D] -> bf16 [heads][Mp][DP] in 64-row tiles stored chunk column
-// by chunk column (fab_tiles.h); rows >= M and columns >= D zero.
-hipError_t launch_pack_rows_bf16(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D, int DP,
-                                 hipStream_t s);
+// f32 rows -> bf16 tiles (fab_tiles.h), one launch: q [DK,N,H,B] -> q16 [B,H,Np,DKP]
+// (skipped when q is NULL), k / v -> k16 / v16 [B,Hkv,Mp,DKP / DVP]; rows past the
+// data and columns past DK / DV zero.
+hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+                           int Np, int Mp, const Dims &d, hipStream_t s);
 
 // Key-block-outer backward, f32 mode: dV, dK per key tile (stored into dk/dv with
 // per-query-head layout when part_heads != 0) and dQ by f32 atomics into dq
@@ -88,7 +89,7 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
                                hipStream_t s);
 
 // Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
-// (launch_pack_rows_bf16 / launch_prep, Np rows per head), K, V (Mp rows per head)
+// (launch_pack_qkv / launch_prep_bf16, Np rows per head), K, V (Mp rows per head)
 // and the LSE/D blocks; stored as in launch_backward_f32.
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
