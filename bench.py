@@ -34,6 +34,32 @@ if ROOT not in sys.path:
 
 import fab_inputs as fi  # noqa: E402
 
+# HBM bytes of the dominant kernel measured by rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, scaled by the same counters on a copy kernel of known size), with a
+# hash of the sources they were taken on; reported only while the sources match.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_backward_causal_gqa_B1_H32x8_N2048_D128_bf16.json")
+KERNEL_SOURCES = ("fab_bwd.hip", "fab_tiles.h", "fab_common.h")
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_backward_fab_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("workload") != workload or t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
 METRIC = "attention-backward TFLOP/s and % of MFMA peak (bf16 and fp32 modes), 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks (published)
 HBM_GBS = 8000.0
@@ -92,6 +118,9 @@ def parse():
     ap.add_argument("--mode", default=None, choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy before the timed region (the known-size "
+                         "reference of the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -194,6 +223,13 @@ def main():
     def step_fwd():
         fab.forward_lse(tq, tk, tv, scale, mask=tm, mode=mode, O=O, lse=lse, ws=ws_bwd)
 
+    if args.calib_copy:
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     # ---- timed region: the whole path, per-kernel HIP events on the launch stream
     for _ in range(args.warmup):
         step_full()
@@ -235,12 +271,12 @@ def main():
     if dom_kind == "flop":
         ach = per_launch / (dom_launch_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "per_launch_flops": per_launch,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(dom, w.name), "per_launch_flops": per_launch,
                 "avg_launch_ms": round(dom_launch_ms, 5)}
     else:
         ach = per_launch / (dom_launch_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_GBS, 4), "traffic": None, "per_launch_bytes": per_launch,
+                "frac": round(ach / HBM_GBS, 4), "traffic": measured_traffic(dom, w.name), "per_launch_bytes": per_launch,
                 "avg_launch_ms": round(dom_launch_ms, 5)}
 
     out = {
