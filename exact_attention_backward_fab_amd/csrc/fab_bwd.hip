@@ -59,8 +59,11 @@ struct KvArgs {
     float scale;
 };
 
-constexpr int kKW = 4, kKNT = 64 * kKW;
-constexpr int kKBC = 32 * kKW;   // keys per work-group
+// 8 waves, two per SIMD: wave w owns keys 32 (w & 3).. of the block and the
+// 32-query half (w >> 2) of every 64-query step; the two halves' dK/dV are summed
+// through LDS at the end.
+constexpr int kKW = 8, kKNT = 64 * kKW;
+constexpr int kKBC = 128;        // keys per work-group
 constexpr int kKBR = kTR;        // queries per step
 constexpr int kKList = 512;      // live query steps listed at a time
 
@@ -69,22 +72,287 @@ template <int DKP, int DVP>
 struct KStages {
     static constexpr int kQ = DKP / 8 * kChunkL, kO = DVP / 8 * kChunkL, kS = kStatsTile * 4;
     static constexpr int kBytes = kQ + kO + kS;
+    static constexpr int kKV = 2 * (kQ + kO);   // the block's K and V rows: two 64-row tiles each
+    static constexpr int kFit = (160 * 1024 - 4 * kKList - 256 - kKV) / kBytes;
+    static constexpr int N = kFit > 4 ? 4 : kFit;
+    static_assert(N >= 2, "two LDS stages must fit");
+};
+
+template <int DKP, int DVP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(KvArgs p)
+{
+    using ST = KStages<DKP, DVP>;
+    constexpr int NS = ST::N;
+    // chunk columns copied per wave; when a tile has fewer columns than 2 per wave,
+    // the surplus copies repeat a column (same bytes to the same place) so that
+    // every wave issues the same number of copies per step (its vmcnt waits count on it)
+    constexpr int QCH = (DKP / 8 + kKW - 1) / kKW, OCH = (DVP / 8 + kKW - 1) / kKW;
+    constexpr int PER = QCH + OCH + 1;                         // copies per wave and step
+    static_assert((DKP > DVP ? DKP : DVP) / 32 * 16 * 64 * 4 * 4 <= NS * ST::kBytes, "dK/dV exchange area");
+    __shared__ __attribute__((aligned(16))) char sQO[NS * ST::kBytes];
+    __shared__ __attribute__((aligned(16))) char sKV[ST::kKV];   // K tiles, then V tiles of the block
+    __shared__ int sList[kKList];
+    __shared__ int sCount[kKW + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int kw = w & 3, qq = w >> 2;                         // key sub-block, query half
+    const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
+    const uint32_t qo_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sQO;
+
+    // ---- work-group -> (key block, head): first key blocks first (under a causal
+    // mask they see the most queries); heads dealt to the XCDs in contiguous ranges
+    const int HB = p.H * p.B;
+    int kb, hb;
+    if (HB % 8 == 0) {
+        const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HB / 8;
+        kb = jj / per;
+        hb = xcd * per + jj % per;
+    } else {
+        kb = blockIdx.x / HB;
+        hb = blockIdx.x % HB;
+    }
+    const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
+    const int key0 = kb * kKBC;
+    const int mykey = key0 + 32 * kw + l32;  // this lane's key in the C layout of S and dP
+    const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
+    const float sl2 = p.scale * kLog2e;
+
+    // ---- the block's K and V rows (B operands of S = Q K^T and dP = dO V^T, one key
+    // per lane) into LDS: 2 tiles of each, copied by chunk columns
+    {
+        const rsrc_t rk = make_rsrc(p.k16 + (size_t)(g + p.Hkv * b) * p.Mp * DKP, (uint32_t)(p.Mp * DKP) * 2u);
+        const rsrc_t rv = make_rsrc(p.v16 + (size_t)(g + p.Hkv * b) * p.Mp * DVP, (uint32_t)(p.Mp * DVP) * 2u);
+        const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
+        // rows past Mp read as zero (buffer bounds); chunk column c of tile tt
+        for (int c = w; c < 2 * (DKP / 8); c += kKW) {
+            const int tt = c / (DKP / 8), cc = c - tt * (DKP / 8);
+            lds_copy16(rk, kv_lds + tt * ST::kQ + cc * kChunkL,
+                       (uint32_t)((key0 / 64 + tt) * DKP / 8 + cc) * kChunkG + (uint32_t)lane * 16u);
+        }
+        for (int c = w; c < 2 * (DVP / 8); c += kKW) {
+            const int tt = c / (DVP / 8), cc = c - tt * (DVP / 8);
+            lds_copy16(rv, kv_lds + 2 * ST::kQ + tt * ST::kO + cc * kChunkL,
+                       (uint32_t)((key0 / 64 + tt) * DVP / 8 + cc) * kChunkG + (uint32_t)lane * 16u);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // published by the first barrier of the step loop
+    }
+    // this lane's key row in the K and V tiles: tile kw / 2, row 32 (kw & 1) + l32
+    const char *Krow = sKV + (kw >> 1) * ST::kQ + 512 * (kw & 1) + row_off;
+    const char *Vrow = sKV + 2 * ST::kQ + (kw >> 1) * ST::kO + 512 * (kw & 1) + row_off;
+    f32x16 dkacc[DKP / 32], dvacc[DVP / 32];
+#pragma unroll
+    for (int i = 0; i < DKP / 32; ++i) dkacc[i] = zero16();
+#pragma unroll
+    for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
+
+    const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // first tile row of this head
+    const rsrc_t rq = make_rsrc(p.q16 + qhead * DKP, (uint32_t)(p.Np * DKP) * 2u);
+    const rsrc_t ro = make_rsrc(p.o16 + qhead * DVP, (uint32_t)(p.Np * DVP) * 2u);
+    const rsrc_t rs = make_rsrc(p.stats + qhead / 64 * kStatsTile, (uint32_t)(p.Np / 64 * kStatsTile) * 4u);
+
+    // copies of query step it into stage bf: Q and dO chunk columns split over the
+    // waves, lanes 0-7 of each wave copy a quarter of the LSE/D block
+    auto issue = [&](int it, int bf) {
+        const uint32_t stg = qo_lds + (uint32_t)(bf * ST::kBytes);
+#pragma unroll
+        for (int i = 0; i < QCH; ++i) {
+            const int c = (i * kKW + w) % (DKP / 8);
+            lds_copy16(rq, stg + c * kChunkL, (uint32_t)(it * DKP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
+        }
+#pragma unroll
+        for (int i = 0; i < OCH; ++i) {
+            const int c = (i * kKW + w) % (DVP / 8);
+            lds_copy16(ro, stg + ST::kQ + c * kChunkL, (uint32_t)(it * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
+        }
+        if (lane < 4)
+            lds_copy16(rs, stg + ST::kQ + ST::kO + w * 64,
+                       (uint32_t)(it * kStatsTile * 4 + w * 64) + (uint32_t)lane * 16u);
+    };
+
+    const int nqt = p.Np / kKBR;
+    for (int seg = 0; seg < nqt; seg += kKList) {
+        const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
+            return tile_class(p.map, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
+                              kKBC / kMapTile);
+        });
+        if (count == 0) continue;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < count) issue(sList[i] >> 2, i);
+        for (int li = 0; li < count; ++li) {
+            wait_vm_steps<PER>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
+            __syncthreads();                                    // ... for every wave; stage li-1 is free
+            if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
+            const int e = sList[li];
+            const int it = e >> 2, cls = e & 3;
+            const int q0 = it * kKBR;
+            const char *Qb = sQO + (li % NS) * ST::kBytes;
+            const char *Ob = Qb + ST::kQ;
+            const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
+
+            // ---- S = Q K^T and dP = dO V^T for this wave's 32 queries (lane = key)
+            f32x16 sacc = zero16(), pacc = zero16();
+            {
+                bf16x8 a[DKP / 16];
+#pragma unroll
+                for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
+#pragma unroll
+                for (int t = 0; t < DKP / 16; ++t) sacc = mfma_bf16(a[t], lds_row8(Krow + 2304 * t), sacc);
+                bf16x8 o[DVP / 16];
+#pragma unroll
+                for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
+#pragma unroll
+                for (int t = 0; t < DVP / 16; ++t) pacc = mfma_bf16(o[t], lds_row8(Vrow + 2304 * t), pacc);
+            }
+
+            // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
+            // every key visible folds the scale into the exponent
+            const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
+            const float mul = fast ? sl2 : 1.f;
+            const int qb = q0 + 32 * qq;   // first query of this wave's half
+            if (!fast) {
+                const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = sacc[r] * sl2 + kbias;
+                    sacc[r] = (qb + crow(r, half) >= thr) ? x : -INFINITY;
+                }
+                if (cls == kTileMixed) {
+                    const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int n = min(qb + crow(r, half), p.N - 1);
+                        sacc[r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int qr = 32 * qq + 8 * r4 + 4 * half;
+                const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(Sb + qr);
+                const f32x4 del4 = *reinterpret_cast<const f32x4 *>(Sb + 64 + qr);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * r4 + c;
+                    const float P = fast_exp2(__builtin_fmaf(sacc[r], mul, -lse4[c]));
+                    sacc[r] = P;
+                    pacc[r] = P * (pacc[r] - del4[c]);
+                }
+            }
+
+            // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
+            // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float pv[8], dv8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pv[i] = sacc[8 * u + i];
+                    dv8[i] = pacc[8 * u + i];
+                }
+                const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
+                bf16x8 bo[DVP / 32], bq[DKP / 32];
+#pragma unroll
+                for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
+#pragma unroll
+                for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa, bo[dt], dvacc[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
+#pragma unroll
+                for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da, bq[dt], dkacc[dt]);
+            }
+        }
+        __syncthreads();   // every wave is done with the stages before they are refilled
+    }
+
+    // ---- sum the two query halves: waves 4-7 hand their accumulators to waves 0-3
+    // through LDS, dK then dV (the stream ended with a barrier: the stage memory is free)
+    {
+        float *xch = reinterpret_cast<float *>(sQO) + kw * ((DKP > DVP ? DKP : DVP) / 2) * 64;
+        if (qq == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(16 * dt + r) * 64 + lane] = dkacc[dt][r];
+        }
+        __syncthreads();
+        if (qq == 0) {
+#pragma unroll
+            for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dkacc[dt][r] += xch[(16 * dt + r) * 64 + lane];
+        }
+        __syncthreads();
+        if (qq == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(16 * dt + r) * 64 + lane] = dvacc[dt][r];
+        }
+        __syncthreads();
+        if (qq == 1) return;
+#pragma unroll
+        for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dvacc[dt][r] += xch[(16 * dt + r) * 64 + lane];
+    }
+
+    // ---- store dK (scaled) and dV of this key block
+    const int hdd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
+    float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
+    float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
+#pragma unroll
+    for (int dt = 0; dt < DKP / 32; ++dt) {
+        const int col = dt * 32 + l32;
+        if (col < p.DK)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 32 * kw + crow(r, half);
+                if (key < p.M) dkb[col + (size_t)p.DK * key] = dkacc[dt][r] * p.scale;
+            }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DVP / 32; ++dt) {
+        const int col = dt * 32 + l32;
+        if (col < p.DV)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 32 * kw + crow(r, half);
+                if (key < p.M) dvb[col + (size_t)p.DV * key] = dvacc[dt][r];
+            }
+    }
+}
+
+// 4-wave variant for the large head dims (K and V rows of the block in registers,
+// one wave per SIMD): wave w owns keys 32w.. of the block and both 32-query halves
+// of every step.
+constexpr int kKW4 = 4, kKNT4 = 64 * kKW4;
+
+
+// LDS stages of the 4-wave kernel: the Q tile, the dO tile and the LSE/D block of
+// one step each.
+template <int DKP, int DVP>
+struct KStages4 {
+    static constexpr int kQ = DKP / 8 * kChunkL, kO = DVP / 8 * kChunkL, kS = kStatsTile * 4;
+    static constexpr int kBytes = kQ + kO + kS;
     static constexpr int kFit = (160 * 1024 - 4 * kKList - 256) / kBytes;
     static constexpr int N = kFit > 4 ? 4 : kFit;
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
 template <int DKP, int DVP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_kernel(KvArgs p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_w4_kernel(KvArgs p)
 {
-    using ST = KStages<DKP, DVP>;
+    using ST = KStages4<DKP, DVP>;
     constexpr int NS = ST::N;
-    constexpr int QCH = DKP / 8 / kKW, OCH = DVP / 8 / kKW;   // chunk columns copied per wave
-    static_assert(QCH * 8 * kKW == DKP && OCH * 8 * kKW == DVP, "tile copy split");
+    constexpr int QCH = DKP / 8 / kKW4, OCH = DVP / 8 / kKW4;   // chunk columns copied per wave
+    static_assert(QCH * 8 * kKW4 == DKP && OCH * 8 * kKW4 == DVP, "tile copy split");
     constexpr int PER = QCH + OCH + 1;                         // copies per wave and step
     __shared__ __attribute__((aligned(16))) char sQO[NS * ST::kBytes];
     __shared__ int sList[kKList];
-    __shared__ int sCount[kKW + 1];
+    __shared__ int sCount[kKW4 + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -140,12 +408,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint32_t stg = qo_lds + (uint32_t)(bf * ST::kBytes);
 #pragma unroll
         for (int i = 0; i < QCH; ++i) {
-            const int c = i * kKW + w;
+            const int c = i * kKW4 + w;
             lds_copy16(rq, stg + c * kChunkL, (uint32_t)(it * DKP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
 #pragma unroll
         for (int i = 0; i < OCH; ++i) {
-            const int c = i * kKW + w;
+            const int c = i * kKW4 + w;
             lds_copy16(ro, stg + ST::kQ + c * kChunkL, (uint32_t)(it * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
         if (lane < 8)
@@ -155,7 +423,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int nqt = p.Np / kKBR;
     for (int seg = 0; seg < nqt; seg += kKList) {
-        const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
+        const int count = build_live_list<kKW4>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
             return tile_class(p.map, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
                               kKBC / kMapTile);
         });
@@ -501,8 +769,12 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
 {
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
-    } else {
+    } else if constexpr (DKP + DVP <= 256) {
         hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT), 0, s, a);
+        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT4), 0, s,
+                           a);
         return hipGetLastError();
     }
 }
