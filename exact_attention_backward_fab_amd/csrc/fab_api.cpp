@@ -39,7 +39,8 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_pk, ws_pv, ws_bytes;
+    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_dqp, ws_tick, ws_pk,
+        ws_pv, ws_bytes;
     int dkp, dvp;  // padded head dims of the kernels
     int np;        // query rows per head of the bf16 Q / dO tiles
     int mp;        // key rows per head of the bf16 K / V copies
@@ -98,6 +99,7 @@ int check_shape(const fab_shape *s, Plan *pl)
 //   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward, f32 mode)
 //   q16, o16   bf16 Q / dO tiles, Np rows per head             (backward, bf16 mode)
 //   stats      LSE / D blocks [B][H][Np/64][128]               (backward, bf16 mode)
+//   dqp, tick  dQ partials of split query blocks and counters  (backward, bf16 mode, few blocks)
 //   pk, pv     per-query-head dK / dV partials                 (backward, H > Hkv)
 // ws_fwd is the end of the part the forward alone uses.
 void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
@@ -135,6 +137,13 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         off = align_up(off + 2 * qrows * pl->dvp);
         pl->ws_stats = off;
         off = align_up(off + sizeof(float) * qrows / 64 * 128);
+    }
+    pl->ws_dqp = off;
+    pl->ws_tick = off;
+    if (mode == FAB_MODE_BF16) {
+        off = align_up(off + sizeof(float) * (size_t)fab::dq_part_floats(d, pl->dkp));
+        pl->ws_tick = off;
+        off = align_up(off + sizeof(int) * (size_t)fab::dq_split_blocks(d));
     }
     pl->ws_pk = off;
     pl->ws_pv = off;
@@ -438,11 +447,14 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
     __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
     float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
+    float *dqp = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_dqp) : nullptr;
+    int *tick = bf16 ? reinterpret_cast<int *>(wsb + pl.ws_tick) : nullptr;
     // bf16: dQ is written once by the query-block-outer kernel (only its pad is
     // zeroed); f32: dQ is accumulated by atomics into a zeroed slice
     if (bf16)
         FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, Ou, lseu, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
-                                                pl.off_v, pl.nv, pl.total, pl.d, s),
+                                                pl.off_v, pl.nv, pl.total, tick, (int)fab::dq_split_blocks(pl.d), pl.d,
+                                                s),
                    "prep launch");
     else
         FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
@@ -453,7 +465,8 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
         FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, pl.gqa ? 1 : 0,
                                                    pl.np, pl.mp, pl.d, s),
                    "backward launch");
-        FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, pl.np, pl.mp, pl.d, s),
+        FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
+                                                 pl.d, s),
                    "dQ launch");
     } else {
         FAB_LAUNCH(kBwd, fab::launch_backward_f32(q, k, v, d, mk, map, lseu, delta, scale, blob, dk, dv,

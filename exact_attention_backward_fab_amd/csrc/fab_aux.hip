@@ -142,6 +142,8 @@ struct PrepExtra {
     float *stats;                     // LSE/D blocks [heads][Mp/64][128]
     float *blob;                      // result blob whose pads are zeroed (work-group 0)
     int64_t pad_lo[3], pad_hi[3];
+    int *zero;                        // nzero ints set to 0 (the dQ split counters)
+    int nzero;
 };
 
 // One 64-row tile of job j (tile index bt within the job), through LDS so that the
@@ -225,6 +227,7 @@ template <int DVP>
 __global__ __launch_bounds__(256) void prep_tiles_kernel(PackJob j, PrepExtra x)
 {
     pack_tile<DVP>(j, blockIdx.x, &x);
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < x.nzero; i += gridDim.x * 256) x.zero[i] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 4)
         for (int k = 0; k < 3; ++k)
             if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) x.blob[x.pad_lo[k] + threadIdx.x] = 0.f;
@@ -266,7 +269,7 @@ hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf1
 
 hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
                             int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
-                            int64_t total, const Dims &d, hipStream_t s)
+                            int64_t total, int *zero, int nzero, const Dims &d, hipStream_t s)
 {
     PackJob j = {};
     j.src = dO; j.dst = dO16;
@@ -279,6 +282,7 @@ hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, _
     x.pad_lo[0] = nq; x.pad_hi[0] = off_k;
     x.pad_lo[1] = off_k + nk; x.pad_hi[1] = off_v;
     x.pad_lo[2] = off_v + nv; x.pad_hi[2] = total;
+    x.zero = zero; x.nzero = nzero;
     if (j.tiles == 0) return hipSuccess;
     switch (dvp) {
     case 32: hipLaunchKernelGGL(prep_tiles_kernel<32>, dim3(j.tiles), dim3(256), 0, s, j, x); break;

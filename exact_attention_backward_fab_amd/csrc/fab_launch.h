@@ -69,7 +69,7 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
 // of the result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)).
 hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
                             int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
-                            int64_t total, const Dims &d, hipStream_t s);
+                            int64_t total, int *zero, int nzero, const Dims &d, hipStream_t s);
 
 // Rows of the bf16 tiles are padded per head to a multiple of this.
 constexpr int kPackRows = 64;
@@ -95,11 +95,24 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
                                 float *dv, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
 
+// dQ work split.  Query blocks have kDqBlock rows.  A grid of at most
+// kDqSplitBlocks blocks fills one round of two work-groups per CU on the 256 CUs
+// of an MI355X, so the latest (heaviest, when causal) blocks would bound the
+// kernel; there each block is run by two work-groups that take alternate live
+// key steps and merge their partial sums (dq_part_floats floats of scratch and
+// dq_split_blocks zeroed counters).
+constexpr int kDqBlock = 128, kDqSplitBlocks = 512;
+inline int64_t dq_blocks(const Dims &d) { return (int64_t)((d.N + kDqBlock - 1) / kDqBlock) * d.H * d.B; }
+inline int dq_split(const Dims &d) { return dq_blocks(d) <= kDqSplitBlocks ? 2 : 1; }
+inline int64_t dq_part_floats(const Dims &d, int dkp) { return dq_split(d) == 2 ? dq_blocks(d) * 2 * kDqBlock * dkp : 0; }
+inline int64_t dq_split_blocks(const Dims &d) { return dq_split(d) == 2 ? dq_blocks(d) : 0; }
+
 // Query-block-outer dQ (bf16 mode): dq [DK,N,H,B] = scale dS K, every element
-// written once; inputs as for launch_backward_bf16.
+// written once; inputs as for launch_backward_bf16.  part and ticket as sized
+// above (ticket zeroed by launch_prep_bf16), used when dq_split(d) == 2.
 hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16, const __bf16 *v16,
-                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, int Np, int Mp, const Dims &d,
-                     hipStream_t s);
+                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, float *part, int *ticket,
+                     int Np, int Mp, const Dims &d, hipStream_t s);
 
 // dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] for one of dK / dV.
 hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s);

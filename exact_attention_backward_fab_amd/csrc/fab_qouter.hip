@@ -12,7 +12,9 @@
 //                          P = exp(scale S + mask - LSE), dS = P o (dP - D)
 //                          (labml "Flash Attention", "Backward pass"), and
 //                          accumulating dQ in registers.  Every dQ element is
-//                          written once; no atomics.
+//                          written once; no atomics on dQ.  Small grids run each
+//                          query block as two work-groups on alternate key steps
+//                          whose partial sums meet through a per-block counter.
 #include <algorithm>
 #include <climits>
 
@@ -70,39 +72,44 @@ __device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB)
 // waits for its own copies of it (vmcnt) and a barrier publishes them; the same
 // barrier tells every wave that the stage about to be refilled has been consumed.
 // sKV is the stage array and kv_lds its LDS byte address.
-template <int DKP, int DVP, typename ClassOf, typename Body>
+// With stride > 1 the work-group takes only the live steps at list positions
+// off, off + stride, ... (one share of a query block split over work-groups).
+template <int DKP, int DVP, int W = kQW, typename ST = QStages<DKP, DVP>, typename ClassOf, typename Body>
 __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const char *sKV, uint32_t kv_lds, int *sList,
                                                  int *sCount, int nks, int tid, int lane, int w, ClassOf class_of,
-                                                 Body body)
+                                                 Body body, int off = 0, int stride = 1)
 {
-    using ST = QStages<DKP, DVP>;
     constexpr int NS = ST::N;
-    constexpr int KCH = DKP / 8 / kQW, VCH = DVP / 8 / kQW;   // chunk columns copied per wave
-    static_assert(KCH * 8 * kQW == DKP && VCH * 8 * kQW == DVP, "tile copy split");
+    // chunk columns copied per wave; when a tile has fewer columns than waves, the
+    // surplus copies repeat a column (same bytes to the same place) so that every
+    // wave issues the same number of copies per step (its vmcnt waits count on it)
+    constexpr int KCH = (DKP / 8 + W - 1) / W, VCH = (DVP / 8 + W - 1) / W;
     auto issue = [&](int s, int bf) {
         const uint32_t stg = kv_lds + (uint32_t)(bf * ST::kBytes);   // wave-uniform LDS byte address
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int c = i * kQW + w;
+            const int c = (i * W + w) % (DKP / 8);
             lds_copy16(rk, stg + c * kChunkL, (uint32_t)(s * DKP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-            const int c = i * kQW + w;
+            const int c = (i * W + w) % (DVP / 8);
             lds_copy16(rv, stg + ST::kK + c * kChunkL, (uint32_t)(s * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
     };
     for (int seg = 0; seg < nks; seg += kQList) {
-        const int count = build_live_list<kQW>(sList, sCount, seg, min(seg + kQList, nks), tid, lane, w, class_of);
+        const int live = build_live_list<W>(sList, sCount, seg, min(seg + kQList, nks), tid, lane, w, class_of);
+        const int count = live > off ? (live - off + stride - 1) / stride : 0;   // this share's steps
         if (count == 0) continue;
+        const int *list = sList + off;
 #pragma unroll
         for (int i = 0; i < NS - 1; ++i)
-            if (i < count) issue(sList[i] >> 2, i);
+            if (i < count) issue(list[stride * i] >> 2, i);
         for (int li = 0; li < count; ++li) {
             wait_vm_steps<KCH + VCH>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
             __syncthreads();                                          // ... for every wave; stage li-1 is free
-            if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
-            const int e = sList[li];
+            if (li + NS - 1 < count) issue(list[stride * (li + NS - 1)] >> 2, (li + NS - 1) % NS);
+            const int e = list[stride * li];
             const char *stg = sKV + (li % NS) * ST::kBytes;
             body(e >> 2, e & 3, stg, stg + ST::kK);
         }
@@ -137,23 +144,25 @@ __device__ __forceinline__ f32x16 st_tile(const char *Kb, const bf16x8 *qf, int 
     return acc;
 }
 
-// Scaled scores (log2 units) of a 64-key step for the lane's query: keys past
-// lim get -inf; MIXED steps add the mask row of the query.  A lane's keys come in
-// runs of 4 (slots 4j..4j+3), read as one 8-byte load when vecM (M % 4 == 0).
+// Scaled scores (log2 units) of NT 32-key sub-tiles from key0 on for the lane's
+// query: keys past lim get -inf; MIXED steps add the mask row of the query.  A
+// lane's keys come in runs of 4 (slots 4j..4j+3), read as one 8-byte load when
+// vecM (M % 4 == 0).
+template <int NT>
 __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bool mixed, const uint16_t *mrow, int M,
                                                bool vecM, float sl2, int half)
 {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NT; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float x = st[kk][r] * sl2;
             st[kk][r] = (key0 + kk * 32 + crow(r, half) <= lim) ? x : -INFINITY;
         }
     if (mixed) {
-        uint16_t m[2][16];
+        uint16_t m[NT][16];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < NT; ++kk)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int k0 = key0 + kk * 32 + 8 * r4 + 4 * half;
@@ -169,7 +178,7 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
                 }
             }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < NT; ++kk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[kk][r] += half_bits_to_float(m[kk][r]) * kLog2e;
     }
@@ -235,7 +244,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             float mul = sl2;
             if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f)) {
                 const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
-                scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                scale_and_mask<2>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
                 mul = 1.f;
             }
 
@@ -324,7 +333,10 @@ struct DqArgs {
     const uint16_t *mask;
     const uint8_t *map;
     float *dq;                      // [DK,N,H,B] slice of the result blob
+    float *part;                    // split == 2: per-share dQ partials [blocks][2][4 waves][DKP/2 * 64]
+    int *ticket;                    // split == 2: one zeroed counter per query block
     int B, H, Hkv, N, Np, M, Mp, DK, DV, nqb, nkb;
+    int split;                      // work-groups per query block (1 or 2)
     float scale;
 };
 
@@ -335,18 +347,32 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     __shared__ __attribute__((aligned(16))) char sKV[QStages<DKP, DVP>::N * QStages<DKP, DVP>::kBytes];
     __shared__ int sList[kQList];
     __shared__ int sCount[kQW + 1];
+    __shared__ int sTicket;
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
-    const int nqt = (p.N + kQBQ - 1) / kQBQ;
-    const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B);   // latest queries first (most keys if causal)
+    const int nqt = (p.N + kQBQ - 1) / kQBQ, HB = p.H * p.B;
+    // Query block of this work-group; with split == 2 each block is run by two
+    // work-groups (shares) that take alternate live key steps.  The shares of a
+    // block are 8 work-groups apart, so the round-robin dispatch puts them on one
+    // XCD next to each other.
+    int unit = blockIdx.x, share = 0;
+    if (p.split == 2) {
+        if (HB % 8 == 0) {
+            unit = (int)(blockIdx.x & 7) + 8 * (int)(blockIdx.x >> 4);
+            share = (blockIdx.x >> 3) & 1;
+        } else {
+            unit = blockIdx.x >> 1;
+            share = blockIdx.x & 1;
+        }
+    }
+    const QWork wk = qouter_work(unit, nqt, HB);   // latest queries first (most keys if causal)
     const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int q0 = qt * kQBQ;
     const int myq = q0 + 32 * w + l32;  // this lane's query (C-layout column of S^T and dP^T)
-    const bool qok = myq < p.N;
     const size_t hrow = (size_t)p.N * (h + p.H * b);
     const size_t kvrow = (size_t)p.Mp * (g + p.Hkv * b);
     const rsrc_t rk = make_rsrc(p.k16 + kvrow * DKP, (uint32_t)(p.Mp * DKP) * 2u);
@@ -408,7 +434,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             float mul = sl2;
             if (!(cls == kTileFree && key0 + kQBK <= p.M)) {
                 const int lim = min(cls == kTileCausal ? myq : INT_MAX, p.M - 1);
-                scale_and_mask(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                scale_and_mask<2>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
                 mul = 1.f;
             }
 #pragma unroll
@@ -436,7 +462,37 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 #pragma unroll
                     for (int dt = 0; dt < DKP / 32; ++dt) dqacc[dt] = mfma_bf16(da, bk[dt], dqacc[dt]);
                 }
-        });
+        },
+        share, p.split);
+
+    // ---- two shares: both publish their partial sums and take the block's ticket;
+    // the second to arrive adds the other's partial (a + b = b + a: the result
+    // does not depend on which share that is) and stores the block.  The partials
+    // are written and read with device-coherent accesses (write-through stores,
+    // loads that bypass the non-coherent caches), so no cache-wide writeback or
+    // invalidate is needed: the stores have completed (vmcnt) before the ticket.
+    if (p.split == 2) {
+        constexpr int PW = DKP / 32 * 16 * 64;   // floats of one wave's partial
+        float *mine = p.part + ((size_t)(2 * unit + share) * kQW + w) * PW;
+#pragma unroll
+        for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                __hip_atomic_store(mine + (dt * 16 + r) * 64 + lane, dqacc[dt][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) sTicket = __hip_atomic_fetch_add(p.ticket + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (sTicket == 0) return;   // first share: the other one finishes the block
+        const float *other = p.part + ((size_t)(2 * unit + (share ^ 1)) * kQW + w) * PW;
+#pragma unroll
+        for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dqacc[dt][r] += __hip_atomic_load(other + (dt * 16 + r) * 64 + lane, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- store dQ (scaled): lane = head-dim column, rows = this wave's queries
     float *dqh = p.dq + hrow * p.DK;
@@ -461,7 +517,8 @@ hipError_t run_dq(const DqArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((dq_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT), 0, s, a);
+        hipLaunchKernelGGL((dq_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B * a.split), dim3(kQNT),
+                           0, s, a);
         return hipGetLastError();
     }
 }
@@ -494,14 +551,16 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
 }
 
 hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16, const __bf16 *v16,
-                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, int Np, int Mp, const Dims &d,
-                     hipStream_t s)
+                     const uint16_t *mask, const uint8_t *map, float scale, float *dq, float *part, int *ticket,
+                     int Np, int Mp, const Dims &d, hipStream_t s)
 {
+    static_assert(kQBQ == kDqBlock, "dQ query block");
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
     DqArgs a;
     a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
-    a.dq = dq;
+    a.dq = dq; a.part = part; a.ticket = ticket; a.split = dq_split(d);
+    if (a.split == 2 && (!part || !ticket)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
     a.scale = scale;

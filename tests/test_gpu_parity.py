@@ -130,6 +130,9 @@ SMALL = [
     ("one_key", Shape(1, 2, 1, 17, 1, 16, 16), None, 47),
     ("one_query", Shape(1, 2, 2, 1, 130, 64, 64), "random", 48),
     ("workload1", fi.WORKLOADS[1].shape, None, 1),
+    # 16 x 33 = 528 query blocks of 128: above the two-share dQ split's limit (512),
+    # so dQ runs one work-group per block (every other case here is split)
+    ("dq_unsplit_528_blocks", Shape(1, 33, 3, 2000, 600, 32, 32), "causal", 49),
 ]
 
 
@@ -192,6 +195,30 @@ def test_route_agreement_supplied_vs_recomputed_forward(torch_dev):
     a = run_gpu(torch, dev, s, q, k, v, d, mask, 0.125, "f32", with_o_lse=False)
     b = run_gpu(torch, dev, s, q, k, v, d, mask, 0.125, "f32", with_o_lse=True)
     assert rel_err(a, b) <= 1e-5
+
+
+def test_bf16_repeat_is_bitwise_stable(torch_dev):
+    # the same inputs and workspace three times: bf16 mode has no order-dependent
+    # sums (dQ blocks split over two work-groups add their halves with a + b = b + a;
+    # the split counters are re-zeroed on every call), so the blobs are identical
+    torch, dev = torch_dev
+    fab = fabmod()
+    s = Shape(1, 8, 2, 700, 700, 128, 128)
+    q, k, v, d = make_qkvd(s, 91)
+    mask = causal_mask(s.N, s.M)
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    tm = to_dev(torch, dev, mask)
+    fs = fab.Shape(*s.astuple())
+    ws, _ = fab.alloc_workspace(fs, "bf16", True, False, dev)
+    outs = []
+    for _ in range(3):
+        blob = fab.backward(t[0], t[1], t[2], t[3], 0.1, mask=tm, mode="bf16", ws=ws)
+        torch.cuda.synchronize()
+        outs.append(blob.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    ref = oracle_full(s, q, k, v, d, mask, 0.1)
+    check_blob(s, outs[0], ref, "bf16", tag="repeat", mask=mask)
 
 
 def test_d_ones_closed_form_on_gpu(torch_dev):
