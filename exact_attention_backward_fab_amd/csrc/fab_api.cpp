@@ -95,7 +95,7 @@ int check_shape(const fab_shape *s, Plan *pl)
 // Workspace carving (256-byte aligned sub-buffers, in this order):
 //   map        u8 block map of the mask                       (mask given)
 //   k16, v16   bf16 K / V rows, Mp per head, swizzled chunks   (bf16 mode)
-//   lse, O     forward recompute                               (O, lse not given)
+//   lse, O     forward recompute                               (O, lse not given, f32 mode)
 //   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward, f32 mode)
 //   q16, o16   bf16 Q / dO tiles, Np rows per head             (backward, bf16 mode)
 //   stats      LSE / D blocks [B][H][Np/64][128]               (backward, bf16 mode)
@@ -120,7 +120,7 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     pl->ws_fwd = off;
     pl->ws_lse = off;
     pl->ws_O = off;
-    if (!have_o_lse) {
+    if (!have_o_lse && mode == FAB_MODE_F32) {   // bf16: the backward's own forward stores no O
         off = align_up(off + sizeof(float) * (size_t)pl->nrow);
         pl->ws_O = off;
         off = align_up(off + sizeof(float) * (size_t)pl->nO);
@@ -435,30 +435,40 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
     __bf16 *q16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_q16) : nullptr;
     if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
-    if (bf16) FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, s));
-    const float *Ou = O, *lseu = lse;
-    if (!have) {
-        float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
-        float *lw = reinterpret_cast<float *>(wsb + pl.ws_lse);
-        FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, mk, map, scale, Ow, lw, s));
-        Ou = Ow;
-        lseu = lw;
-    }
-    float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
     __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
     float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
     float *dqp = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_dqp) : nullptr;
     int *tick = bf16 ? reinterpret_cast<int *>(wsb + pl.ws_tick) : nullptr;
-    // bf16: dQ is written once by the query-block-outer kernel (only its pad is
-    // zeroed); f32: dQ is accumulated by atomics into a zeroed slice
-    if (bf16)
-        FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, Ou, lseu, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
-                                                pl.off_v, pl.nv, pl.total, tick, (int)fab::dq_split_blocks(pl.d), pl.d,
-                                                s),
+    const int ntick = (int)fab::dq_split_blocks(pl.d);
+    float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
+    const float *lseu = lse;
+    if (bf16 && !have) {
+        // the backward's own forward writes the Q and dO tiles and the LSE/D blocks
+        // directly (no O, no separate prep pass); dQ is written once by the
+        // query-block-outer kernel (only its pad is zeroed)
+        FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, s));
+        FAB_LAUNCH(kFwd, fab::launch_forward_prep_bf16(q, k16, v16, mk, map, scale, d, q16, o16, stats, blob, pl.nq,
+                                                       pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, tick, ntick, pl.np,
+                                                       pl.mp, pl.d, s),
+                   "forward launch");
+    } else if (bf16) {
+        FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, s));
+        FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, O, lse, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
+                                                pl.off_v, pl.nv, pl.total, tick, ntick, pl.d, s),
                    "prep launch");
-    else
+    } else {
+        // f32: dQ is accumulated by atomics into a zeroed slice
+        const float *Ou = O;
+        if (!have) {
+            float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
+            float *lw = reinterpret_cast<float *>(wsb + pl.ws_lse);
+            FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, mk, map, scale, Ow, lw, s));
+            Ou = Ow;
+            lseu = lw;
+        }
         FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
                    "prep launch");
+    }
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     if (bf16) {

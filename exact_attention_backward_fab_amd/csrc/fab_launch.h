@@ -58,6 +58,15 @@ hipError_t launch_forward_f32(const float *q, const float *k, const float *v, co
 hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
                                const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s);
+// The backward's own forward in bf16 mode: instead of O and the LSE it writes
+// what the backward kernels read, as launch_pack_qkv (Q) and launch_prep_bf16 do
+// from a stored O and LSE: the bf16 tiles of Q and dO, the LSE/D blocks, the blob
+// pads (nq, off_k, nk, off_v, nv, total as there) and nzero zeroed ints.
+hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+                                    const uint8_t *map, float scale, const float *dO, __bf16 *q16, __bf16 *o16,
+                                    float *stats, float *blob, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v,
+                                    int64_t nv, int64_t total, int *zero, int nzero, int Np, int Mp, const Dims &d,
+                                    hipStream_t s);
 
 // f32 mode prep: Delta = rowsum(d o O) [N,H,B]; zero the dQ slice [0, off_k)
 // (the atomics target) and the other blob pads.

@@ -193,9 +193,20 @@ struct FwdArgs16 {
     float *O, *lse;                 // O [DV,H,N,B], lse [N,H,B]
     int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK, vecV;
     float scale;
+    // The backward's own forward (PREP) writes, instead of O and lse, what the
+    // backward kernels read: the bf16 tiles of Q and dO (rows >= N and columns
+    // >= DK / DV zero), the LSE/D blocks (D = rowsum(dO o O)), and it zeroes the
+    // blob pads (work-group 0) and the dQ split counters.
+    const float *dO;                // [DV,H,N,B]
+    __bf16 *q16, *o16;              // tiles [B,H,Np,DKP] / [B,H,Np,DVP]
+    float *stats;                   // [B,H,Np/64][128]
+    float *blob;
+    int64_t pad_lo[3], pad_hi[3];
+    int *zero;
+    int nzero, Np;
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool PREP>
 __global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
 __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
 {
@@ -221,6 +232,19 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 
     bf16x8 qf[DKP / 16];
     load_q_operand<DKP>(qf, p.q + (hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half);
+    const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // PREP: first tile row of this head
+    if constexpr (PREP) {
+        if (myq < p.Np) {
+            __bf16 *qt16 = p.q16 + qhead * DKP;
+#pragma unroll
+            for (int t = 0; t < DKP / 16; ++t)
+                *reinterpret_cast<bf16x8 *>(qt16 + tile_elem(myq, 16 * t + 8 * half, DKP)) = qf[t];
+        }
+        for (int i = blockIdx.x * kQNT + tid; i < p.nzero; i += gridDim.x * kQNT) p.zero[i] = 0;
+        if (blockIdx.x == 0 && tid < 4)
+            for (int k = 0; k < 3; ++k)
+                if (p.pad_lo[k] + tid < p.pad_hi[k]) p.blob[p.pad_lo[k] + tid] = 0.f;
+    }
     f32x16 oacc[DVP / 32];
 #pragma unroll
     for (int i = 0; i < DVP / 32; ++i) oacc[i] = zero16();
@@ -302,6 +326,33 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
     const float l = swap_halves_sum(l_part);
     const float inv = l > 0.f ? 1.f / l : 0.f;
+    if constexpr (PREP) {
+        // D = rowsum(dO o O) with O = Õ / l in f32, the bf16 dO row into its tile, and
+        // the row's LSE (log2 units; +inf = no weight: all-masked or past N) and D
+        if (myq >= p.Np) return;
+        const float *drow = p.dO + (size_t)p.DV * (h + p.H * (min(myq, p.N - 1) + (size_t)p.N * b));
+        __bf16 *ot16 = p.o16 + qhead * DVP;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        float dsum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int c0 = dt * 32 + 8 * r4 + 4 * half;
+                const f32x4 dv = qok ? load_row4(drow, c0, p.DV, p.vecV) : z;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dsum += dv[i] * (oacc[dt][4 * r4 + i] * inv);
+                *reinterpret_cast<bf16x4 *>(ot16 + tile_elem(myq, c0, DVP)) = to_bf16x4(dv);
+            }
+        dsum = swap_halves_sum(dsum);
+        if (half == 0) {
+            float *st = p.stats + (qhead / 64 + myq / 64) * kStatsTile + (myq & 63);
+            const bool live = qok && l > 0.f;
+            st[0] = live ? m_run + log2f(l) : INFINITY;
+            st[64] = live ? dsum : 0.f;
+        }
+        return;
+    }
     if (qok) {
         float *orow = p.O + (size_t)p.DV * (h + p.H * (myq + (size_t)p.N * b));
 #pragma unroll
@@ -529,7 +580,12 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT), 0, s, a);
+        if (a.dO)
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT), 0,
+                               s, a);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT),
+                               0, s, a);
         return hipGetLastError();
     }
 }
@@ -541,12 +597,34 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
-    FwdArgs16 a;
+    FwdArgs16 a = {};
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
+    FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
+}
+
+hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+                                    const uint8_t *map, float scale, const float *dO, __bf16 *q16, __bf16 *o16,
+                                    float *stats, float *blob, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v,
+                                    int64_t nv, int64_t total, int *zero, int nzero, int Np, int Mp, const Dims &d,
+                                    hipStream_t s)
+{
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd) || !dO || !q16 || !o16 || !stats) return hipErrorInvalidValue;
+    FwdArgs16 a = {};
+    a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
+    a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
+    a.scale = scale;
+    a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
+    a.pad_lo[0] = nq; a.pad_hi[0] = off_k;
+    a.pad_lo[1] = off_k + nk; a.pad_hi[1] = off_v;
+    a.pad_lo[2] = off_v + nv; a.pad_hi[2] = total;
+    a.zero = zero; a.nzero = nzero; a.Np = Np;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
 }
 
