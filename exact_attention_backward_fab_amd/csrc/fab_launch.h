@@ -113,8 +113,8 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
 constexpr int kDqBlock = 128, kDqSplitBlocks = 512;
 inline int64_t dq_blocks(const Dims &d) { return (int64_t)((d.N + kDqBlock - 1) / kDqBlock) * d.H * d.B; }
 inline int dq_split(const Dims &d) { return dq_blocks(d) <= kDqSplitBlocks ? 2 : 1; }
-inline int64_t dq_part_floats(const Dims &d, int dkp) { return dq_split(d) == 2 ? dq_blocks(d) * 2 * kDqBlock * dkp : 0; }
 inline int64_t dq_split_blocks(const Dims &d) { return dq_split(d) == 2 ? dq_blocks(d) : 0; }
+inline int64_t dq_part_floats(const Dims &d, int dkp) { return dq_split_blocks(d) * 2 * kDqBlock * dkp; }
 
 // Query-block-outer dQ (bf16 mode): dq [DK,N,H,B] = scale dS K, every element
 // written once; inputs as for launch_backward_bf16.  part and ticket as sized

@@ -65,6 +65,47 @@ __device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB)
     return r;
 }
 
+// Work-group -> (query block index for qouter_work, share) of the dQ kernel.
+// With split == 2 each query block is run by two work-groups (shares) that take
+// alternate live key steps; the shares of a block are 8 work-groups apart, so
+// the round-robin dispatch over the XCDs puts them on one XCD, one shortly after
+// the other.
+struct QShare {
+    int unit, share;
+};
+__device__ __forceinline__ QShare query_share(int bid, int HB, int split)
+{
+    QShare r{bid, 0};
+    if (split == 2) {
+        if (HB % 8 == 0) {
+            r.unit = (bid & 7) + 8 * (bid >> 4);
+            r.share = (bid >> 3) & 1;
+        } else {
+            r.unit = bid >> 1;
+            r.share = bid & 1;
+        }
+    }
+    return r;
+}
+
+// The two shares of a block exchange their partial results through global
+// memory with device-coherent accesses (write-through stores, loads that bypass
+// the non-coherent caches), so no cache-wide writeback or invalidate is needed:
+// a share's stores have completed (s_waitcnt vmcnt(0)) before it takes the
+// block's ticket, and the share that finds the ticket taken reads them after.
+__device__ __forceinline__ void coherent_store(float *p, float x)
+{
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ticket_take(int *t)
+{
+    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Streams the live key steps (block map) of one query block through the LDS
 // stages: the K and V tiles of later steps are copied from global memory straight
 // into LDS while body(step, class, K tile, V tile) works on the current one.  Each
@@ -405,20 +446,8 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
     const int nqt = (p.N + kQBQ - 1) / kQBQ, HB = p.H * p.B;
-    // Query block of this work-group; with split == 2 each block is run by two
-    // work-groups (shares) that take alternate live key steps.  The shares of a
-    // block are 8 work-groups apart, so the round-robin dispatch puts them on one
-    // XCD next to each other.
-    int unit = blockIdx.x, share = 0;
-    if (p.split == 2) {
-        if (HB % 8 == 0) {
-            unit = (int)(blockIdx.x & 7) + 8 * (int)(blockIdx.x >> 4);
-            share = (blockIdx.x >> 3) & 1;
-        } else {
-            unit = blockIdx.x >> 1;
-            share = blockIdx.x & 1;
-        }
-    }
+    const QShare sh = query_share(blockIdx.x, HB, p.split);
+    const int unit = sh.unit, share = sh.share;
     const QWork wk = qouter_work(unit, nqt, HB);   // latest queries first (most keys if causal)
     const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
@@ -518,10 +547,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 
     // ---- two shares: both publish their partial sums and take the block's ticket;
     // the second to arrive adds the other's partial (a + b = b + a: the result
-    // does not depend on which share that is) and stores the block.  The partials
-    // are written and read with device-coherent accesses (write-through stores,
-    // loads that bypass the non-coherent caches), so no cache-wide writeback or
-    // invalidate is needed: the stores have completed (vmcnt) before the ticket.
+    // does not depend on which share that is) and stores the block.
     if (p.split == 2) {
         constexpr int PW = DKP / 32 * 16 * 64;   // floats of one wave's partial
         float *mine = p.part + ((size_t)(2 * unit + share) * kQW + w) * PW;
@@ -529,11 +555,10 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
         for (int dt = 0; dt < DKP / 32; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                __hip_atomic_store(mine + (dt * 16 + r) * 64 + lane, dqacc[dt][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                coherent_store(mine + (dt * 16 + r) * 64 + lane, dqacc[dt][r]);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) sTicket = __hip_atomic_fetch_add(p.ticket + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) sTicket = ticket_take(p.ticket + unit);
         __syncthreads();
         if (sTicket == 0) return;   // first share: the other one finishes the block
         const float *other = p.part + ((size_t)(2 * unit + (share ^ 1)) * kQW + w) * PW;
@@ -541,8 +566,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
         for (int dt = 0; dt < DKP / 32; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dqacc[dt][r] += __hip_atomic_load(other + (dt * 16 + r) * 64 + lane, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+                dqacc[dt][r] += coherent_load(other + (dt * 16 + r) * 64 + lane);
     }
 
     // ---- store dQ (scaled): lane = head-dim column, rows = this wave's queries
@@ -580,12 +604,11 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
+        const dim3 grid(ceil_div(a.N, kQBQ) * a.H * a.B);
         if (a.dO)
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT), 0,
-                               s, a);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), grid, dim3(kQNT), 0, s, a);
         else
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B), dim3(kQNT),
-                               0, s, a);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), grid, dim3(kQNT), 0, s, a);
         return hipGetLastError();
     }
 }
