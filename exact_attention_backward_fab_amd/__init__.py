@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libfab.so")
 
 FAB_MODE_F32 = 0
 FAB_MODE_BF16 = 1
+FAB_CAUSAL = 0x100   # flag: the causal rule (key m seen by query n iff m <= n) without a mask
 MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
          FAB_MODE_BF16: FAB_MODE_BF16}
 
@@ -120,9 +121,13 @@ def blob_layout(shape: Shape):
     return tuple(x.value for x in o)
 
 
-def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False) -> int:
+def _mode(mode, causal):
+    return MODES[mode] | (FAB_CAUSAL if causal else 0)
+
+
+def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False, causal=False) -> int:
     n = ctypes.c_size_t()
-    _check(lib().fab_workspace_bytes(ctypes.byref(shape.c()), MODES[mode], int(bool(has_mask)),
+    _check(lib().fab_workspace_bytes(ctypes.byref(shape.c()), _mode(mode, causal), int(bool(has_mask)),
                                      int(bool(have_o_lse)), ctypes.byref(n)))
     return n.value
 
@@ -160,15 +165,16 @@ def _check_tensor(t, name, shape, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device):
+def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device, causal=False):
     import torch
-    n = workspace_bytes(shape, mode, has_mask, have_o_lse)
+    n = workspace_bytes(shape, mode, has_mask, have_o_lse, causal)
     # torch's caching allocator returns 512-byte aligned blocks
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
 
 
-def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None):
-    """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v."""
+def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False):
+    """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v.
+    causal=True applies the causal rule without a mask (mask must be None)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
@@ -181,18 +187,19 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     if lse is None:
         lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
     if ws is None:
-        ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev)
+        ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
     else:
         nbytes = ws.numel() * ws.element_size()
     _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
-                                 float(scale), MODES[mode], _ptr(O), _ptr(lse), _ptr(ws), nbytes,
+                                 float(scale), _mode(mode, causal), _ptr(O), _ptr(lse), _ptr(ws), nbytes,
                                  _stream_handle(stream)))
     return O, lse
 
 
 def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=None, ws=None,
-             stream=None):
-    """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v)."""
+             stream=None, causal=False):
+    """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
+    causal=True applies the causal rule without a mask (mask must be None)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
@@ -205,11 +212,11 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
     if blob is None:
         blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
     if ws is None:
-        ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev)
+        ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
     else:
         nbytes = ws.numel() * ws.element_size()
     _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                              float(scale), MODES[mode], _ptr(O), _ptr(lse), _ptr(blob),
+                              float(scale), _mode(mode, causal), _ptr(O), _ptr(lse), _ptr(blob),
                               _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 

@@ -161,6 +161,14 @@ int check_mode(int mode)
     return FAB_OK;
 }
 
+// Splits the FAB_CAUSAL flag off the mode argument and checks the rest.
+int take_mode(int *mode, bool *causal)
+{
+    *causal = (*mode & FAB_CAUSAL) != 0;
+    *mode &= ~FAB_CAUSAL;
+    return check_mode(*mode);
+}
+
 int check_ptr(const void *p, int64_t elems, const char *name)
 {
     if (elems == 0) return FAB_OK;
@@ -353,8 +361,10 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    FAB_TRY(check_mode(mode));
+    bool causal;
+    FAB_TRY(take_mode(&mode, &causal));
     if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
+    if (causal && has_mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     plan_workspace(&pl, mode, has_mask != 0, have_o_lse != 0);
     *bytes = pl.ws_bytes;
     return FAB_OK;
@@ -367,7 +377,10 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    FAB_TRY(check_mode(mode));
+    bool causal;
+    FAB_TRY(take_mode(&mode, &causal));
+    if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
+    pl.d.causal = causal;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     FAB_TRY(check_ptr(q, pl.nq, "q"));
     FAB_TRY(check_ptr(k, pl.nk, "k"));
@@ -400,7 +413,10 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    FAB_TRY(check_mode(mode));
+    bool causal;
+    FAB_TRY(take_mode(&mode, &causal));
+    if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
+    pl.d.causal = causal;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     if ((O == nullptr) != (lse == nullptr))
         return fail(FAB_E_INVAL, "O and lse must be given together or both be NULL");

@@ -35,6 +35,7 @@ struct BwdArgs {
     float *dq, *dk, *dv;
     int B, H, Hkv, N, M, DK, DV;
     int part_heads, nqb, nkb, vecK, vecV;
+    int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
 };
 
@@ -56,6 +57,7 @@ struct KvArgs {
     float *dk, *dv;
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
     int part_heads, nqb, nkb;
+    int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
 };
 
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nqt = p.Np / kKBR;
     for (int seg = 0; seg < nqt; seg += kKList) {
         const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
-            return tile_class(p.map, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
+            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
                               kKBC / kMapTile);
         });
         if (count == 0) continue;
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nqt = p.Np / kKBR;
     for (int seg = 0; seg < nqt; seg += kKList) {
         const int count = build_live_list<kKW4>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
-            return tile_class(p.map, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
+            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
                               kKBC / kMapTile);
         });
         if (count == 0) continue;
@@ -616,7 +618,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     const int nqt = (p.N + BR - 1) / BR;
 
     for (int it = 0; it < nqt; ++it) {
-        const int cls = tile_class(p.map, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile,
+        const int cls = tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile,
                                    key0 / kMapTile, BC / kMapTile);
         if (cls == kTileSkip) continue;
         const int q0 = it * BR;
@@ -792,7 +794,7 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
     a.lse = lse; a.delta = delta; a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_bwd_f32, a, s, hd, false);
@@ -809,7 +811,7 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     a.dk = dk; a.dv = dv;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_bwd_bf16, a, s, hd, true);
 }

@@ -208,12 +208,21 @@ __device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xo
 
 // Class of a kernel tile made of nq x nk map blocks starting at (qb0, kb0):
 // SKIP if every block is all -inf, FREE if every block is all zero, CAUSAL if
-// every block follows the causal rule exactly, MIXED otherwise.  A NULL map
-// (no mask) is FREE.
-__device__ __forceinline__ int tile_class(const uint8_t *map, int nqb, int nkb, int qb0, int nq,
-                                          int kb0, int nk)
+// every block follows the causal rule exactly, MIXED otherwise.  Without a map:
+// FREE, or with the causal flag (the pages' boolean mask: key m is seen by query
+// n iff m <= n) the same classes from the tile's extent alone, counted over the
+// queries < N and keys < M as the map counts them.
+__device__ __forceinline__ int tile_class(const uint8_t *map, int causal, int N, int M, int nqb, int nkb, int qb0,
+                                          int nq, int kb0, int nk)
 {
-    if (!map) return kTileFree;
+    if (!map) {
+        if (!causal) return kTileFree;
+        const int qlo = kMapTile * qb0, qhi = min(kMapTile * (qb0 + nq), N) - 1;
+        const int klo = kMapTile * kb0, khi = min(kMapTile * (kb0 + nk), M) - 1;
+        if (qlo > qhi || klo > khi || klo > qhi) return kTileSkip;   // no pair, or every key after every query
+        if (khi <= qlo) return kTileFree;
+        return kTileCausal;
+    }
     bool all_skip = true, all_free = true, all_causal = true;
     const int qe = min(qb0 + nq, nqb), ke = min(kb0 + nk, nkb);
     for (int i = qb0; i < qe; ++i)

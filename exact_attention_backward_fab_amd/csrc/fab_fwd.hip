@@ -19,6 +19,7 @@ struct FwdArgs {
     float *O, *lse;
     int B, H, Hkv, N, M, DK, DV;
     int nqb, nkb, vecK, vecV;
+    int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
 };
 
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p)
 
     for (int kt = 0; kt < nkt_total; ++kt) {
         const int key0 = kt * BC;
-        const int cls = tile_class(p.map, p.nqb, p.nkb, qt * (BR / kMapTile), BR / kMapTile,
+        const int cls = tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, qt * (BR / kMapTile), BR / kMapTile,
                                    key0 / kMapTile, BC / kMapTile);
         if (cls == kTileSkip) continue;
         __syncthreads();
@@ -200,7 +201,7 @@ hipError_t launch_forward_f32(const float *q, const float *k, const float *v, co
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_fwd, a, s, hd, false);

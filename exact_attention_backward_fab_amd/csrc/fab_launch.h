@@ -10,6 +10,7 @@ namespace fab {
 
 struct Dims {
     int B, H, Hkv, N, M, DK, DV;
+    int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
 };
 
 // Padded head dimensions (DKP, DVP) the kernels are instantiated for; a shape

@@ -233,6 +233,7 @@ struct FwdArgs16 {
     const uint8_t *map;
     float *O, *lse;                 // O [DV,H,N,B], lse [N,H,B]
     int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK, vecV;
+    int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
     // The backward's own forward (PREP) writes, instead of O and lse, what the
     // backward kernels read: the bf16 tiles of Q and dO (rows >= N and columns
@@ -296,7 +297,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     stream_key_steps<DKP, DVP>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
-            return tile_class(p.map, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
+            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
                               kQBK / kMapTile);
         },
         [&](int s, int cls, const char *Kb, const char *Vb) {
@@ -428,6 +429,7 @@ struct DqArgs {
     float *part;                    // split == 2: per-share dQ partials [blocks][2][4 waves][DKP/2 * 64]
     int *ticket;                    // split == 2: one zeroed counter per query block
     int B, H, Hkv, N, Np, M, Mp, DK, DV, nqb, nkb;
+    int causal;                     // causal rule as a flag (no mask, no map)
     int split;                      // work-groups per query block (1 or 2)
     float scale;
 };
@@ -491,7 +493,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     stream_key_steps<DKP, DVP>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
-            return tile_class(p.map, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
+            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
                               kQBK / kMapTile);
         },
         [&](int s, int cls, const char *Kb, const char *Vb) {
@@ -623,7 +625,7 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
     FwdArgs16 a = {};
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
@@ -640,7 +642,7 @@ hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __b
     FwdArgs16 a = {};
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
     a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
@@ -663,7 +665,7 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
     a.dq = dq; a.part = part; a.ticket = ticket; a.split = dq_split(d);
     if (a.split == 2 && (!part || !ticket)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile);
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_dq, a, s, hd, true);
 }

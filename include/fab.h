@@ -71,6 +71,14 @@ typedef struct fab_shape {
  *                  accumulation, the softmax statistics, D and the scale stay f32. */
 typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
 
+/* Flag OR-ed into the mode argument of fab_workspace_bytes, fab_forward_lse and
+ * fab_backward: the causal rule without a mask tensor -- key m is seen by query
+ * n iff m <= n (the boolean `masked` argument of PowerInfer's
+ * `ggml_flash_attn_back`; for N != M the same rule as the 0 / -inf f16 mask
+ * with entry (n, m) = 0 iff m <= n).  The mask pointer must then be NULL
+ * (has_mask = 0), else FAB_E_INVAL; no block map is built and no mask is read. */
+#define FAB_CAUSAL 0x100
+
 typedef enum fab_status {
     FAB_OK = 0,
     FAB_E_INVAL = -1,        /* bad shape, NULL pointer, bad scale or mode */
@@ -97,7 +105,7 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
  *   q, k, v   device, f32, layouts above (read only)
  *   mask      device f16 bits [M,N] or NULL for no mask (read only)
  *   scale     finite f32 softmax scale
- *   mode      fab_mode
+ *   mode      fab_mode, optionally | FAB_CAUSAL (then mask must be NULL)
  *   O         device f32 [DV,H,N,B] (written): softmax(scale*q.k + mask) v
  *   lse       device f32 [N,H,B] (written): natural-log log-sum-exp of the row's
  *             scores, -inf for an all-masked row

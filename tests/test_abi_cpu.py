@@ -94,10 +94,24 @@ GOOD = (1, 4, 2, 8, 8, 16, 16)
     (GOOD, {"ws": FAKE + 16}, fab.FAB_E_ALIGN),
     (GOOD, {"ws": None}, fab.FAB_E_WORKSPACE),
     (GOOD, {"ws_bytes": 16}, fab.FAB_E_WORKSPACE),
+    (GOOD, {"mode": fab.FAB_CAUSAL, "mask": FAKE}, fab.FAB_E_INVAL),         # mask and causal flag
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x200}, fab.FAB_E_INVAL),           # unknown flag bit
 ])
 def test_backward_rejects_bad_arguments_before_device_work(shape, kw, code):
     assert call_bwd(shape, **kw) == code
     assert fab.lib().fab_last_error().decode() != ""
+
+
+def test_causal_flag_workspace():
+    # the causal flag needs no block map: the same workspace as no mask; with a
+    # mask it is rejected
+    s = fab.Shape(1, 8, 2, 300, 400, 64, 64)
+    for mode in ("f32", "bf16"):
+        assert fab.workspace_bytes(s, mode, False, False, causal=True) == fab.workspace_bytes(s, mode, False, False)
+        assert fab.workspace_bytes(s, mode, True, False) > fab.workspace_bytes(s, mode, False, False, causal=True)
+    with pytest.raises(fab.FabError) as e:
+        fab.workspace_bytes(s, "bf16", True, False, causal=True)
+    assert e.value.code == fab.FAB_E_INVAL
 
 
 def test_forward_rejects_bad_arguments():

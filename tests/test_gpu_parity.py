@@ -221,6 +221,63 @@ def test_bf16_repeat_is_bitwise_stable(torch_dev):
     check_blob(s, outs[0], ref, "bf16", tag="repeat", mask=mask)
 
 
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_autograd_grads_are_views_of_one_blob(torch_dev, mode):
+    # [RT] "autodiff views address their own slice of the packed buffer": through
+    # torch.autograd, the three gradients are views of one blob at its padded
+    # offsets, and they match the oracle
+    torch, dev = torch_dev
+    fab = fabmod()
+    from exact_attention_backward_fab_amd.autograd import attention
+    s = Shape(2, 4, 2, 150, 170, 64, 48)
+    q, k, v, d = make_qkvd(s, 101)
+    mask = random_mask(s.N, s.M, 101, p_inf=0.3, full_rows=1, full_cols=1)
+    scale = 0.125
+    tq, tk, tv = [to_dev(torch, dev, x).requires_grad_(True) for x in (q, k, v)]
+    O = attention(tq, tk, tv, mask=to_dev(torch, dev, mask), scale=scale, mode=mode)
+    gq, gk, gv = torch.autograd.grad(O, (tq, tk, tv), grad_outputs=to_dev(torch, dev, d))
+    base = gq.untyped_storage().data_ptr()
+    assert gk.untyped_storage().data_ptr() == base and gv.untyped_storage().data_ptr() == base
+    _, off_k, off_v, _ = fab.blob_layout(fab.Shape(*s.astuple()))
+    assert (gq.storage_offset(), gk.storage_offset(), gv.storage_offset()) == (0, off_k, off_v)
+    ref = oracle_full(s, q, k, v, d, mask, scale)
+    for name, g in (("dq", gq), ("dk", gk), ("dv", gv)):
+        assert rel_err(g.cpu().numpy(), ref[name]) <= TOL[mode], name
+
+
+CAUSAL_FLAG = [
+    ("square_gqa", Shape(1, 4, 2, 333, 333, 128, 128), 51),
+    ("n_gt_m", Shape(2, 2, 1, 300, 130, 64, 64), 52),
+    ("n_lt_m", Shape(1, 3, 3, 97, 260, 40, 72), 53),
+    ("d192", Shape(1, 2, 1, 200, 200, 192, 128), 54),
+]
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+@pytest.mark.parametrize("name,s,seed", CAUSAL_FLAG, ids=[c[0] for c in CAUSAL_FLAG])
+def test_causal_flag_equals_causal_mask(torch_dev, name, s, seed, mode):
+    # FAB_CAUSAL (no mask tensor, no block map) against the oracle on the explicit
+    # 0 / -inf causal mask, and bit for bit against the library's own masked path
+    torch, dev = torch_dev
+    fab = fabmod()
+    print(f"[parity] causal flag {name} {mode} {s}", flush=True)
+    q, k, v, d = make_qkvd(s, seed)
+    mask = causal_mask(s.N, s.M)
+    scale = float(np.float32(1.0 / math.sqrt(s.DK)))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    flag = fab.backward(*t, scale, mode=mode, causal=True)
+    masked = fab.backward(*t, scale, mask=to_dev(torch, dev, mask), mode=mode)
+    O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mode=mode, causal=True)
+    torch.cuda.synchronize()
+    flag = flag[:fab.blob_layout(fab.Shape(*s.astuple()))[3]].cpu().numpy()
+    ref = oracle_full(s, q, k, v, d, mask, scale)
+    check_blob(s, flag, ref, mode, tag=f"causal flag {name}/{mode}", mask=mask)
+    assert np.array_equal(flag.view(np.uint32), masked[:flag.size].cpu().numpy().view(np.uint32))
+    from oracle import oracle as orc
+    O_ref, _ = orc.forward(s, q, k, v, mask, scale)
+    assert rel_err(O.cpu().numpy(), O_ref) <= TOL[mode]
+
+
 def test_d_ones_closed_form_on_gpu(torch_dev):
     # d = ones: every component of dV[:, m] equals the summed attention weight of key m
     torch, dev = torch_dev
