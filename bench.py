@@ -10,7 +10,8 @@ O), the key-block-outer dK/dV kernel, the query-block-outer dQ kernel, the
 grouped-query reduction and the blob packing).  `value` counts the work that
 pass must do: forward 2*N*M*(DK+DV)*H*B plus the backward 10*N*M*(DK+DV)/2*H*B,
 each halved under a causal mask, over K steps timed with two HIP events on the
-launch stream and nothing else in between.  The same K steps are then run
+launch stream and nothing else in between (after at least W warm-up steps and
+1 s of warm-up; the median of three such runs).  The same K steps are then run
 again with every kernel bracketed by HIP events (which adds gaps between the
 kernels: `ms_per_step_with_kernel_events`) for every kernel's time per step
 and its algorithmic rate (TFLOP/s for the matrix-core kernels, GB/s for the
@@ -18,7 +19,9 @@ memory-bound ones) and the `roofline` object of the dominant kernel.  The line
 also reports the backward alone (O and LSE supplied by a prior forward, the
 usual training convention) and the forward alone, and (`other_workloads`,
 --also) the whole step and the backward alone of further workloads, by
-default the long-context one.  `cpu_baseline` times the
+default the long-context one.  Causal workloads are also timed with the causal
+rule passed as a flag instead of the mask tensor (`causal_flag_instead_of_mask`:
+same result, no block map or mask reads).  `cpu_baseline` times the
 f64 CPU oracle on a bounded sample of the same workload on this host's cores.
 
 Prints exactly one JSON line.
@@ -124,24 +127,37 @@ def parse():
     ap.add_argument("--also", default="4",
                     help="comma-separated workloads also timed (whole step and backward alone), '' for none")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--min-warm-s", type=float, default=1.0,
+                    help="warm-up of every timed loop lasts at least this long (seconds of GPU work)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (the known-size "
                          "reference of the HBM byte counters)")
     return ap.parse_args()
 
 
-def time_loop(torch, fn, steps, warmup, stream):
-    for _ in range(warmup):
+def time_loop(torch, fn, steps, warmup, stream, min_warm_s=1.0, repeats=3):
+    # warm-up: at least `warmup` steps and at least min_warm_s of GPU work (the
+    # chip's clocks settle over the first tens of milliseconds of load)
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < min_warm_s:
         fn()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    # three back-to-back timed runs of `steps` steps each; the median run counts
+    runs = []
+    for _ in range(repeats):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / steps)
+    return sorted(runs)[len(runs) // 2]
 
 
 def cpu_baseline(s, q, k, v, d, mask, scale, causal, budget_s):
@@ -237,13 +253,13 @@ def main():
         del a, b
 
     # ---- timed region: the whole path, K steps with nothing but the launches
-    ms_step = time_loop(torch, step_full, args.steps, args.warmup, stream)
+    ms_step = time_loop(torch, step_full, args.steps, args.warmup, stream, args.min_warm_s)
     # ---- the same K steps again with every kernel bracketed by HIP events on its
     # launch stream: per-kernel durations (the event records add gaps between the
     # kernels, so this pass is not the one `value` is taken from)
     fab.profile_reset()
     fab.profile_enable(True)
-    ms_step_prof = time_loop(torch, step_full, args.steps, 0, stream)
+    ms_step_prof = time_loop(torch, step_full, args.steps, 0, stream, min_warm_s=0.0, repeats=1)
     prof = fab.profile_read()
     fab.profile_enable(False)
     fab.profile_reset()
@@ -251,8 +267,8 @@ def main():
     # ---- the backward alone (O, LSE from a prior forward) and the forward alone
     step_fwd()
     torch.cuda.synchronize()
-    ms_bwd = time_loop(torch, step_bwd, args.steps, args.warmup, stream)
-    ms_fwd = time_loop(torch, step_fwd, args.steps, args.warmup, stream)
+    ms_bwd = time_loop(torch, step_bwd, args.steps, args.warmup, stream, args.min_warm_s)
+    ms_fwd = time_loop(torch, step_fwd, args.steps, args.warmup, stream, args.min_warm_s)
 
     F_f, F_b = fwd_flops(s, causal), bwd_flops(s, causal)
     peak = PEAK_TFLOPS[mode]
@@ -312,6 +328,17 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    # ---- the same step with the causal rule given as a flag instead of the mask
+    # tensor (identical result; no block map, no mask reads)
+    mask_free = None
+    if causal:
+        ws_c, _ = fab.alloc_workspace(fs, mode, False, False, dev, causal=True)
+        ms_c = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mode=mode, blob=blob, ws=ws_c,
+                                                     causal=True), args.steps, args.warmup, stream, args.min_warm_s)
+        mask_free = {"ms_per_step": round(ms_c, 4), "value": round((F_f + F_b) / (ms_c * 1e-3) / 1e12, 3),
+                     "frac_of_peak": round((F_f + F_b) / (ms_c * 1e-3) / 1e12 / peak, 4)}
+        del ws_c
+
     # ---- other workloads (e.g. the long-context one), same protocol, same mode
     also = {}
     for wid in [int(x) for x in args.also.split(",") if x.strip()]:
@@ -330,15 +357,26 @@ def main():
         ws2b, _ = fab.alloc_workspace(fs2, mode, tm2 is not None, True, dev)
         O2, lse2 = fab.forward_lse(t2[0], t2[1], t2[2], scale2, mask=tm2, mode=mode, ws=ws2b)
         ms2 = time_loop(torch, lambda: fab.backward(*t2, scale2, mask=tm2, mode=mode, blob=blob2, ws=ws2),
-                        args.steps, args.warmup, stream)
+                        args.steps, args.warmup, stream, args.min_warm_s)
         ms2b = time_loop(torch, lambda: fab.backward(*t2, scale2, mask=tm2, mode=mode, O=O2, lse=lse2, blob=blob2,
-                                                     ws=ws2b), args.steps, args.warmup, stream)
+                                                     ws=ws2b), args.steps, args.warmup, stream, args.min_warm_s)
+        ms2c = None
+        if c2:
+            ws2c, _ = fab.alloc_workspace(fs2, mode, False, False, dev, causal=True)
+            ms2c = time_loop(torch, lambda: fab.backward(*t2, scale2, mode=mode, blob=blob2, ws=ws2c, causal=True),
+                             args.steps, args.warmup, stream, args.min_warm_s)
+            del ws2c
         Ff2, Fb2 = fwd_flops(s2, c2), bwd_flops(s2, c2)
         also[w2.name] = {"ms_per_step": round(ms2, 4), "value": round((Ff2 + Fb2) / (ms2 * 1e-3) / 1e12, 3),
                          "frac_of_peak": round((Ff2 + Fb2) / (ms2 * 1e-3) / 1e12 / peak, 4),
                          "backward_only": {"ms": round(ms2b, 4), "tflops": round(Fb2 / (ms2b * 1e-3) / 1e12, 3),
                                            "frac_of_peak": round(Fb2 / (ms2b * 1e-3) / 1e12 / peak, 4)}}
+        if ms2c:
+            also[w2.name]["causal_flag_instead_of_mask"] = {
+                "ms_per_step": round(ms2c, 4), "value": round((Ff2 + Fb2) / (ms2c * 1e-3) / 1e12, 3)}
         del t2, tm2, blob2, ws2, ws2b, O2, lse2
+    if mask_free:
+        out["causal_flag_instead_of_mask"] = mask_free
     if also:
         out["other_workloads"] = also
     if not args.no_cpu_baseline:

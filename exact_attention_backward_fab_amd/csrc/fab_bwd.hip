@@ -176,8 +176,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nqt = p.Np / kKBR;
     for (int seg = 0; seg < nqt; seg += kKList) {
         const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
-            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
-                              kKBC / kMapTile);
+            return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
+                              key0 / kMapTile);
         });
         if (count == 0) continue;
 #pragma unroll
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nqt = p.Np / kKBR;
     for (int seg = 0; seg < nqt; seg += kKList) {
         const int count = build_live_list<kKW4>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
-            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile), kKBR / kMapTile, key0 / kMapTile,
-                              kKBC / kMapTile);
+            return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
+                              key0 / kMapTile);
         });
         if (count == 0) continue;
 #pragma unroll
@@ -618,8 +618,8 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     const int nqt = (p.N + BR - 1) / BR;
 
     for (int it = 0; it < nqt; ++it) {
-        const int cls = tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (BR / kMapTile), BR / kMapTile,
-                                   key0 / kMapTile, BC / kMapTile);
+        const int cls = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
+                                                                 it * (BR / kMapTile), key0 / kMapTile);
         if (cls == kTileSkip) continue;
         const int q0 = it * BR;
         __syncthreads();  // the previous step is done with sQ, sO, sS

@@ -206,31 +206,44 @@ __device__ __forceinline__ float group_sum(float x, int width)
 __device__ __forceinline__ float swap_halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float swap_halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
-// Class of a kernel tile made of nq x nk map blocks starting at (qb0, kb0):
+// Class of a kernel tile made of NQ x NK map blocks starting at (qb0, kb0):
 // SKIP if every block is all -inf, FREE if every block is all zero, CAUSAL if
-// every block follows the causal rule exactly, MIXED otherwise.  Without a map:
-// FREE, or with the causal flag (the pages' boolean mask: key m is seen by query
-// n iff m <= n) the same classes from the tile's extent alone, counted over the
-// queries < N and keys < M as the map counts them.
+// every block follows the causal rule exactly, MIXED otherwise; blocks past the
+// map's extent do not count.  Without a map: FREE, or with the causal flag (the
+// pages' boolean mask: key m is seen by query n iff m <= n) the same classes from
+// the tile's extent alone, counted over the queries < N and keys < M as the map
+// counts them.  The map bytes of a tile are loaded together (one latency).
+template <int NQ, int NK>
 __device__ __forceinline__ int tile_class(const uint8_t *map, int causal, int N, int M, int nqb, int nkb, int qb0,
-                                          int nq, int kb0, int nk)
+                                          int kb0)
 {
     if (!map) {
         if (!causal) return kTileFree;
-        const int qlo = kMapTile * qb0, qhi = min(kMapTile * (qb0 + nq), N) - 1;
-        const int klo = kMapTile * kb0, khi = min(kMapTile * (kb0 + nk), M) - 1;
+        const int qlo = kMapTile * qb0, qhi = min(kMapTile * (qb0 + NQ), N) - 1;
+        const int klo = kMapTile * kb0, khi = min(kMapTile * (kb0 + NK), M) - 1;
         if (qlo > qhi || klo > khi || klo > qhi) return kTileSkip;   // no pair, or every key after every query
         if (khi <= qlo) return kTileFree;
         return kTileCausal;
     }
+    uint8_t c[NQ][NK];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const bool in = qb0 + i < nqb && kb0 + j < nkb;
+            // a block outside the map counts as SKIP, FREE and causal at once
+            c[i][j] = in ? map[(qb0 + i) * nkb + kb0 + j] : (uint8_t)0xFF;
+        }
     bool all_skip = true, all_free = true, all_causal = true;
-    const int qe = min(qb0 + nq, nqb), ke = min(kb0 + nk, nkb);
-    for (int i = qb0; i < qe; ++i)
-        for (int j = kb0; j < ke; ++j) {
-            const uint8_t c = map[i * nkb + j];
-            all_skip = all_skip && ((c & 3) == kBlockSkip);
-            all_free = all_free && ((c & 3) == kBlockFree);
-            all_causal = all_causal && ((c & kBlockCausalBit) != 0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const uint8_t x = c[i][j];
+            const bool out = x == 0xFF;
+            all_skip = all_skip && (out || (x & 3) == kBlockSkip);
+            all_free = all_free && (out || (x & 3) == kBlockFree);
+            all_causal = all_causal && (out || (x & kBlockCausalBit) != 0);
         }
     if (all_skip) return kTileSkip;
     if (all_free) return kTileFree;

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p)
 
     for (int kt = 0; kt < nkt_total; ++kt) {
         const int key0 = kt * BC;
-        const int cls = tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, qt * (BR / kMapTile), BR / kMapTile,
-                                   key0 / kMapTile, BC / kMapTile);
+        const int cls = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
+                                                                 qt * (BR / kMapTile), key0 / kMapTile);
         if (cls == kTileSkip) continue;
         __syncthreads();
         // ---- stage K and V rows

@@ -297,8 +297,8 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     stream_key_steps<DKP, DVP>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
-            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
-                              kQBK / kMapTile);
+            return tile_class<kQBQ / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
+                              s * (kQBK / kMapTile));
         },
         [&](int s, int cls, const char *Kb, const char *Vb) {
             const int key0 = s * kQBK;
@@ -493,8 +493,8 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     stream_key_steps<DKP, DVP>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
-            return tile_class(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile, kQBQ / kMapTile, s * (kQBK / kMapTile),
-                              kQBK / kMapTile);
+            return tile_class<kQBQ / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
+                              s * (kQBK / kMapTile));
         },
         [&](int s, int cls, const char *Kb, const char *Vb) {
             const int key0 = s * kQBK;
