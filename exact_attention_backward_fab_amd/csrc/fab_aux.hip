@@ -22,38 +22,43 @@
 namespace fab {
 
 // ============================================================== block map
-// One wave per 32x32 block, 4 blocks per work-group: lane l reads row l/2 of the
-// block, columns 16 (l & 1)..+15 (two 16-byte loads when the row is aligned).
+// A work-group classifies one 32-row strip of 8 blocks (32 x 256 mask entries):
+// thread t reads row t / 8, the 64 bytes of block t % 8 in that row, so each wave
+// reads 8 rows of 512 contiguous bytes.  A block's flags are and-ed over its 32
+// rows in LDS.  Entries past N or M do not count.
+constexpr int kMapStrip = 8;   // blocks per work-group
 __global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restrict__ mask,
                                                         uint8_t *__restrict__ map, int N, int M,
                                                         int nqb, int nkb)
 {
-    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= nqb * nkb) return;   // whole waves: the votes below stay within one wave
-    const int qb = blk / nkb, kb = blk - qb * nkb;
-    const int lane = threadIdx.x & 63;
-    const int n = qb * kMapTile + (lane >> 1);
-    const int m0 = kb * kMapTile + (lane & 1) * 16;
+    __shared__ int sFlag[kMapStrip][3];   // all -inf, all zero, follows the causal rule
+    const int strips = (nkb + kMapStrip - 1) / kMapStrip;
+    const int qb = blockIdx.x / strips, kb0 = (blockIdx.x - qb * strips) * kMapStrip;
+    const int tid = threadIdx.x, j = tid & (kMapStrip - 1), kb = kb0 + j;
+    if (tid < kMapStrip * 3) sFlag[tid / 3][tid % 3] = 1;
+    __syncthreads();
+    const int n = qb * kMapTile + (tid >> 3);
+    const int m0 = kb * kMapTile;
     bool all_inf = true, all_zero = true, causal = true;
-    if (n < N) {
+    if (n < N && kb < nkb) {
         const uint16_t *row = mask + (size_t)n * M;
-        uint16_t x[16];
-        if ((M & 7) == 0 && m0 + 16 <= M) {
-            const u32x4 a = *reinterpret_cast<const u32x4 *>(row + m0);
-            const u32x4 b = *reinterpret_cast<const u32x4 *>(row + m0 + 8);
+        uint16_t x[kMapTile];
+        if ((M & 7) == 0 && m0 + kMapTile <= M) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = (uint16_t)(a[i] & 0xFFFFu);
-                x[2 * i + 1] = (uint16_t)(a[i] >> 16);
-                x[8 + 2 * i] = (uint16_t)(b[i] & 0xFFFFu);
-                x[8 + 2 * i + 1] = (uint16_t)(b[i] >> 16);
+            for (int c = 0; c < kMapTile / 8; ++c) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(row + m0 + 8 * c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[8 * c + 2 * i] = (uint16_t)(a[i] & 0xFFFFu);
+                    x[8 * c + 2 * i + 1] = (uint16_t)(a[i] >> 16);
+                }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = m0 + i < M ? row[m0 + i] : (uint16_t)0xFC00u;
+            for (int i = 0; i < kMapTile; ++i) x[i] = m0 + i < M ? row[m0 + i] : (uint16_t)0xFC00u;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < kMapTile; ++i) {
             const int m = m0 + i;
             if (m < M) {
                 const bool is_inf = x[i] == 0xFC00u, is_zero = (x[i] & 0x7FFFu) == 0;
@@ -63,12 +68,13 @@ __global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restri
             }
         }
     }
-    all_inf = __all(all_inf);
-    all_zero = __all(all_zero);
-    causal = __all(causal);
-    if (lane == 0) {
-        const uint8_t cls = all_inf ? kBlockSkip : (all_zero ? kBlockFree : kBlockMixed);
-        map[qb * nkb + kb] = cls | (causal ? kBlockCausalBit : 0);
+    if (!all_inf) atomicAnd(&sFlag[j][0], 0);
+    if (!all_zero) atomicAnd(&sFlag[j][1], 0);
+    if (!causal) atomicAnd(&sFlag[j][2], 0);
+    __syncthreads();
+    if (tid < kMapStrip && kb0 + tid < nkb) {
+        const uint8_t cls = sFlag[tid][0] ? kBlockSkip : (sFlag[tid][1] ? kBlockFree : kBlockMixed);
+        map[qb * nkb + kb0 + tid] = cls | (sFlag[tid][2] ? kBlockCausalBit : 0);
     }
 }
 
@@ -327,9 +333,8 @@ hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, h
 {
     const int nqb = (d.N + kMapTile - 1) / kMapTile, nkb = (d.M + kMapTile - 1) / kMapTile;
     if (nqb == 0 || nkb == 0) return hipSuccess;
-    const int64_t blocks = (int64_t)nqb * nkb;
-    hipLaunchKernelGGL(block_map_kernel, dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, s, mask, map, d.N, d.M,
-                       nqb, nkb);
+    const int64_t groups = (int64_t)nqb * ((nkb + kMapStrip - 1) / kMapStrip);
+    hipLaunchKernelGGL(block_map_kernel, dim3((unsigned)groups), dim3(256), 0, s, mask, map, d.N, d.M, nqb, nkb);
     return hipGetLastError();
 }
 
