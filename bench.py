@@ -82,7 +82,7 @@ def bwd_flops(s, causal):
     return f / 2 if causal else f
 
 
-def kernel_work(s, causal, mode):
+def kernel_work(s, causal, mode, has_mask):
     """Algorithmic work of one launch-set of each kernel in a step: (amount,
     unit), flops for the matrix-core kernels and bytes for the memory-bound
     ones.  A causal mask halves the (query, key) pairs the contractions visit."""
@@ -107,9 +107,10 @@ def kernel_work(s, causal, mode):
         # f32: read d and O, write D and zero the dQ slice
         "prep": ((rows * (8.0 * s.DV + 4.0) + s.H * s.B * (np_ * dvp * 2.0 + np_ / 64 * 512.0)) if bf16
                  else rows * (8.0 * s.DV + 4.0) + rows * s.DK * 4.0, "byte"),
-        # read K, V (and Q) in f32, write the bf16 tiles
+        # (the whole step, bf16) read K, V in f32, write the bf16 tiles, and, with a
+        # mask, read it and write its block map in the same launch
         "pack": (s.Hkv * s.B * (4.0 * s.M * (s.DK + s.DV) + 2.0 * mp * (dkp + dvp))
-                 + s.H * s.B * (4.0 * s.N * s.DK + 2.0 * np_ * dkp), "byte"),
+                 + ((2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32)) if has_mask else 0.0), "byte"),
         # read per-query-head partials, write per-group sums
         "gqa_reduce": (4.0 * s.M * (s.DK + s.DV) * s.B * (s.H + s.Hkv), "byte"),
     }
@@ -272,7 +273,7 @@ def main():
 
     F_f, F_b = fwd_flops(s, causal), bwd_flops(s, causal)
     peak = PEAK_TFLOPS[mode]
-    work = kernel_work(s, causal, mode)
+    work = kernel_work(s, causal, mode, mask is not None)
     kernels = {}
     for name, (tot_ms, launches) in prof.items():
         if not launches:

@@ -258,10 +258,12 @@ struct ProfScope {
     } while (0)
 
 // The bf16 tiles of Q (when q16 is given), K and V (bf16 mode), one launch.
+// (and the block map of the mask when map is given: the same launch)
 int launch_pack(const Plan &pl, const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
-                __bf16 *v16, hipStream_t s)
+                __bf16 *v16, const uint16_t *mask, uint8_t *map, hipStream_t s)
 {
-    FAB_LAUNCH(kPack, fab::launch_pack_qkv(q16 ? q : nullptr, k, v, q16, k16, v16, pl.np, pl.mp, pl.d, s),
+    FAB_LAUNCH(kPack,
+               fab::launch_pack_qkv(q16 ? q : nullptr, k, v, q16, k16, v16, mask, map, pl.np, pl.mp, pl.d, s),
                "pack launch");
     return FAB_OK;
 }
@@ -400,8 +402,10 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     const int bf16 = mode == FAB_MODE_BF16;
     __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
     __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
-    if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mask, map, pl.d, s), "block map launch");
-    if (bf16) FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, s));
+    if (bf16)
+        FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, mask, map, s));
+    else if (map)
+        FAB_LAUNCH(kMap, fab::launch_block_map(mask, map, pl.d, s), "block map launch");
     FAB_TRY(launch_fwd(pl, bf16, q, k, v, k16, v16, use_mask ? mask : nullptr, map, scale, O, lse, s));
     return FAB_OK;
 }
@@ -450,7 +454,7 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
     __bf16 *k16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_k16) : nullptr;
     __bf16 *v16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_v16) : nullptr;
     __bf16 *q16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_q16) : nullptr;
-    if (map) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
+    if (map && !bf16) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
     __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
     float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
     float *dqp = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_dqp) : nullptr;
@@ -462,13 +466,13 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
         // the backward's own forward writes the Q and dO tiles and the LSE/D blocks
         // directly (no O, no separate prep pass); dQ is written once by the
         // query-block-outer kernel (only its pad is zeroed)
-        FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, s));
+        FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, mk, map, s));
         FAB_LAUNCH(kFwd, fab::launch_forward_prep_bf16(q, k16, v16, mk, map, scale, d, q16, o16, stats, blob, pl.nq,
                                                        pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, tick, ntick, pl.np,
                                                        pl.mp, pl.d, s),
                    "forward launch");
     } else if (bf16) {
-        FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, s));
+        FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, mk, map, s));
         FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, O, lse, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
                                                 pl.off_v, pl.nv, pl.total, tick, ntick, pl.d, s),
                    "prep launch");

@@ -27,13 +27,12 @@ namespace fab {
 // reads 8 rows of 512 contiguous bytes.  A block's flags are and-ed over its 32
 // rows in LDS.  Entries past N or M do not count.
 constexpr int kMapStrip = 8;   // blocks per work-group
-__global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restrict__ mask,
-                                                        uint8_t *__restrict__ map, int N, int M,
-                                                        int nqb, int nkb)
+__device__ __forceinline__ void block_map_strip(const uint16_t *__restrict__ mask, uint8_t *__restrict__ map, int N,
+                                                int M, int nqb, int nkb, int group)
 {
     __shared__ int sFlag[kMapStrip][3];   // all -inf, all zero, follows the causal rule
     const int strips = (nkb + kMapStrip - 1) / kMapStrip;
-    const int qb = blockIdx.x / strips, kb0 = (blockIdx.x - qb * strips) * kMapStrip;
+    const int qb = group / strips, kb0 = (group - qb * strips) * kMapStrip;
     const int tid = threadIdx.x, j = tid & (kMapStrip - 1), kb = kb0 + j;
     if (tid < kMapStrip * 3) sFlag[tid / 3][tid % 3] = 1;
     __syncthreads();
@@ -76,6 +75,19 @@ __global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restri
         const uint8_t cls = sFlag[tid][0] ? kBlockSkip : (sFlag[tid][1] ? kBlockFree : kBlockMixed);
         map[qb * nkb + kb0 + tid] = cls | (sFlag[tid][2] ? kBlockCausalBit : 0);
     }
+}
+
+__global__ __launch_bounds__(256) void block_map_kernel(const uint16_t *__restrict__ mask,
+                                                        uint8_t *__restrict__ map, int N, int M,
+                                                        int nqb, int nkb)
+{
+    block_map_strip(mask, map, N, M, nqb, nkb, blockIdx.x);
+}
+
+inline int64_t map_groups(int N, int M)
+{
+    const int nqb = (N + kMapTile - 1) / kMapTile, nkb = (M + kMapTile - 1) / kMapTile;
+    return (int64_t)nqb * ((nkb + kMapStrip - 1) / kMapStrip);
 }
 
 // ============================================================== zero fill
@@ -210,12 +222,21 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
 // work-groups [0, t0) job 0, [t0, t0 + t1) job 1, the rest job 2.
 struct PackJobs {
     PackJob j[3];
+    // the mask's block map in the same launch (work-groups [0, map_groups))
+    const uint16_t *mask;
+    uint8_t *map;
+    int N, M, nqb, nkb, map_groups;
 };
 
 template <int DKP, int DVP>
 __global__ __launch_bounds__(256) void pack_qkv_kernel(PackJobs a)
 {
     int bt = blockIdx.x;
+    if (bt < a.map_groups) {
+        block_map_strip(a.mask, a.map, a.N, a.M, a.nqb, a.nkb, bt);
+        return;
+    }
+    bt -= a.map_groups;
     if (bt < a.j[0].tiles) {
         pack_tile<DKP>(a.j[0], bt, nullptr);
         return;
@@ -253,7 +274,7 @@ PackJob rows_job(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, in
 template <int DKP, int DVP, bool BF16>
 hipError_t run_pack(const PackJobs &a, hipStream_t s)
 {
-    const int64_t grid = (int64_t)a.j[0].tiles + a.j[1].tiles + a.j[2].tiles;
+    const int64_t grid = (int64_t)a.map_groups + a.j[0].tiles + a.j[1].tiles + a.j[2].tiles;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((pack_qkv_kernel<DKP, DVP>), dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -261,7 +282,7 @@ hipError_t run_pack(const PackJobs &a, hipStream_t s)
 }  // namespace
 
 hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
-                           int Np, int Mp, const Dims &d, hipStream_t s)
+                           const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
@@ -270,6 +291,11 @@ hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf1
     a.j[0] = rows_job(q, q16, qh, d.N, Np, d.DK);
     a.j[1] = rows_job(k, k16, kh, d.M, Mp, d.DK);
     a.j[2] = rows_job(v, v16, kh, d.M, Mp, d.DV);
+    if (map) {
+        a.mask = mask; a.map = map; a.N = d.N; a.M = d.M;
+        a.nqb = (d.N + kMapTile - 1) / kMapTile; a.nkb = (d.M + kMapTile - 1) / kMapTile;
+        a.map_groups = (int)map_groups(d.N, d.M);
+    }
     FAB_DISPATCH_HEAD_DIMS(run_pack, a, s, hd, true);
 }
 
@@ -333,8 +359,8 @@ hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, h
 {
     const int nqb = (d.N + kMapTile - 1) / kMapTile, nkb = (d.M + kMapTile - 1) / kMapTile;
     if (nqb == 0 || nkb == 0) return hipSuccess;
-    const int64_t groups = (int64_t)nqb * ((nkb + kMapStrip - 1) / kMapStrip);
-    hipLaunchKernelGGL(block_map_kernel, dim3((unsigned)groups), dim3(256), 0, s, mask, map, d.N, d.M, nqb, nkb);
+    hipLaunchKernelGGL(block_map_kernel, dim3((unsigned)map_groups(d.N, d.M)), dim3(256), 0, s, mask, map, d.N, d.M,
+                       nqb, nkb);
     return hipGetLastError();
 }
 

@@ -86,9 +86,10 @@ constexpr int kPackRows = 64;
 
 // f32 rows -> bf16 tiles (fab_tiles.h), one launch: q [DK,N,H,B] -> q16 [B,H,Np,DKP]
 // (skipped when q is NULL), k / v -> k16 / v16 [B,Hkv,Mp,DKP / DVP]; rows past the
-// data and columns past DK / DV zero.
+// data and columns past DK / DV zero.  With map, the same launch also builds the
+// mask's block map (as launch_block_map).
 hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
-                           int Np, int Mp, const Dims &d, hipStream_t s);
+                           const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s);
 
 // Key-block-outer backward, f32 mode: dV, dK per key tile (stored into dk/dv with
 // per-query-head layout when part_heads != 0) and dQ by f32 atomics into dq
