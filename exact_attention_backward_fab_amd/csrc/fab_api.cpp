@@ -504,8 +504,8 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
                    "backward launch");
     }
     if (pl.gqa) {
-        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, pl.d.DK, pl.d, s), "dK reduce launch");
-        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dv, blob + pl.off_v, pl.d.DV, pl.d, s), "dV reduce launch");
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, s),
+                   "dK/dV reduce launch");
     }
     return FAB_OK;
 }

@@ -327,30 +327,40 @@ hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, _
 }
 
 // ============================================================== GQA reduce
-__global__ __launch_bounds__(256) void gqa_reduce_kernel(const float *__restrict__ part,
-                                                         float *__restrict__ dst, int64_t chunk,
-                                                         int rk2, int64_t groups, int vec)
+// dK and dV in one launch: work items [0, n0) reduce job 0, the rest job 1; each
+// sums the rk2 per-query-head partials of a group in head order.
+struct ReduceJob {
+    const float *part;
+    float *dst;
+    int64_t chunk;   // floats of one head's slice (D * M)
+    int vec;         // chunk % 4 == 0: float4 items
+    int64_t items;   // work items (float4 or float) over all groups
+};
+__device__ __forceinline__ void reduce_item(const ReduceJob &r, int rk2, int64_t i)
+{
+    if (r.vec) {
+        const int64_t c4 = r.chunk / 4, gb = i / c4, off = i - gb * c4;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(r.part) + gb * rk2 * c4 + off;
+        f32x4 s = src[0];
+        for (int k = 1; k < rk2; ++k) s += src[k * c4];
+        reinterpret_cast<f32x4 *>(r.dst)[i] = s;
+    } else {
+        const int64_t gb = i / r.chunk, off = i - gb * r.chunk;
+        const float *src = r.part + gb * rk2 * r.chunk + off;
+        float s = src[0];
+        for (int k = 1; k < rk2; ++k) s += src[k * r.chunk];
+        r.dst[i] = s;
+    }
+}
+__global__ __launch_bounds__(256) void gqa_reduce_kernel(ReduceJob j0, ReduceJob j1, int rk2)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (vec) {
-        const int64_t c4 = chunk / 4, total4 = c4 * groups;
-        for (int64_t i = i0; i < total4; i += stride) {
-            const int64_t gb = i / c4, off = i - gb * c4;
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + gb * rk2 * c4 + off;
-            f32x4 s = src[0];
-            for (int r = 1; r < rk2; ++r) s += src[r * c4];
-            reinterpret_cast<f32x4 *>(dst)[i] = s;
-        }
-    } else {
-        const int64_t total = chunk * groups;
-        for (int64_t i = i0; i < total; i += stride) {
-            const int64_t gb = i / chunk, off = i - gb * chunk;
-            const float *src = part + gb * rk2 * chunk + off;
-            float s = src[0];
-            for (int r = 1; r < rk2; ++r) s += src[r * chunk];
-            dst[i] = s;
-        }
+    const int64_t total = j0.items + j1.items;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        if (i < j0.items)
+            reduce_item(j0, rk2, i);
+        else
+            reduce_item(j1, rk2, i - j0.items);
     }
 }
 
@@ -386,16 +396,25 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
     return hipGetLastError();
 }
 
-hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s)
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s)
 {
     const int rk2 = d.H / d.Hkv;
-    const int64_t chunk = (int64_t)D * d.M, groups = (int64_t)d.Hkv * d.B;
-    const int vec = (chunk % 4 == 0);
-    const int64_t work = vec ? chunk / 4 * groups : chunk * groups;
+    const int64_t groups = (int64_t)d.Hkv * d.B;
+    ReduceJob j[2];
+    const float *part[2] = {pk, pv};
+    float *dst[2] = {dk, dv};
+    const int D[2] = {d.DK, d.DV};
+    for (int t = 0; t < 2; ++t) {
+        j[t].part = part[t];
+        j[t].dst = dst[t];
+        j[t].chunk = (int64_t)D[t] * d.M;
+        j[t].vec = (j[t].chunk % 4 == 0);
+        j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;
+    }
+    const int64_t work = j[0].items + j[1].items;
     if (work == 0) return hipSuccess;
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);
-    hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid), dim3(256), 0, s, part, dst, chunk, rk2,
-                       groups, vec);
+    hipLaunchKernelGGL(gqa_reduce_kernel, dim3(grid), dim3(256), 0, s, j[0], j[1], rk2);
     return hipGetLastError();
 }
 

@@ -125,8 +125,9 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
                      const uint16_t *mask, const uint8_t *map, float scale, float *dq, float *part, int *ticket,
                      int Np, int Mp, const Dims &d, hipStream_t s);
 
-// dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] for one of dK / dV.
-hipError_t launch_gqa_reduce(const float *part, float *dst, int D, const Dims &d, hipStream_t s);
+// dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] (r in order) for dK
+// (pk -> dk) and dV (pv -> dv), one launch.
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s);
 
 // Fill n floats with zero.
 hipError_t launch_zero(float *p, int64_t n, hipStream_t s);
