@@ -195,6 +195,25 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Work-groups that meet on a shared result exchange partial results through
+// global memory with device-coherent accesses (write-through stores, loads that
+// bypass the non-coherent caches), so no cache-wide writeback or invalidate is
+// needed: a work-group's stores have completed (s_waitcnt vmcnt(0)) before it
+// takes the result's ticket, and the one that finds the others done reads them
+// after.
+__device__ __forceinline__ void coherent_store(float *p, float x)
+{
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ticket_take(int *t)
+{
+    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- reductions
 // Butterfly sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float x, int width)

@@ -88,24 +88,6 @@ __device__ __forceinline__ QShare query_share(int bid, int HB, int split)
     return r;
 }
 
-// The two shares of a block exchange their partial results through global
-// memory with device-coherent accesses (write-through stores, loads that bypass
-// the non-coherent caches), so no cache-wide writeback or invalidate is needed:
-// a share's stores have completed (s_waitcnt vmcnt(0)) before it takes the
-// block's ticket, and the share that finds the ticket taken reads them after.
-__device__ __forceinline__ void coherent_store(float *p, float x)
-{
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float *p)
-{
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ticket_take(int *t)
-{
-    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Streams the live key steps (block map) of one query block through the LDS
 // stages: the K and V tiles of later steps are copied from global memory straight
 // into LDS while body(step, class, K tile, V tile) works on the current one.  Each
