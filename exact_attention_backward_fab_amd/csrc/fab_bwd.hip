@@ -137,8 +137,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             lds_copy16(rv, kv_lds + 2 * ST::kQ + tt * ST::kO + cc * kChunkL,
                        (uint32_t)((key0 / 64 + tt) * DVP / 8 + cc) * kChunkG + (uint32_t)lane * 16u);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // published by the first barrier of the step loop
+        // not waited for here: the waits of the first step (and the map reads of the
+        // live list) cover these older copies, so their latency overlaps
     }
     // this lane's key row in the K and V tiles: tile kw / 2, row 32 (kw & 1) + l32
     const char *Krow = sKV + (kw >> 1) * ST::kQ + 512 * (kw & 1) + row_off;
@@ -268,6 +268,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __syncthreads();   // every wave is done with the stages before they are refilled
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the K/V copies, also with no live step
 
     // ---- sum the two query halves: waves 4-7 hand their accumulators to waves 0-3
     // through LDS, dK then dV (the stream ended with a barrier: the stage memory is free)
