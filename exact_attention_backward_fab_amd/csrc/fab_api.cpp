@@ -472,10 +472,13 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
                                                        pl.mp, pl.d, s),
                    "forward launch");
     } else if (bf16) {
-        FAB_TRY(launch_pack(pl, q, k, v, q16, k16, v16, mk, map, s));
-        FAB_LAUNCH(kPrep, fab::launch_prep_bf16(d, O, lse, o16, stats, blob, pl.dvp, pl.np, pl.nq, pl.off_k, pl.nk,
-                                                pl.off_v, pl.nv, pl.total, tick, ntick, pl.d, s),
-                   "prep launch");
+        // the bf16 tiles of Q, K, V (and the block map) with the dO tiles and LSE/D
+        // blocks of the supplied O and LSE: one launch
+        FAB_LAUNCH(kPack,
+                   fab::launch_pack_prep_bf16(q, k, v, q16, k16, v16, mk, map, d, O, lse, o16, stats, blob, pl.nq,
+                                              pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, tick, ntick, pl.np, pl.mp,
+                                              pl.d, s),
+                   "pack and prep launch");
     } else {
         // f32: dQ is accumulated by atomics into a zeroed slice
         const float *Ou = O;

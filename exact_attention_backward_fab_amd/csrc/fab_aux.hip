@@ -250,14 +250,37 @@ __global__ __launch_bounds__(256) void pack_qkv_kernel(PackJobs a)
     pack_tile<DVP>(a.j[2], bt, nullptr);
 }
 
-template <int DVP>
-__global__ __launch_bounds__(256) void prep_tiles_kernel(PackJob j, PrepExtra x)
+// The pack (Q, K, V, block map) and the prep of a supplied O and LSE (dO tiles,
+// LSE/D blocks, blob pads, counters) in one launch: work-groups [0, npack) pack,
+// the rest prep.
+template <int DKP, int DVP>
+__global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, int npack, PackJob j, PrepExtra x)
 {
-    pack_tile<DVP>(j, blockIdx.x, &x);
     for (int i = blockIdx.x * 256 + threadIdx.x; i < x.nzero; i += gridDim.x * 256) x.zero[i] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 4)
         for (int k = 0; k < 3; ++k)
             if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) x.blob[x.pad_lo[k] + threadIdx.x] = 0.f;
+    int bt = blockIdx.x;
+    if (bt >= npack) {
+        pack_tile<DVP>(j, bt - npack, &x);
+        return;
+    }
+    if (bt < a.map_groups) {
+        block_map_strip(a.mask, a.map, a.N, a.M, a.nqb, a.nkb, bt);
+        return;
+    }
+    bt -= a.map_groups;
+    if (bt < a.j[0].tiles) {
+        pack_tile<DKP>(a.j[0], bt, nullptr);
+        return;
+    }
+    bt -= a.j[0].tiles;
+    if (bt < a.j[1].tiles) {
+        pack_tile<DKP>(a.j[1], bt, nullptr);
+        return;
+    }
+    bt -= a.j[1].tiles;
+    pack_tile<DVP>(a.j[2], bt, nullptr);
 }
 
 namespace {
@@ -281,11 +304,10 @@ hipError_t run_pack(const PackJobs &a, hipStream_t s)
 }
 }  // namespace
 
-hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
-                           const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s)
+namespace {
+PackJobs pack_jobs(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+                   const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d)
 {
-    HeadDims hd;
-    if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
     PackJobs a = {};
     const int64_t qh = q ? (int64_t)d.H * d.B : 0, kh = (int64_t)d.Hkv * d.B;
     a.j[0] = rows_job(q, q16, qh, d.N, Np, d.DK);
@@ -296,12 +318,12 @@ hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf1
         a.nqb = (d.N + kMapTile - 1) / kMapTile; a.nkb = (d.M + kMapTile - 1) / kMapTile;
         a.map_groups = (int)map_groups(d.N, d.M);
     }
-    FAB_DISPATCH_HEAD_DIMS(run_pack, a, s, hd, true);
+    return a;
 }
 
-hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
-                            int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
-                            int64_t total, int *zero, int nzero, const Dims &d, hipStream_t s)
+void prep_job(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob, int Np,
+              int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero,
+              const Dims &d, PackJob *pj, PrepExtra *px)
 {
     PackJob j = {};
     j.src = dO; j.dst = dO16;
@@ -315,15 +337,49 @@ hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, _
     x.pad_lo[1] = off_k + nk; x.pad_hi[1] = off_v;
     x.pad_lo[2] = off_v + nv; x.pad_hi[2] = total;
     x.zero = zero; x.nzero = nzero;
-    if (j.tiles == 0) return hipSuccess;
-    switch (dvp) {
-    case 32: hipLaunchKernelGGL(prep_tiles_kernel<32>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
-    case 64: hipLaunchKernelGGL(prep_tiles_kernel<64>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
-    case 128: hipLaunchKernelGGL(prep_tiles_kernel<128>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
-    case 192: hipLaunchKernelGGL(prep_tiles_kernel<192>, dim3(j.tiles), dim3(256), 0, s, j, x); break;
-    default: return hipErrorInvalidValue;
-    }
+    *pj = j;
+    *px = x;
+}
+
+struct PackPrep {
+    PackJobs a;
+    int npack;
+    PackJob j;
+    PrepExtra x;
+};
+
+template <int DKP, int DVP, bool BF16>
+hipError_t run_pack_prep(const PackPrep &p, hipStream_t s)
+{
+    const int64_t grid = (int64_t)p.npack + p.j.tiles;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((pack_prep_kernel<DKP, DVP>), dim3((unsigned)grid), dim3(256), 0, s, p.a, p.npack, p.j, p.x);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+                           const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s)
+{
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
+    const PackJobs a = pack_jobs(q, k, v, q16, k16, v16, mask, map, Np, Mp, d);
+    FAB_DISPATCH_HEAD_DIMS(run_pack, a, s, hd, true);
+}
+
+hipError_t launch_pack_prep_bf16(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const float *dO, const float *O,
+                                 const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
+                                 int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
+                                 int Mp, const Dims &d, hipStream_t s)
+{
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
+    PackPrep p;
+    p.a = pack_jobs(q, k, v, q16, k16, v16, mask, map, Np, Mp, d);
+    p.npack = p.a.map_groups + p.a.j[0].tiles + p.a.j[1].tiles + p.a.j[2].tiles;
+    prep_job(dO, O, lse, dO16, stats, blob, Np, nq, off_k, nk, off_v, nv, total, zero, nzero, d, &p.j, &p.x);
+    FAB_DISPATCH_HEAD_DIMS(run_pack_prep, p, s, hd, true);
 }
 
 // ============================================================== GQA reduce

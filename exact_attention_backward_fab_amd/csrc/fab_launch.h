@@ -60,7 +60,7 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
                                const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s);
 // The backward's own forward in bf16 mode: instead of O and the LSE it writes
-// what the backward kernels read, as launch_pack_qkv (Q) and launch_prep_bf16 do
+// what the backward kernels read, as launch_pack_prep_bf16 does
 // from a stored O and LSE: the bf16 tiles of Q and dO, the LSE/D blocks, the blob
 // pads (nq, off_k, nk, off_v, nv, total as there) and nzero zeroed ints.
 hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
@@ -74,12 +74,16 @@ hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __b
 hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blob, int64_t off_k, int64_t nk,
                        int64_t off_v, int64_t nv, int64_t total, const Dims &d, hipStream_t s);
 
-// bf16 mode prep: D and the LSE/D blocks (stats, [B][H][Np/64][128]) from d, O and
-// lse, d as bf16 tiles [B][H][Np][dvp] (fab_tiles.h, zero-padded), and the pads
-// of the result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)).
-hipError_t launch_prep_bf16(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob,
-                            int dvp, int Np, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv,
-                            int64_t total, int *zero, int nzero, const Dims &d, hipStream_t s);
+// bf16 mode with O and LSE supplied: launch_pack_qkv's work and the prep, in one
+// launch: D and the LSE/D blocks (stats, [B][H][Np/64][128]) from d, O and lse,
+// d as bf16 tiles [B][H][Np][DVP] (fab_tiles.h, zero-padded), the pads of the
+// result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)) and
+// nzero ints of zero written.
+hipError_t launch_pack_prep_bf16(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const float *dO, const float *O,
+                                 const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
+                                 int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
+                                 int Mp, const Dims &d, hipStream_t s);
 
 // Rows of the bf16 tiles are padded per head to a multiple of this.
 constexpr int kPackRows = 64;
@@ -100,7 +104,7 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
                                hipStream_t s);
 
 // Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
-// (launch_pack_qkv / launch_prep_bf16, Np rows per head), K, V (Mp rows per head)
+// (launch_pack_prep_bf16 or the forward of launch_forward_prep_bf16, Np rows per head), K, V (Mp rows per head)
 // and the LSE/D blocks; stored as in launch_backward_f32.
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
@@ -120,7 +124,7 @@ inline int64_t dq_part_floats(const Dims &d, int dkp) { return dq_split_blocks(d
 
 // Query-block-outer dQ (bf16 mode): dq [DK,N,H,B] = scale dS K, every element
 // written once; inputs as for launch_backward_bf16.  part and ticket as sized
-// above (ticket zeroed by launch_prep_bf16), used when dq_split(d) == 2.
+// above (ticket zeroed by the launch that writes the tiles), used when dq_split(d) == 2.
 hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16, const __bf16 *v16,
                      const uint16_t *mask, const uint8_t *map, float scale, float *dq, float *part, int *ticket,
                      int Np, int Mp, const Dims &d, hipStream_t s);

@@ -133,10 +133,11 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
 /* Measurement hooks (they compute nothing).  While enabled, every kernel
  * launch made by fab_forward_lse and fab_backward is bracketed by a pair of
  * HIP events recorded on the caller's stream.  fab_profile_read waits for the
- * recorded events of one kernel -- "block_map" (f32 mode), "forward", "prep",
- * "pack" (bf16 copies of k and v, of q when O and lse are supplied, and in bf16
- * mode the block map of the mask), "backward" (dK, dV; f32 mode also dQ), "dq"
- * (bf16 mode's dQ) or "gqa_reduce" -- and returns their summed duration in milliseconds and the
+ * recorded events of one kernel -- "block_map" (f32 mode), "forward", "prep"
+ * (f32 mode), "pack" (bf16 copies of k and v, the block map of the mask, and with
+ * O and lse supplied also of q and the prep of d), "backward" (dK, dV; f32 mode
+ * also dQ), "dq" (bf16 mode's dQ) or "gqa_reduce" -- and returns their summed
+ * duration in milliseconds and the
  * number of launches since the last fab_profile_reset.  The events are created
  * by the library on first use and kept for reuse; only one thread should use
  * the hooks at a time.  Returns FAB_OK, FAB_E_INVAL (unknown kernel name or
