@@ -21,7 +21,8 @@ usual training convention) and the forward alone, and (`other_workloads`,
 --also) the whole step and the backward alone of further workloads, by
 default the long-context one.  Causal workloads are also timed with the causal
 rule passed as a flag instead of the mask tensor (`causal_flag_instead_of_mask`:
-same result, no block map or mask reads).  `cpu_baseline` times the
+same result, no block map or mask reads), and bf16 mode with q, k, v, d stored
+as bf16 (`bf16_inputs`: the values the matrix cores read).  `cpu_baseline` times the
 f64 CPU oracle on a bounded sample of the same workload on this host's cores.
 
 Prints exactly one JSON line.
@@ -340,6 +341,17 @@ def main():
                      "frac_of_peak": round((F_f + F_b) / (ms_c * 1e-3) / 1e12 / peak, 4)}
         del ws_c
 
+    # ---- the same step with q, k, v, d stored as bf16 (bf16 mode: the values the
+    # matrix cores read; the f32 inputs rounded once beforehand, outside the timing)
+    bf16_in = None
+    if mode == "bf16":
+        tb = [x.to(torch.bfloat16) for x in (tq, tk, tv, td)]
+        ms_b = time_loop(torch, lambda: fab.backward(*tb, scale, mask=tm, mode=mode, blob=blob, ws=ws_full),
+                         args.steps, args.warmup, stream, args.min_warm_s)
+        bf16_in = {"ms_per_step": round(ms_b, 4), "value": round((F_f + F_b) / (ms_b * 1e-3) / 1e12, 3),
+                   "frac_of_peak": round((F_f + F_b) / (ms_b * 1e-3) / 1e12 / peak, 4)}
+        del tb
+
     # ---- other workloads (e.g. the long-context one), same protocol, same mode
     also = {}
     for wid in [int(x) for x in args.also.split(",") if x.strip()]:
@@ -378,6 +390,8 @@ def main():
         del t2, tm2, blob2, ws2, ws2b, O2, lse2
     if mask_free:
         out["causal_flag_instead_of_mask"] = mask_free
+    if bf16_in:
+        out["bf16_inputs"] = bf16_in
     if also:
         out["other_workloads"] = also
     if not args.no_cpu_baseline:

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libfab.so")
 FAB_MODE_F32 = 0
 FAB_MODE_BF16 = 1
 FAB_CAUSAL = 0x100   # flag: the causal rule (key m seen by query n iff m <= n) without a mask
+FAB_BF16_INPUTS = 0x200   # flag: q, k, v, d are bf16 (bf16 mode only)
 MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
          FAB_MODE_BF16: FAB_MODE_BF16}
 
@@ -121,8 +122,8 @@ def blob_layout(shape: Shape):
     return tuple(x.value for x in o)
 
 
-def _mode(mode, causal):
-    return MODES[mode] | (FAB_CAUSAL if causal else 0)
+def _mode(mode, causal, bf16_inputs=False):
+    return MODES[mode] | (FAB_CAUSAL if causal else 0) | (FAB_BF16_INPUTS if bf16_inputs else 0)
 
 
 def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False, causal=False) -> int:
@@ -153,10 +154,21 @@ def _mask_arg(mask):
     return mask
 
 
-def _check_tensor(t, name, shape, device):
+def _input_dtype(*ts):
+    """float32 or bfloat16, the same for every input tensor."""
     import torch
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    dt = ts[0].dtype
+    if dt not in (torch.float32, torch.bfloat16) or any(t.dtype != dt for t in ts):
+        raise TypeError("q, k, v (and d) must all be float32 or all bfloat16, got "
+                        + ", ".join(str(t.dtype) for t in ts))
+    return dt
+
+
+def _check_tensor(t, name, shape, device, dtypes=None):
+    import torch
+    dtypes = dtypes or (torch.float32,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
@@ -174,13 +186,15 @@ def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device, causal=Fal
 
 def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False):
     """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v.
-    causal=True applies the causal rule without a mask (mask must be None)."""
+    causal=True applies the causal rule without a mask (mask must be None).  q, k, v
+    are float32, or bfloat16 (all three; mode "bf16")."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
-    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev)
-    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev)
-    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev)
+    bf16_in = _input_dtype(q, k, v) == torch.bfloat16
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev, (q.dtype,))
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev, (q.dtype,))
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev, (q.dtype,))
     mask = _mask_arg(mask)
     if O is None:
         O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
@@ -191,7 +205,7 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     else:
         nbytes = ws.numel() * ws.element_size()
     _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
-                                 float(scale), _mode(mode, causal), _ptr(O), _ptr(lse), _ptr(ws), nbytes,
+                                 float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(ws), nbytes,
                                  _stream_handle(stream)))
     return O, lse
 
@@ -199,14 +213,16 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
 def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=None, ws=None,
              stream=None, causal=False):
     """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
-    causal=True applies the causal rule without a mask (mask must be None)."""
+    causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
+    are float32, or bfloat16 (all four; mode "bf16")."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
-    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev)
-    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev)
-    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev)
-    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), dev)
+    bf16_in = _input_dtype(q, k, v, d) == torch.bfloat16
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev, (q.dtype,))
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev, (q.dtype,))
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev, (q.dtype,))
+    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), dev, (q.dtype,))
     mask = _mask_arg(mask)
     total = blob_layout(s)[3]
     if blob is None:
@@ -216,7 +232,7 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
     else:
         nbytes = ws.numel() * ws.element_size()
     _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                              float(scale), _mode(mode, causal), _ptr(O), _ptr(lse), _ptr(blob),
+                              float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
                               _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 

@@ -161,12 +161,17 @@ int check_mode(int mode)
     return FAB_OK;
 }
 
-// Splits the FAB_CAUSAL flag off the mode argument and checks the rest.
-int take_mode(int *mode, bool *causal)
+// Splits the FAB_CAUSAL and FAB_BF16_INPUTS flags off the mode argument and
+// checks the rest.
+int take_mode(int *mode, bool *causal, bool *in_bf16)
 {
     *causal = (*mode & FAB_CAUSAL) != 0;
-    *mode &= ~FAB_CAUSAL;
-    return check_mode(*mode);
+    *in_bf16 = (*mode & FAB_BF16_INPUTS) != 0;
+    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS);
+    const int rc = check_mode(*mode);
+    if (rc != FAB_OK) return rc;
+    if (*in_bf16 && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS needs FAB_MODE_BF16");
+    return FAB_OK;
 }
 
 int check_ptr(const void *p, int64_t elems, const char *name)
@@ -259,7 +264,7 @@ struct ProfScope {
 
 // The bf16 tiles of Q (when q16 is given), K and V (bf16 mode), one launch.
 // (and the block map of the mask when map is given: the same launch)
-int launch_pack(const Plan &pl, const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
+int launch_pack(const Plan &pl, const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16,
                 __bf16 *v16, const uint16_t *mask, uint8_t *map, hipStream_t s)
 {
     FAB_LAUNCH(kPack,
@@ -268,7 +273,7 @@ int launch_pack(const Plan &pl, const float *q, const float *k, const float *v, 
     return FAB_OK;
 }
 
-int launch_fwd(const Plan &pl, int bf16, const float *q, const float *k, const float *v, const __bf16 *k16,
+int launch_fwd(const Plan &pl, int bf16, const void *q, const void *k, const void *v, const __bf16 *k16,
                const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *O, float *lse,
                hipStream_t s)
 {
@@ -276,7 +281,10 @@ int launch_fwd(const Plan &pl, int bf16, const float *q, const float *k, const f
         FAB_LAUNCH(kFwd, fab::launch_forward_bf16(q, k16, v16, mask, map, scale, O, lse, pl.mp, pl.d, s),
                    "forward launch");
     else
-        FAB_LAUNCH(kFwd, fab::launch_forward_f32(q, k, v, mask, map, scale, O, lse, pl.d, s), "forward launch");
+        FAB_LAUNCH(kFwd,
+                   fab::launch_forward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                           static_cast<const float *>(v), mask, map, scale, O, lse, pl.d, s),
+                   "forward launch");
     return FAB_OK;
 }
 
@@ -363,8 +371,8 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal;
-    FAB_TRY(take_mode(&mode, &causal));
+    bool causal, in_bf16;
+    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
     if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
     if (causal && has_mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     plan_workspace(&pl, mode, has_mask != 0, have_o_lse != 0);
@@ -372,17 +380,18 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     return FAB_OK;
 }
 
-int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, const float *v,
+int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
                     const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
                     size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal;
-    FAB_TRY(take_mode(&mode, &causal));
+    bool causal, in_bf16;
+    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     pl.d.causal = causal;
+    pl.d.in_bf16 = in_bf16;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     FAB_TRY(check_ptr(q, pl.nq, "q"));
     FAB_TRY(check_ptr(k, pl.nk, "k"));
@@ -410,17 +419,18 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
     return FAB_OK;
 }
 
-int fab_backward(const fab_shape *shape, const float *q, const float *k, const float *v,
-                 const uint16_t *mask, const float *d, float scale, int mode, const float *O,
+int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
+                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal;
-    FAB_TRY(take_mode(&mode, &causal));
+    bool causal, in_bf16;
+    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     pl.d.causal = causal;
+    pl.d.in_bf16 = in_bf16;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     if ((O == nullptr) != (lse == nullptr))
         return fail(FAB_E_INVAL, "O and lse must be given together or both be NULL");
@@ -489,7 +499,8 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
             Ou = Ow;
             lseu = lw;
         }
-        FAB_LAUNCH(kPrep, fab::launch_prep(d, Ou, delta, blob, pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, pl.d, s),
+        FAB_LAUNCH(kPrep, fab::launch_prep(static_cast<const float *>(d), Ou, delta, blob, pl.off_k, pl.nk, pl.off_v,
+                                           pl.nv, pl.total, pl.d, s),
                    "prep launch");
     }
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
@@ -502,7 +513,9 @@ int fab_backward(const fab_shape *shape, const float *q, const float *k, const f
                                                  pl.d, s),
                    "dQ launch");
     } else {
-        FAB_LAUNCH(kBwd, fab::launch_backward_f32(q, k, v, d, mk, map, lseu, delta, scale, blob, dk, dv,
+        FAB_LAUNCH(kBwd, fab::launch_backward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                                  static_cast<const float *>(v), static_cast<const float *>(d), mk,
+                                                  map, lseu, delta, scale, blob, dk, dv,
                                                   pl.gqa ? 1 : 0, pl.d, s),
                    "backward launch");
     }

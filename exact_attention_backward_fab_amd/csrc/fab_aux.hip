@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 // One packing job: heads of M rows of D floats -> bf16 tiles [heads][Mp][DP].  Row
 // m of head hd = hh + H*bb starts at src + hh*sh + bb*sb + m*rs floats.
 struct PackJob {
-    const float *src;
+    const void *src;                  // f32 rows, or bf16 rows when src_bf16
+    int src_bf16;
     __bf16 *dst;
     int64_t sh, sb, rs;
     int H, M, Mp, D, vec;
@@ -178,8 +179,8 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
     const int ntile = j.Mp / 64;
     const int hd = bt / ntile, t = bt - hd * ntile;
     const int hh = hd % j.H, bb = hd / j.H;
-    const float *base = j.src + hh * j.sh + bb * j.sb;
-    const float *obase = x ? x->O + hh * j.sh + bb * j.sb : nullptr;
+    const int64_t head_off = hh * j.sh + bb * j.sb;
+    const float *obase = x ? x->O + head_off : nullptr;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     // all loads of the tile first (independent, so they are in flight together)
     f32x4 xv[IT], yv[IT];
@@ -189,7 +190,7 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
         const int r = idx / C4, col = 4 * (idx - r * C4);
         const int m = t * 64 + r;
         const bool ok = idx < 64 * C4 && m < j.M;
-        xv[i] = ok ? load_row4(base + m * j.rs, col, j.D, j.vec) : z;
+        xv[i] = ok ? load_row4_any(j.src, head_off + m * j.rs, col, j.D, j.vec, j.src_bf16) : z;
         yv[i] = (ok && obase) ? load_row4(obase + m * j.rs, col, j.D, j.vec) : z;
     }
 #pragma unroll
@@ -284,10 +285,10 @@ __global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, int npack, P
 }
 
 namespace {
-PackJob rows_job(const float *src, __bf16 *dst, int64_t heads, int M, int Mp, int D)
+PackJob rows_job(const void *src, int src_bf16, __bf16 *dst, int64_t heads, int M, int Mp, int D)
 {
     PackJob j = {};
-    j.src = src; j.dst = dst;
+    j.src = src; j.src_bf16 = src_bf16; j.dst = dst;
     j.H = 1; j.sh = 0; j.sb = (int64_t)M * D; j.rs = D;   // heads are consecutive blocks of M rows
     j.M = M; j.Mp = Mp; j.D = D; j.vec = (D % 4 == 0);
     j.tiles = (int)(heads * (Mp / 64));
@@ -305,14 +306,14 @@ hipError_t run_pack(const PackJobs &a, hipStream_t s)
 }  // namespace
 
 namespace {
-PackJobs pack_jobs(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+PackJobs pack_jobs(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
                    const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d)
 {
     PackJobs a = {};
     const int64_t qh = q ? (int64_t)d.H * d.B : 0, kh = (int64_t)d.Hkv * d.B;
-    a.j[0] = rows_job(q, q16, qh, d.N, Np, d.DK);
-    a.j[1] = rows_job(k, k16, kh, d.M, Mp, d.DK);
-    a.j[2] = rows_job(v, v16, kh, d.M, Mp, d.DV);
+    a.j[0] = rows_job(q, d.in_bf16, q16, qh, d.N, Np, d.DK);
+    a.j[1] = rows_job(k, d.in_bf16, k16, kh, d.M, Mp, d.DK);
+    a.j[2] = rows_job(v, d.in_bf16, v16, kh, d.M, Mp, d.DV);
     if (map) {
         a.mask = mask; a.map = map; a.N = d.N; a.M = d.M;
         a.nqb = (d.N + kMapTile - 1) / kMapTile; a.nkb = (d.M + kMapTile - 1) / kMapTile;
@@ -321,12 +322,12 @@ PackJobs pack_jobs(const float *q, const float *k, const float *v, __bf16 *q16, 
     return a;
 }
 
-void prep_job(const float *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob, int Np,
+void prep_job(const void *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob, int Np,
               int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero,
               const Dims &d, PackJob *pj, PrepExtra *px)
 {
     PackJob j = {};
-    j.src = dO; j.dst = dO16;
+    j.src = dO; j.src_bf16 = d.in_bf16; j.dst = dO16;
     // d, O [DV,H,N,B]: row n of head (h, b) at DV*(h + H*(n + N*b))
     j.H = d.H; j.sh = d.DV; j.sb = (int64_t)d.DV * d.H * d.N; j.rs = (int64_t)d.DV * d.H;
     j.M = d.N; j.Mp = Np; j.D = d.DV; j.vec = (d.DV % 4 == 0);
@@ -358,7 +359,7 @@ hipError_t run_pack_prep(const PackPrep &p, hipStream_t s)
 }
 }  // namespace
 
-hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
                            const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s)
 {
     HeadDims hd;
@@ -367,8 +368,8 @@ hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf1
     FAB_DISPATCH_HEAD_DIMS(run_pack, a, s, hd, true);
 }
 
-hipError_t launch_pack_prep_bf16(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
-                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const float *dO, const float *O,
+hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const float *O,
                                  const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
                                  int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
                                  int Mp, const Dims &d, hipStream_t s)

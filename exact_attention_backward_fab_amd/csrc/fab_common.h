@@ -189,6 +189,32 @@ __device__ __forceinline__ f32x4 load_row4(const float *row, int c, int D, bool 
     return r;
 }
 
+// The same from a row of bf16 values (widened to f32, exactly); vec: D % 4 == 0
+// (8-byte loads).
+__device__ __forceinline__ f32x4 load_row4(const __bf16 *row, int c, int D, bool vec)
+{
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    if (c >= D) return r;
+    if (vec) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4 *>(row + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = (float)x[i];
+        return r;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (c + i < D) r[i] = (float)row[c + i];
+    return r;
+}
+
+// Row m of a tensor of f32 (bf16 == 0) or bf16 (bf16 != 0) elements, elem_off
+// elements past base: four entries from column c.
+__device__ __forceinline__ f32x4 load_row4_any(const void *base, int64_t elem_off, int c, int D, bool vec, int bf16)
+{
+    if (bf16) return load_row4(static_cast<const __bf16 *>(base) + elem_off, c, D, vec);
+    return load_row4(static_cast<const float *>(base) + elem_off, c, D, vec);
+}
+
 // Additive f16 mask value (as f32) from its bit pattern.
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {

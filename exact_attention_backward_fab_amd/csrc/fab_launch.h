@@ -11,6 +11,7 @@ namespace fab {
 struct Dims {
     int B, H, Hkv, N, M, DK, DV;
     int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
+    int in_bf16 = 0;  // q, k, v and d are bf16 (bf16 mode only); otherwise f32
 };
 
 // Padded head dimensions (DKP, DVP) the kernels are instantiated for; a shape
@@ -56,15 +57,15 @@ hipError_t launch_block_map(const uint16_t *mask, uint8_t *map, const Dims &d, h
 hipError_t launch_forward_f32(const float *q, const float *k, const float *v, const uint16_t *mask,
                               const uint8_t *map, float scale, float *O, float *lse, const Dims &d,
                               hipStream_t s);
-hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
                                const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s);
 // The backward's own forward in bf16 mode: instead of O and the LSE it writes
 // what the backward kernels read, as launch_pack_prep_bf16 does
 // from a stored O and LSE: the bf16 tiles of Q and dO, the LSE/D blocks, the blob
 // pads (nq, off_k, nk, off_v, nv, total as there) and nzero zeroed ints.
-hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
-                                    const uint8_t *map, float scale, const float *dO, __bf16 *q16, __bf16 *o16,
+hipError_t launch_forward_prep_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+                                    const uint8_t *map, float scale, const void *dO, __bf16 *q16, __bf16 *o16,
                                     float *stats, float *blob, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v,
                                     int64_t nv, int64_t total, int *zero, int nzero, int Np, int Mp, const Dims &d,
                                     hipStream_t s);
@@ -79,8 +80,8 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
 // d as bf16 tiles [B][H][Np][DVP] (fab_tiles.h, zero-padded), the pads of the
 // result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)) and
 // nzero ints of zero written.
-hipError_t launch_pack_prep_bf16(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16,
-                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const float *dO, const float *O,
+hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const float *O,
                                  const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
                                  int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
                                  int Mp, const Dims &d, hipStream_t s);
@@ -92,7 +93,7 @@ constexpr int kPackRows = 64;
 // (skipped when q is NULL), k / v -> k16 / v16 [B,Hkv,Mp,DKP / DVP]; rows past the
 // data and columns past DK / DV zero.  With map, the same launch also builds the
 // mask's block map (as launch_block_map).
-hipError_t launch_pack_qkv(const float *q, const float *k, const float *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
+hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
                            const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s);
 
 // Key-block-outer backward, f32 mode: dV, dK per key tile (stored into dk/dv with

@@ -143,13 +143,14 @@ __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const cha
 // Per-lane query operands: B operands of S^T = K Q^T (Q rows, f32 -> bf16) for
 // query row `row` (all zero when !ok).
 template <int DKP>
-__device__ __forceinline__ void load_q_operand(bf16x8 *qf, const float *qr, bool ok, int DK, int vecK, int half)
+__device__ __forceinline__ void load_q_operand(bf16x8 *qf, const void *q, int64_t row_off, bool ok, int DK, int vecK,
+                                               int half, int in_bf16)
 {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DKP / 16; ++t) {
-        const f32x4 lo = ok ? load_row4(qr, 16 * t + 8 * half, DK, vecK) : z;
-        const f32x4 hi = ok ? load_row4(qr, 16 * t + 8 * half + 4, DK, vecK) : z;
+        const f32x4 lo = ok ? load_row4_any(q, row_off, 16 * t + 8 * half, DK, vecK, in_bf16) : z;
+        const f32x4 hi = ok ? load_row4_any(q, row_off, 16 * t + 8 * half + 4, DK, vecK, in_bf16) : z;
         qf[t] = __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
@@ -209,7 +210,8 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
 
 // ============================================================== forward
 struct FwdArgs16 {
-    const float *q;
+    const void *q;                  // f32, or bf16 when in_bf16 (as dO)
+    int in_bf16;
     const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
@@ -221,7 +223,7 @@ struct FwdArgs16 {
     // backward kernels read: the bf16 tiles of Q and dO (rows >= N and columns
     // >= DK / DV zero), the LSE/D blocks (D = rowsum(dO o O)), and it zeroes the
     // blob pads (work-group 0) and the dQ split counters.
-    const float *dO;                // [DV,H,N,B]
+    const void *dO;                 // [DV,H,N,B]
     __bf16 *q16, *o16;              // tiles [B,H,Np,DKP] / [B,H,Np,DVP]
     float *stats;                   // [B,H,Np/64][128]
     float *blob;
@@ -255,7 +257,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const rsrc_t rv = make_rsrc(p.v16 + kvrow * DVP, (uint32_t)(p.Mp * DVP) * 2u);
 
     bf16x8 qf[DKP / 16];
-    load_q_operand<DKP>(qf, p.q + (hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half);
+    load_q_operand<DKP>(qf, p.q, (int64_t)(hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half, p.in_bf16);
     const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // PREP: first tile row of this head
     if constexpr (PREP) {
         if (myq < p.Np) {
@@ -354,7 +356,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
         // D = rowsum(dO o O) with O = Õ / l in f32, the bf16 dO row into its tile, and
         // the row's LSE (log2 units; +inf = no weight: all-masked or past N) and D
         if (myq >= p.Np) return;
-        const float *drow = p.dO + (size_t)p.DV * (h + p.H * (min(myq, p.N - 1) + (size_t)p.N * b));
+        const int64_t drow = (int64_t)p.DV * (h + p.H * (min(myq, p.N - 1) + (int64_t)p.N * b));
         __bf16 *ot16 = p.o16 + qhead * DVP;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         float dsum = 0.f;
@@ -363,7 +365,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int c0 = dt * 32 + 8 * r4 + 4 * half;
-                const f32x4 dv = qok ? load_row4(drow, c0, p.DV, p.vecV) : z;
+                const f32x4 dv = qok ? load_row4_any(p.dO, drow, c0, p.DV, p.vecV, p.in_bf16) : z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dsum += dv[i] * (oacc[dt][4 * r4 + i] * inv);
                 *reinterpret_cast<bf16x4 *>(ot16 + tile_elem(myq, c0, DVP)) = to_bf16x4(dv);
@@ -598,7 +600,7 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
 }
 }  // namespace
 
-hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
                                const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s)
 {
@@ -608,13 +610,13 @@ hipError_t launch_forward_bf16(const float *q, const __bf16 *k16, const __bf16 *
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
-    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
+    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
 }
 
-hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
-                                    const uint8_t *map, float scale, const float *dO, __bf16 *q16, __bf16 *o16,
+hipError_t launch_forward_prep_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
+                                    const uint8_t *map, float scale, const void *dO, __bf16 *q16, __bf16 *o16,
                                     float *stats, float *blob, int64_t nq, int64_t off_k, int64_t nk, int64_t off_v,
                                     int64_t nv, int64_t total, int *zero, int nzero, int Np, int Mp, const Dims &d,
                                     hipStream_t s)
@@ -625,7 +627,7 @@ hipError_t launch_forward_prep_bf16(const float *q, const __bf16 *k16, const __b
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
-    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
+    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
     a.scale = scale;
     a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
     a.pad_lo[0] = nq; a.pad_hi[0] = off_k;

@@ -79,6 +79,14 @@ typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
  * (has_mask = 0), else FAB_E_INVAL; no block map is built and no mask is read. */
 #define FAB_CAUSAL 0x100
 
+/* Flag OR-ed into the mode argument: q, k, v and d are bf16 (16-bit bit
+ * patterns, the same layouts) instead of f32 -- the storage the bf16 matrix
+ * cores read anyway, so the values are those FAB_MODE_BF16 would round f32
+ * inputs to, and the results equal those for the f32 inputs holding the same
+ * values.  FAB_MODE_BF16 only (FAB_E_INVAL otherwise); O, lse and the blob stay
+ * f32. */
+#define FAB_BF16_INPUTS 0x200
+
 typedef enum fab_status {
     FAB_OK = 0,
     FAB_E_INVAL = -1,        /* bad shape, NULL pointer, bad scale or mode */
@@ -102,23 +110,25 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
 
 /* Forward with row log-sum-exp (labml "Flash Attention": "Forward pass" and the
  * running max/sum of "Flash Attention Optimization").
- *   q, k, v   device, f32, layouts above (read only)
+ *   q, k, v   device, f32 (bf16 with FAB_BF16_INPUTS), layouts above (read only)
  *   mask      device f16 bits [M,N] or NULL for no mask (read only)
  *   scale     finite f32 softmax scale
  *   mode      fab_mode, optionally | FAB_CAUSAL (then mask must be NULL)
+ *             | FAB_BF16_INPUTS (FAB_MODE_BF16 only)
  *   O         device f32 [DV,H,N,B] (written): softmax(scale*q.k + mask) v
  *   lse       device f32 [N,H,B] (written): natural-log log-sum-exp of the row's
  *             scores, -inf for an all-masked row
  *   ws        device workspace of ws_bytes >= fab_workspace_bytes(.., have_o_lse=1)
  *   stream    hipStream_t of the caller (NULL = default stream) */
-int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, const float *v,
+int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
                     const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
                     size_t ws_bytes, void *stream);
 
 /* The attention backward ("Function ggml_flash_attn_back"; ggmlR
  * `fab_grads`): gradients of sum(d * attn(q,k,v)) packed into blob.
  *   q, k, v, mask, scale, mode  as for fab_forward_lse
- *   d         device f32 [DV,H,N,B]: upstream gradient of the attention output
+ *   d         device f32 (bf16 with FAB_BF16_INPUTS) [DV,H,N,B]: upstream gradient
+ *             of the attention output
  *   O, lse    either both NULL (the forward is recomputed internally, the
  *             pages' semantics) or both given: the output and row LSE of the
  *             same forward (as written by fab_forward_lse); exactly one NULL
@@ -126,8 +136,8 @@ int fab_forward_lse(const fab_shape *shape, const float *q, const float *k, cons
  *   blob      device f32, total_floats of fab_blob_layout (written in full)
  *   ws        device workspace, ws_bytes >= fab_workspace_bytes(.., have_o_lse)
  *   stream    hipStream_t of the caller */
-int fab_backward(const fab_shape *shape, const float *q, const float *k, const float *v,
-                 const uint16_t *mask, const float *d, float scale, int mode, const float *O,
+int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
+                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
 
 /* Measurement hooks (they compute nothing).  While enabled, every kernel

@@ -95,7 +95,8 @@ GOOD = (1, 4, 2, 8, 8, 16, 16)
     (GOOD, {"ws": None}, fab.FAB_E_WORKSPACE),
     (GOOD, {"ws_bytes": 16}, fab.FAB_E_WORKSPACE),
     (GOOD, {"mode": fab.FAB_CAUSAL, "mask": FAKE}, fab.FAB_E_INVAL),         # mask and causal flag
-    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x200}, fab.FAB_E_INVAL),           # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x400}, fab.FAB_E_INVAL),           # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_BF16_INPUTS}, fab.FAB_E_INVAL),  # bf16 inputs need bf16 mode
 ])
 def test_backward_rejects_bad_arguments_before_device_work(shape, kw, code):
     assert call_bwd(shape, **kw) == code

@@ -278,6 +278,46 @@ def test_causal_flag_equals_causal_mask(torch_dev, name, s, seed, mode):
     assert rel_err(O.cpu().numpy(), O_ref) <= TOL[mode]
 
 
+BF16_IN = [
+    ("gqa_causal", Shape(1, 4, 2, 333, 333, 128, 128), "causal", 61),
+    ("random_mask", Shape(2, 2, 1, 150, 170, 64, 64), "random", 62),
+    ("d192_padding", Shape(1, 2, 2, 130, 260, 192, 128), "padding", 63),
+    ("odd_dims", Shape(1, 3, 1, 70, 90, 40, 72), None, 64),
+]
+
+
+@pytest.mark.parametrize("supplied", [False, True], ids=["own_forward", "o_lse_supplied"])
+@pytest.mark.parametrize("name,s,mkind,seed", BF16_IN, ids=[c[0] for c in BF16_IN])
+def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mkind, seed, supplied):
+    # FAB_BF16_INPUTS: q, k, v, d stored as bf16 give bit for bit the result of the
+    # f32 inputs holding the same (bf16) values -- the values bf16 mode rounds to
+    # anyway -- and that result matches the oracle on those values
+    torch, dev = torch_dev
+    fab = fabmod()
+    print(f"[parity] bf16 inputs {name} supplied={supplied} {s}", flush=True)
+    q, k, v, d = make_qkvd(s, seed)
+    mask = small_mask(mkind, s, seed)
+    tm = to_dev(torch, dev, mask)
+    scale = float(np.float32(1.0 / math.sqrt(s.DK)))
+    t16 = [to_dev(torch, dev, x).to(torch.bfloat16) for x in (q, k, v, d)]
+    t32 = [x.float() for x in t16]
+    outs = []
+    for t in (t16, t32):
+        O = lse = None
+        if supplied:
+            O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode="bf16")
+        outs.append(fab.backward(*t, scale, mask=tm, mode="bf16", O=O, lse=lse))
+        if supplied:
+            outs.append(torch.cat([O.flatten(), lse.flatten()]))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[:len(outs) // 2], outs[len(outs) // 2:]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    qr, kr, vr, dr = (x.cpu().numpy() for x in t32)
+    ref = oracle_full(s, qr, kr, vr, dr, mask, scale)
+    total = fab.blob_layout(fab.Shape(*s.astuple()))[3]
+    check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"bf16 inputs {name}", mask=mask)
+
+
 def test_d_ones_closed_form_on_gpu(torch_dev):
     # d = ones: every component of dV[:, m] equals the summed attention weight of key m
     torch, dev = torch_dev
