@@ -318,6 +318,62 @@ def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mki
     check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"bf16 inputs {name}", mask=mask)
 
 
+def test_caller_stream_is_used(torch_dev):
+    # every launch goes to the stream the caller passes: the same call on a side
+    # stream (inputs written there, nothing synchronised in between) gives the same blob
+    torch, dev = torch_dev
+    fab = fabmod()
+    s = Shape(1, 4, 2, 300, 300, 64, 64)
+    q, k, v, d = make_qkvd(s, 71)
+    mask = to_dev(torch, dev, causal_mask(s.N, s.M))
+    ref = fab.backward(*[to_dev(torch, dev, x) for x in (q, k, v, d)], 0.125, mask=mask, mode="bf16")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        t = [torch.from_numpy(x).to(dev, non_blocking=False) for x in (q, k, v, d)]
+        out = fab.backward(*t, 0.125, mask=mask, mode="bf16", stream=side)
+    side.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("mode", ["bf16", "f32"])
+def test_graph_capture_replays(torch_dev, mode):
+    # fab_backward captured into a graph (no memset nodes: every zeroing is a
+    # kernel) and replayed three times with eager work and synchronisation in
+    # between; every replay matches the eager result (bf16 mode bit for bit, f32
+    # mode up to the order of its dQ atomics)
+    torch, dev = torch_dev
+    fab = fabmod()
+    s = Shape(1, 4, 2, 257, 300, 64, 64)
+    q, k, v, d = make_qkvd(s, 72)
+    mask = to_dev(torch, dev, random_mask(s.N, s.M, 72, p_inf=0.3, full_rows=1, full_cols=1))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    fs = fab.Shape(*s.astuple())
+    ws, _ = fab.alloc_workspace(fs, mode, True, False, dev)
+    blob = torch.empty(fab.blob_layout(fs)[3], device=dev)
+    eager = fab.backward(*t, 0.125, mask=mask, mode=mode, ws=ws).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            fab.backward(*t, 0.125, mask=mask, mode=mode, blob=blob, ws=ws, stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        blob.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if mode == "bf16":
+            assert torch.equal(blob.view(torch.int32), eager.view(torch.int32)), rep
+        else:
+            assert torch.allclose(blob, eager, rtol=1e-5, atol=1e-6 * float(eager.abs().max())), rep
+        # eager work between replays
+        _ = fab.backward(*t, 0.125, mask=mask, mode=mode)
+        torch.cuda.synchronize()
+
+
 def test_d_ones_closed_form_on_gpu(torch_dev):
     # d = ones: every component of dV[:, m] equals the summed attention weight of key m
     torch, dev = torch_dev
