@@ -2,14 +2,17 @@
 //   block_map_kernel   one byte per 32x32 (query x key) block of the additive
 //                      f16 mask: SKIP (all -inf), FREE (all zero) or MIXED, plus
 //                      a bit telling whether the block follows the causal rule
+//                      (f32 mode; in bf16 mode the pack launches build the map)
 //   prep_kernel        f32 mode: D = rowsum(dO o O) (labml "Flash Attention",
 //                      "Backward pass"); zeroes the dQ slice (atomics target) and
 //                      the pads of the result blob
-//   pack_tiles_kernel  f32 rows -> bf16 64-row tiles (fab_tiles.h), one tile per
-//                      work-group through LDS, so that the row reads and the tile
-//                      writes are both contiguous; with a second input it also
-//                      forms D = rowsum(dO o O) and the per-query LSE/D blocks
-//                      (the bf16-mode prep)
+//   pack_qkv_kernel    f32 (or bf16) rows of Q, K, V -> bf16 64-row tiles
+//                      (fab_tiles.h), one tile per work-group through LDS so that
+//                      the row reads and the tile writes are both contiguous,
+//                      and the block map of the mask in the same launch
+//   pack_prep_kernel   the same with O and the LSE supplied, plus the bf16-mode
+//                      prep: the dO tiles, D = rowsum(dO o O) and the per-query
+//                      LSE/D blocks
 //   gqa_reduce_kernel  sums per-query-head dK/dV partials over each group of
 //                      H/Hkv heads (grouped-query attention, head map h/(H/Hkv))
 //   zero_kernel        zero fill

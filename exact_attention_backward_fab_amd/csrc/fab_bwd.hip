@@ -7,7 +7,8 @@
 // the row log-sum-exp of the forward, then forms, as in the labml "Flash
 // Attention" page ("Backward pass"):
 //     dV += P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dK += scale dS^T Q
-// with D = rowsum(dO o O) from the prep kernel.  The products run on the
+// with D = rowsum(dO o O) from the prep (bf16: the backward's forward or the
+// pack launch).  The products run on the
 // matrix cores: bf16 operands with f32 accumulation (v_mfma_f32_32x32x16_bf16)
 // or f32 operands (v_mfma_f32_32x32x2_f32).
 //
@@ -16,9 +17,11 @@
 // once; in f32 mode this kernel adds every key block's share with f32 atomics
 // into the result blob.
 //
-// Wave layout: wave w owns keys 32w..32w+31 of the block.  S and dP come out of
-// the matrix core with one key per lane (the C layout, see fab_common.h), which
-// is exactly the A-operand layout of P^T and dS^T for dV and dK.
+// Wave layout: a wave owns 32 keys of the block (the bf16 kernel: 8 waves, 4
+// key sub-blocks x 2 query halves of each 64-query step; the f32 and the wide-head
+// bf16 kernels: 4 waves, all queries of a step).  S and dP come out of the matrix
+// core with one key per lane (the C layout, see fab_common.h), which is exactly
+// the A-operand layout of P^T and dS^T for dV and dK.
 #include <algorithm>
 
 #include "fab_common.h"

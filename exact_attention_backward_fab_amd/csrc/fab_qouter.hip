@@ -4,7 +4,10 @@
 //   fwd_bf16_kernel        O = softmax(scale S + mask) V and the row LSE by query
 //                          blocks, with the running max and running sum of the
 //                          labml "Flash Attention" page ("Flash Attention
-//                          Optimization")
+//                          Optimization"); as the backward's own forward (PREP)
+//                          it stores no O but, from the O in registers, the
+//                          inputs of the backward kernels: D = rowsum(dO o O),
+//                          the bf16 Q and dO tiles and the LSE/D blocks
 //   dq_bf16_kernel         dQ = scale dS K by query blocks: a work-group owns 128
 //                          queries of one (batch, head) and streams the key
 //                          blocks that see them (block map), recomputing
