@@ -216,8 +216,8 @@ def cpu_baseline(s, q, k, v, d, mask, scale, causal, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              f"split of this path is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the split of this path "
+              f"over several GPUs (by key/value head group) is not built.", file=sys.stderr)
         sys.exit(2)
     import torch
     import exact_attention_backward_fab_amd as fab
