@@ -21,8 +21,10 @@ usual training convention) and the forward alone, and (`other_workloads`,
 --also) the whole step and the backward alone of further workloads, by
 default the long-context one.  Causal workloads are also timed with the causal
 rule passed as a flag instead of the mask tensor (`causal_flag_instead_of_mask`:
-same result, no block map or mask reads), and bf16 mode with q, k, v, d stored
-as bf16 (`bf16_inputs`: the values the matrix cores read).  `cpu_baseline` times the
+same result, no block map or mask reads), bf16 mode with q, k, v, d stored
+as bf16 (`bf16_inputs`: the values the matrix cores read), and the other
+arithmetic mode on the same workload (`other_mode`: f32 operands on the f32
+matrix cores, priced against the f32 peak).  `cpu_baseline` times the
 f64 CPU oracle on a bounded sample of the same workload on this host's cores.
 
 Prints exactly one JSON line.
@@ -352,6 +354,27 @@ def main():
                    "frac_of_peak": round((F_f + F_b) / (ms_b * 1e-3) / 1e12 / peak, 4)}
         del tb
 
+    # ---- the other arithmetic mode on the same workload (f32 operands on the f32
+    # matrix cores, priced against the f32 peak), whole step and backward alone
+    other_mode = None
+    om = "f32" if mode == "bf16" else "bf16"
+    if om in w.modes or om == "f32":
+        ws_o, _ = fab.alloc_workspace(fs, om, tm is not None, False, dev)
+        ws_ob, _ = fab.alloc_workspace(fs, om, tm is not None, True, dev)
+        O_o, lse_o = fab.forward_lse(tq, tk, tv, scale, mask=tm, mode=om, ws=ws_ob)
+        ms_o = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mask=tm, mode=om, blob=blob, ws=ws_o),
+                         args.steps, args.warmup, stream, args.min_warm_s)
+        ms_ob = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mask=tm, mode=om, O=O_o, lse=lse_o,
+                                                      blob=blob, ws=ws_ob), args.steps, args.warmup, stream,
+                          args.min_warm_s)
+        pk = PEAK_TFLOPS[om]
+        other_mode = {"mode": om, "ms_per_step": round(ms_o, 4),
+                      "value": round((F_f + F_b) / (ms_o * 1e-3) / 1e12, 3),
+                      "frac_of_peak": round((F_f + F_b) / (ms_o * 1e-3) / 1e12 / pk, 4), "peak": pk,
+                      "backward_only": {"ms": round(ms_ob, 4), "tflops": round(F_b / (ms_ob * 1e-3) / 1e12, 3),
+                                        "frac_of_peak": round(F_b / (ms_ob * 1e-3) / 1e12 / pk, 4)}}
+        del ws_o, ws_ob, O_o, lse_o
+
     # ---- other workloads (e.g. the long-context one), same protocol, same mode
     also = {}
     for wid in [int(x) for x in args.also.split(",") if x.strip()]:
@@ -392,6 +415,8 @@ def main():
         out["causal_flag_instead_of_mask"] = mask_free
     if bf16_in:
         out["bf16_inputs"] = bf16_in
+    if other_mode:
+        out["other_mode"] = other_mode
     if also:
         out["other_workloads"] = also
     if not args.no_cpu_baseline:
