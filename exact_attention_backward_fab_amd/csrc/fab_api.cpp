@@ -89,6 +89,10 @@ int check_shape(const fab_shape *s, Plan *pl)
     pl->dvp = hd.dv;
     pl->mp = (int)((s->M + fab::kPackRows - 1) / fab::kPackRows * fab::kPackRows);
     pl->np = (int)((s->N + fab::kPackRows - 1) / fab::kPackRows * fab::kPackRows);
+    // one head's bf16 tiles are addressed with 32-bit offsets: keep them below 2 GiB
+    const double head_elems = (double)std::max(pl->mp, pl->np) * std::max(pl->dkp, pl->dvp);
+    if (head_elems >= (double)(1 << 30))
+        return fail(FAB_E_UNSUPPORTED, "one head's rows exceed the kernels' 32-bit tile addressing (N or M too large)");
     return FAB_OK;
 }
 
