@@ -59,7 +59,9 @@ extern "C" {
 #define FAB_VERSION 100  /* 1.0.0 */
 
 /* Problem extents.  B, N, M >= 0 (zero gives an empty problem); H, Hkv, DK,
- * DV >= 1; H % Hkv == 0; DK, DV <= 192; every tensor below 2^31 elements. */
+ * DV >= 1; H % Hkv == 0; DK, DV <= 192; every tensor below 2^31 elements, and
+ * one head's rows (N or M, rounded up to 64) times its padded head dim below
+ * 2^30 (FAB_E_UNSUPPORTED otherwise). */
 typedef struct fab_shape {
     int64_t B, H, Hkv, N, M, DK, DV;
 } fab_shape;
