@@ -33,8 +33,16 @@ struct FwdCfg {
     static constexpr int LV = DVP + 4;     // sV row stride
 };
 
+// Two waves per SIMD where the operands fit 256 registers per wave (the head
+// dims up to 128), else one.
 template <int DKP, int DVP>
-__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs p)
+struct FwdF32Occ {
+    static constexpr int v = DKP + DVP <= 256 ? 2 : 1;
+};
+
+template <int DKP, int DVP>
+__global__ __launch_bounds__(256, (FwdF32Occ<DKP, DVP>::v))
+__attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::v))) void fwd_f32_kernel(FwdArgs p)
 {
     using C = FwdCfg<DKP, DVP>;
     constexpr int BC = C::BC, BR = C::BR, NT = C::NT, LK = C::LK, LV = C::LV;
