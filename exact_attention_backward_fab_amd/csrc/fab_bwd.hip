@@ -562,12 +562,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ============================================================== f32 mode
 // f32 operands: every matrix-core operand is one float per lane, so transposed
 // operands are plain strided LDS reads and no transposed copies are needed.
+// A work-group has KW x QH waves: KW sub-blocks of 32 keys times QH halves of
+// 32 queries of each step (the query halves of one key sub-block add their dK,
+// dV through LDS at the end).  4 x 1 for the small head dims, 2 x 2 for
+// 128 / 128 (every SIMD busy; the LDS just fits), 2 x 1 for the 192-wide ones.
 template <int DKP, int DVP>
 struct F32Cfg {
-    static constexpr int W = (DKP + DVP <= 128) ? 4 : 2;
+    static constexpr int KW = (DKP + DVP <= 128) ? 4 : 2;
+    static constexpr int QH = (DKP + DVP == 256) ? 2 : 1;
+    static constexpr int W = KW * QH;
     static constexpr int NT = 64 * W;
-    static constexpr int BC = 32 * W;   // keys per work-group
-    static constexpr int BR = 32;       // queries per step
+    static constexpr int BC = 32 * KW;  // keys per work-group
+    static constexpr int BR = 32 * QH;  // queries per step
     static constexpr int LK = DKP + 4, LV = DVP + 4, LQ = DKP + 4, LO = DVP + 4, LS = BC + 4;
 };
 
@@ -575,7 +581,7 @@ template <int DKP, int DVP>
 __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdArgs p)
 {
     using C = F32Cfg<DKP, DVP>;
-    constexpr int BC = C::BC, BR = C::BR, W = C::W, NT = C::NT;
+    constexpr int BC = C::BC, BR = C::BR, W = C::W, NT = C::NT, KW = C::KW, QH = C::QH;
     constexpr int LK = C::LK, LV = C::LV, LQ = C::LQ, LO = C::LO, LS = C::LS;
     __shared__ __attribute__((aligned(16))) float sK[BC * LK];
     __shared__ __attribute__((aligned(16))) float sV[BC * LV];
@@ -586,11 +592,12 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     __shared__ __attribute__((aligned(16))) float sD[BR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+    const int kw = QH == 1 ? w : w % KW, qq = QH == 1 ? 0 : w / KW;   // key sub-block, query half
     const int HB = p.H * p.B;
     const int j = blockIdx.x / HB, hb = blockIdx.x % HB;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int key0 = j * BC;
-    const int mykey = key0 + 32 * w + l32;
+    const int mykey = key0 + 32 * kw + l32;
     const bool keyok = mykey < p.M;
     const float *kh = p.k + (size_t)p.DK * p.M * (g + p.Hkv * b);
     const float *vh = p.v + (size_t)p.DV * p.M * (g + p.Hkv * b);
@@ -654,10 +661,10 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         // ---- S = Q K^T, dP = dO V^T (k index = half*(D/2) + t)
         f32x16 sacc = zero16(), pacc = zero16();
         {
-            const float *kr = &sK[(32 * w + l32) * LK + half * (DKP / 2)];
-            const float *vr = &sV[(32 * w + l32) * LV + half * (DVP / 2)];
-            const float *qr = &sQ[l32 * LQ + half * (DKP / 2)];
-            const float *orr = &sO[l32 * LO + half * (DVP / 2)];
+            const float *kr = &sK[(32 * kw + l32) * LK + half * (DKP / 2)];
+            const float *vr = &sV[(32 * kw + l32) * LV + half * (DVP / 2)];
+            const float *qr = &sQ[(32 * qq + l32) * LQ + half * (DKP / 2)];
+            const float *orr = &sO[(32 * qq + l32) * LO + half * (DVP / 2)];
 #pragma unroll
             for (int t = 0; t < DKP / 2; t += 4) {
                 const f32x4 a = *reinterpret_cast<const f32x4 *>(qr + t);
@@ -676,7 +683,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         // ---- P and dS
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int qr = 8 * r4 + 4 * half;
+            const int qr = 32 * qq + 8 * r4 + 4 * half;
             const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&sL[qr]);
             const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&sD[qr]);
 #pragma unroll
@@ -696,7 +703,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         // ---- dV += P^T dO, dK += dS^T Q
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int qr = crow(u, half);
+            const int qr = 32 * qq + crow(u, half);
 #pragma unroll
             for (int dt = 0; dt < DVP / 32; ++dt)
                 dvacc[dt] = mfma_f32(sacc[u], sO[qr * LO + dt * 32 + l32], dvacc[dt]);
@@ -706,14 +713,15 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         }
         // ---- dS to LDS [query][key]
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sS[crow(r, half) * LS + 32 * w + l32] = pacc[r];
+        for (int r = 0; r < 16; ++r) sS[(32 * qq + crow(r, half)) * LS + 32 * kw + l32] = pacc[r];
         __syncthreads();
         // ---- dQ tiles (32 queries x 32 dims), round-robin over the waves
-        for (int dt = w; dt < DKP / 32; dt += W) {
+        for (int tt = w; tt < QH * (DKP / 32); tt += W) {
+            const int qt = tt / (DKP / 32), dt = tt - qt * (DKP / 32);
             f32x16 acc = zero16();
 #pragma unroll
             for (int t = 0; t < BC / 2; t += 4) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sS[l32 * LS + half * (BC / 2) + t]);
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sS[(32 * qt + l32) * LS + half * (BC / 2) + t]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     acc = mfma_f32(a[i], sK[(half * (BC / 2) + t + i) * LK + dt * 32 + l32], acc);
@@ -722,10 +730,40 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             if (col < p.DK)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int n = q0 + crow(r, half);
+                    const int n = q0 + 32 * qt + crow(r, half);
                     if (n < p.N) unsafeAtomicAdd(dqh + col + (size_t)p.DK * n, acc[r] * p.scale);
                 }
         }
+    }
+
+    // ---- the second query half hands its dK, dV to the first through the K and V
+    // rows, which are no longer read (sK holds KW x dK tiles, sV KW x dV tiles)
+    if constexpr (QH == 2) {
+        static_assert(KW * (DKP / 32) * 1024 <= BC * LK && KW * (DVP / 32) * 1024 <= BC * LV,
+                      "dK/dV exchange area");
+        float *xk = sK + kw * (DKP / 32) * 1024;
+        float *xv = sV + kw * (DVP / 32) * 1024;
+        __syncthreads();   // every wave is done with sK and sV
+        if (qq == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xk[(dt * 16 + r) * 64 + lane] = dkacc[dt][r];
+#pragma unroll
+            for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xv[(dt * 16 + r) * 64 + lane] = dvacc[dt][r];
+        }
+        __syncthreads();
+        if (qq == 1) return;
+#pragma unroll
+        for (int dt = 0; dt < DKP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dkacc[dt][r] += xk[(dt * 16 + r) * 64 + lane];
+#pragma unroll
+        for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dvacc[dt][r] += xv[(dt * 16 + r) * 64 + lane];
     }
 
     const int hd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
@@ -737,7 +775,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         if (col < p.DK)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = key0 + 32 * w + crow(r, half);
+                const int key = key0 + 32 * kw + crow(r, half);
                 if (key < p.M) dkb[col + (size_t)p.DK * key] = dkacc[dt][r] * p.scale;
             }
     }
@@ -747,7 +785,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         if (col < p.DV)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = key0 + 32 * w + crow(r, half);
+                const int key = key0 + 32 * kw + crow(r, half);
                 if (key < p.M) dvb[col + (size_t)p.DV * key] = dvacc[dt][r];
             }
     }
