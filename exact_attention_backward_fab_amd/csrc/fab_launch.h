@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fab {
 
 struct Dims {
@@ -20,6 +22,30 @@ struct HeadDims {
     int dk, dv;
 };
 constexpr HeadDims kHeadDims[] = {{32, 32}, {64, 64}, {128, 128}, {192, 128}, {192, 192}};
+
+// Work-groups of one kernel (no dynamic LDS, `threads` per group) that the
+// current device holds resident at once: occupancy per CU times the CU count,
+// asked of the runtime once per device and kept; 0 if the runtime cannot say.
+struct ResidentCache {
+    static constexpr int kDevices = 16;
+    std::atomic<int> n[kDevices] = {};
+    int get(const void *kernel, int threads)
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+        if (dev < kDevices) {
+            const int c = n[dev].load(std::memory_order_relaxed);
+            if (c > 0) return c;
+        }
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        const int c = per_cu * cus;
+        if (dev < kDevices && c > 0) n[dev].store(c, std::memory_order_relaxed);
+        return c;
+    }
+};
 
 inline bool pick_head_dims(int DK, int DV, HeadDims *out)
 {
