@@ -628,23 +628,32 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     const float sl2 = p.scale * kLog2e;
     const int nqt = (p.N + BR - 1) / BR;
 
-    for (int it = 0; it < nqt; ++it) {
-        const int cls = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
-                                                                 it * (BR / kMapTile), key0 / kMapTile);
-        if (cls == kTileSkip) continue;
-        const int q0 = it * BR;
-        __syncthreads();  // the previous step is done with sQ, sO, sS
-        for (int c = tid; c < BR * (DKP / 4); c += NT) {
-            const int r = c / (DKP / 4), col = 4 * (c % (DKP / 4));
-            const int n = q0 + r;
-            *reinterpret_cast<f32x4 *>(&sQ[r * LQ + col]) =
-                n < p.N ? load_row4(qh + (size_t)p.DK * n, col, p.DK, p.vecK) : z;
+    // Live query steps only.  Where the registers allow it (PF), the rows of the
+    // next live step are loaded into registers while the current step computes
+    // and written to LDS at the top of the next one.
+    auto next_live = [&](int from, int *c) {
+        for (int i = from; i < nqt; ++i) {
+            *c = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
+                                                          i * (BR / kMapTile), key0 / kMapTile);
+            if (*c != kTileSkip) return i;
         }
-        for (int c = tid; c < BR * (DVP / 4); c += NT) {
-            const int r = c / (DVP / 4), col = 4 * (c % (DVP / 4));
-            const int n = q0 + r;
-            *reinterpret_cast<f32x4 *>(&sO[r * LO + col]) =
-                n < p.N ? load_row4(dh + dstride * n, col, p.DV, p.vecV) : z;
+        return nqt;
+    };
+    constexpr int PQ = BR * (DKP / 4) / NT, PO = BR * (DVP / 4) / NT;
+    constexpr bool PF = DKP + DVP <= 256 && PQ * NT == BR * (DKP / 4) && PO * NT == BR * (DVP / 4);
+    f32x4 pq[PF ? PQ : 1], po[PF ? PO : 1];
+    float pl = INFINITY, pd = 0.f;
+    auto fetch = [&](int step) {
+        const int q0 = step * BR;
+#pragma unroll
+        for (int i = 0; i < PQ; ++i) {
+            const int c = tid + i * NT, r = c / (DKP / 4), col = 4 * (c % (DKP / 4)), n = q0 + r;
+            pq[i] = n < p.N ? load_row4(qh + (size_t)p.DK * n, col, p.DK, p.vecK) : z;
+        }
+#pragma unroll
+        for (int i = 0; i < PO; ++i) {
+            const int c = tid + i * NT, r = c / (DVP / 4), col = 4 * (c % (DVP / 4)), n = q0 + r;
+            po[i] = n < p.N ? load_row4(dh + dstride * n, col, p.DV, p.vecV) : z;
         }
         if (tid < BR) {
             const int n = q0 + tid;
@@ -653,8 +662,58 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
                 L = p.lse[n + p.N * (h + p.H * b)];
                 Dl = p.delta[n + p.N * (h + p.H * b)];
             }
-            sL[tid] = (L == -INFINITY) ? INFINITY : L * kLog2e;
-            sD[tid] = Dl;
+            pl = (L == -INFINITY) ? INFINITY : L * kLog2e;
+            pd = Dl;
+        }
+    };
+    int cls = kTileSkip;
+    int it = next_live(0, &cls);
+    if constexpr (PF)
+        if (it < nqt) fetch(it);
+    while (it < nqt) {
+        const int q0 = it * BR;
+        int ncls = kTileSkip;
+        const int nx = next_live(it + 1, &ncls);
+        __syncthreads();  // the previous step is done with sQ, sO, sS
+        if constexpr (PF) {
+#pragma unroll
+            for (int i = 0; i < PQ; ++i) {
+                const int c = tid + i * NT, r = c / (DKP / 4), col = 4 * (c % (DKP / 4));
+                *reinterpret_cast<f32x4 *>(&sQ[r * LQ + col]) = pq[i];
+            }
+#pragma unroll
+            for (int i = 0; i < PO; ++i) {
+                const int c = tid + i * NT, r = c / (DVP / 4), col = 4 * (c % (DVP / 4));
+                *reinterpret_cast<f32x4 *>(&sO[r * LO + col]) = po[i];
+            }
+            if (tid < BR) {
+                sL[tid] = pl;
+                sD[tid] = pd;
+            }
+            if (nx < nqt) fetch(nx);
+        } else {
+            for (int c = tid; c < BR * (DKP / 4); c += NT) {
+                const int r = c / (DKP / 4), col = 4 * (c % (DKP / 4));
+                const int n = q0 + r;
+                *reinterpret_cast<f32x4 *>(&sQ[r * LQ + col]) =
+                    n < p.N ? load_row4(qh + (size_t)p.DK * n, col, p.DK, p.vecK) : z;
+            }
+            for (int c = tid; c < BR * (DVP / 4); c += NT) {
+                const int r = c / (DVP / 4), col = 4 * (c % (DVP / 4));
+                const int n = q0 + r;
+                *reinterpret_cast<f32x4 *>(&sO[r * LO + col]) =
+                    n < p.N ? load_row4(dh + dstride * n, col, p.DV, p.vecV) : z;
+            }
+            if (tid < BR) {
+                const int n = q0 + tid;
+                float L = -INFINITY, Dl = 0.f;
+                if (n < p.N) {
+                    L = p.lse[n + p.N * (h + p.H * b)];
+                    Dl = p.delta[n + p.N * (h + p.H * b)];
+                }
+                sL[tid] = (L == -INFINITY) ? INFINITY : L * kLog2e;
+                sD[tid] = Dl;
+            }
         }
         __syncthreads();
 
@@ -734,6 +793,8 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
                     if (n < p.N) unsafeAtomicAdd(dqh + col + (size_t)p.DK * n, acc[r] * p.scale);
                 }
         }
+        it = nx;
+        cls = ncls;
     }
 
     // ---- the second query half hands its dK, dV to the first through the K and V
