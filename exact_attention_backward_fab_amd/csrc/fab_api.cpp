@@ -39,12 +39,13 @@ struct Plan {
     fab::Dims d;
     int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
     // workspace offsets (bytes) and total
-    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_dqp, ws_tick, ws_pk,
-        ws_pv, ws_bytes;
+    size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_dqp, ws_tick, ws_ds,
+        ws_pk, ws_pv, ws_bytes;
     int dkp, dvp;  // padded head dims of the kernels
     int np;        // query rows per head of the bf16 Q / dO tiles
     int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
+    bool ds;       // bf16 mode: dQ from the stored dS^T tiles (else the recompute kernel)
 };
 
 // Shape checks: the asserts of "Function ggml_flash_attn_back" restated for the
@@ -103,7 +104,8 @@ int check_shape(const fab_shape *s, Plan *pl)
 //   delta      f32 D = rowsum(dO o O) [N,H,B]                  (backward, f32 mode)
 //   q16, o16   bf16 Q / dO tiles, Np rows per head             (backward, bf16 mode)
 //   stats      LSE / D blocks [B][H][Np/64][128]               (backward, bf16 mode)
-//   dqp, tick  dQ partials of split query blocks and counters  (backward, bf16 mode, few blocks)
+//   dqp, tick  dQ partials of split query blocks and counters  (backward, bf16 mode, dQ by recompute, few blocks)
+//   ds         bf16 dS^T tiles [B,H,Np/64,ceil(M/128)][128x64]  (backward, bf16 mode, dQ from dS)
 //   pk, pv     per-query-head dK / dV partials                 (backward, H > Hkv)
 // ws_fwd is the end of the part the forward alone uses.
 void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
@@ -142,9 +144,13 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         pl->ws_stats = off;
         off = align_up(off + sizeof(float) * qrows / 64 * 128);
     }
+    pl->ds = mode == FAB_MODE_BF16 && fab::dq_from_ds(d, pl->np, pl->dkp, pl->dvp);
     pl->ws_dqp = off;
     pl->ws_tick = off;
-    if (mode == FAB_MODE_BF16) {
+    pl->ws_ds = off;
+    if (pl->ds) {
+        off = align_up(off + (size_t)fab::ds_bytes(d, pl->np));
+    } else if (mode == FAB_MODE_BF16) {
         off = align_up(off + sizeof(float) * (size_t)fab::dq_part_floats(d, pl->dkp));
         pl->ws_tick = off;
         off = align_up(off + sizeof(int) * (size_t)fab::dq_split_blocks(d));
@@ -471,9 +477,10 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
     if (map && !bf16) FAB_LAUNCH(kMap, fab::launch_block_map(mk, map, pl.d, s), "block map launch");
     __bf16 *o16 = bf16 ? reinterpret_cast<__bf16 *>(wsb + pl.ws_o16) : nullptr;
     float *stats = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_stats) : nullptr;
-    float *dqp = bf16 ? reinterpret_cast<float *>(wsb + pl.ws_dqp) : nullptr;
-    int *tick = bf16 ? reinterpret_cast<int *>(wsb + pl.ws_tick) : nullptr;
-    const int ntick = (int)fab::dq_split_blocks(pl.d);
+    float *dqp = bf16 && !pl.ds ? reinterpret_cast<float *>(wsb + pl.ws_dqp) : nullptr;
+    int *tick = bf16 && !pl.ds ? reinterpret_cast<int *>(wsb + pl.ws_tick) : nullptr;
+    const int ntick = tick ? (int)fab::dq_split_blocks(pl.d) : 0;
+    __bf16 *dst = pl.ds ? reinterpret_cast<__bf16 *>(wsb + pl.ws_ds) : nullptr;
     float *delta = reinterpret_cast<float *>(wsb + pl.ws_delta);
     const float *lseu = lse;
     if (bf16 && !have) {
@@ -510,12 +517,15 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
     float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
     float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     if (bf16) {
-        FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, pl.gqa ? 1 : 0,
-                                                   pl.np, pl.mp, pl.d, s),
+        FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, dst,
+                                                   pl.gqa ? 1 : 0, pl.np, pl.mp, pl.d, s),
                    "backward launch");
-        FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
-                                                 pl.d, s),
-                   "dQ launch");
+        if (pl.ds)
+            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.d, s), "dQ launch");
+        else
+            FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
+                                           pl.d, s),
+                       "dQ launch");
     } else {
         FAB_LAUNCH(kBwd, fab::launch_backward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
                                                   static_cast<const float *>(v), static_cast<const float *>(d), mk,

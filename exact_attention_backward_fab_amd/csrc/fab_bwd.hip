@@ -58,8 +58,14 @@ struct KvArgs {
     const uint16_t *mask;
     const uint8_t *map;
     float *dk, *dv;
+    // dS^T of every visited (key block, query step) pair for the dQ product, or
+    // NULL: bf16 tiles [B,H,Np/64,nkb128] of 128 keys x 64 queries (16 KiB), each
+    // two 64-key tiles in the layout of fab_tiles.h (rows = keys; the 16-byte
+    // chunk c = 4 qq + 2 u + half holds the 8 queries of one matrix-core operand,
+    // see ds_query in fab_tiles.h).  Pairs the block map skips are not written.
+    __bf16 *ds;
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
-    int part_heads, nqb, nkb;
+    int part_heads, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
 };
@@ -249,6 +255,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
             // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
             // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
+            bf16x8 pa[2], da[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 float pv[8], dv8[8];
@@ -257,16 +264,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     pv[i] = sacc[8 * u + i];
                     dv8[i] = pacc[8 * u + i];
                 }
-                const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
+                pa[u] = to_bf16x8(pv);
+                da[u] = to_bf16x8(dv8);
+            }
+            if (p.ds) {
+                // the dS^T operands of this step, for dQ = scale dS K: stored before the
+                // products so that the stores complete behind them (the next step's
+                // vmcnt wait counts them too); streaming stores, which leave the L2 to
+                // the Q and dO tiles this kernel re-reads
+                __bf16 *t = p.ds + (((size_t)hb * nqt + it) * p.nkb128 + kb) * 8192 + (kw >> 1) * 4096 +
+                            (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8;
+                __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
+                __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
                 bf16x8 bo[DVP / 32], bq[DKP / 32];
 #pragma unroll
                 for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
 #pragma unroll
-                for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa, bo[dt], dvacc[dt]);
+                for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa[u], bo[dt], dvacc[dt]);
 #pragma unroll
                 for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
 #pragma unroll
-                for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da, bq[dt], dkacc[dt]);
+                for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da[u], bq[dt], dkacc[dt]);
             }
         }
         __syncthreads();   // every wave is done with the stages before they are refilled
@@ -905,13 +926,14 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
 
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
-                                float *dv, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s)
+                                float *dv, __bf16 *ds, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
+    if (ds && !dq_from_ds(d, Np, hd.dk, hd.dv)) return hipErrorInvalidValue;
     KvArgs a;
     a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
-    a.dk = dk; a.dv = dv;
+    a.dk = dk; a.dv = dv; a.ds = ds; a.nkb128 = ceil_div(d.M, 128);
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;

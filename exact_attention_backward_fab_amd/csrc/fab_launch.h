@@ -130,12 +130,33 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
                                float scale, float *dq, float *dk, float *dv, int part_heads, const Dims &d,
                                hipStream_t s);
 
+// dQ in bf16 mode comes either from the dS^T tiles the dK/dV kernel stores
+// (launch_dq_from_ds: a plain product, no recompute) or, for the wide head dims
+// and for shapes whose tiles would pass kDsMaxBytes, from the query-block-outer
+// kernel that recomputes S and dP (launch_dq).  The tiles are bf16, 128 keys x
+// 64 queries per (batch, head, query step, key block), dense over all pairs.
+constexpr int64_t kDsMaxBytes = int64_t(4) << 30;
+inline int64_t ds_bytes(const Dims &d, int Np)
+{
+    return (int64_t)d.B * d.H * (Np / 64) * ((d.M + 127) / 128) * 16384;
+}
+inline bool dq_from_ds(const Dims &d, int Np, int dkp, int dvp)
+{
+    return dkp + dvp <= 256 && ds_bytes(d, Np) <= kDsMaxBytes;
+}
+
 // Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
 // (launch_pack_prep_bf16 or the forward of launch_forward_prep_bf16, Np rows per head), K, V (Mp rows per head)
-// and the LSE/D blocks; stored as in launch_backward_f32.
+// and the LSE/D blocks; stored as in launch_backward_f32.  With ds (dq_from_ds
+// shapes only) it also stores the dS^T tiles of every pair it visits.
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
-                                float *dv, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
+                                float *dv, __bf16 *ds, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
+
+// dq [DK,N,H,B] = scale dS K from the dS^T tiles of launch_backward_bf16 and the
+// bf16 K tiles; every element written once.
+hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
+                             int Mp, const Dims &d, hipStream_t s);
 
 // dQ work split.  Query blocks have kDqBlock rows.  A grid of at most
 // kDqSplitBlocks blocks fills one round of two work-groups per CU on the 256 CUs

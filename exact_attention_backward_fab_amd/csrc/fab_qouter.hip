@@ -572,8 +572,164 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     }
 }
 
+// ============================================================== dQ from the stored dS
+// dQ = scale dS K as a plain product over the dS^T tiles the dK/dV kernel stored
+// (fab_tiles.h, ds_query): a work-group owns the 128 queries of two consecutive
+// query steps of one (batch, head) and streams the key blocks that see either of
+// them (the block map test of the dK/dV kernel, so exactly the tiles it wrote),
+// 64 keys at a time: both steps' dS^T key tiles and the K tile of those keys are
+// copied straight into LDS, and both operands are taken by transposing reads
+// (keys are the k dimension of the product).  8 waves: wave w owns
+// queries 32 (w & 3).. of the pair and the head-dim tiles of parity w >> 2.  Each
+// dQ element is written once (zero when no key block is live).
+struct DqsArgs {
+    const __bf16 *ds;               // dS^T tiles [B,H,Np/64,nkb128][128 keys x 64 queries]
+    const __bf16 *k16;              // bf16 tiles [B,Hkv,Mp,DKP], rows >= M zero
+    const uint8_t *map;
+    float *dq;                      // [DK,N,H,B] slice of the result blob
+    int B, H, Hkv, N, Np, M, Mp, DK, nqb, nkb, nkb128;
+    int causal;                     // causal rule as a flag (no mask, no map)
+    float scale;
+};
+
+constexpr int kDsW = 8, kDsNT = 64 * kDsW;
+constexpr int kDsList = 512;       // live key blocks listed at a time
+
+// LDS stages: the two dS^T key tiles and the K tile of 64 keys.  Two stages and
+// two work-groups per CU (16 waves): measured on the N=2048 and N=8192 causal
+// workloads, a second resident work-group hides the copy latency better than
+// deeper staging in one (4 stages, one work-group: 70 / 381 us instead of 53 / 256).
+template <int DKP>
+struct DsStages {
+    static constexpr int kCols = 16 + DKP / 8;   // chunk columns: dS^T of step 0, of step 1, K
+    static constexpr int kS = 8 * kChunkL;
+    static constexpr int kBytes = kCols * kChunkL;
+    static constexpr int N = 2;
+    static constexpr int Occ = (2 * (N * kBytes + 4 * kDsList + 256) <= 160 * 1024) ? 2 : 1;
+};
+
+template <int DKP>
+__global__ __launch_bounds__(kDsNT) __attribute__((amdgpu_waves_per_eu(2 * DsStages<DKP>::Occ, 2 * DsStages<DKP>::Occ)))
+void dq_ds_kernel(DqsArgs p)
+{
+    using ST = DsStages<DKP>;
+    constexpr int NS = ST::N;
+    // chunk columns copied per wave; when they do not split evenly, surplus copies
+    // repeat a column (same bytes to the same place), so that every wave issues the
+    // same number of copies per step (its vmcnt waits count on it)
+    constexpr int CH = (ST::kCols + kDsW - 1) / kDsW;
+    constexpr int NDT = DKP / 32, DT = (NDT + 1) / 2;
+    __shared__ __attribute__((aligned(16))) char sSK[NS * ST::kBytes];
+    __shared__ int sList[kDsList];
+    __shared__ int sCount[kDsW + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int sw = (w >> 1) & 1, qh = w & 1, dh = w >> 2;       // step of the pair, query half, head-dim parity
+    const int tr_off = tile_tr_off(lane);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sSK;
+    const int nqt = p.Np / kTR, HB = p.H * p.B;
+    const QWork wk = qouter_work(blockIdx.x, (nqt + 1) / 2, HB);   // latest queries first (most keys if causal)
+    const int it0 = 2 * wk.qt, hb = wk.hb;
+    const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
+    const int nst = min(2, nqt - it0);                                // steps of this pair inside Np
+    const rsrc_t rk = make_rsrc(p.k16 + (size_t)(g + p.Hkv * b) * p.Mp * DKP, (uint32_t)(p.Mp * DKP) * 2u);
+    // this pair's rows of dS^T tiles (nst x nkb128 x 16 KiB)
+    const rsrc_t rs = make_rsrc(p.ds + ((size_t)hb * nqt + it0) * p.nkb128 * 8192,
+                                (uint32_t)(nst * p.nkb128) * 16384u);
+
+    // copies of 64-key step ss (key tile ss: dS^T bytes 8192 ss.. of each step's row,
+    // K tile ss) into stage bf
+    auto issue = [&](int ss, int bf) {
+        const uint32_t stg = lds0 + (uint32_t)(bf * ST::kBytes);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = (i * kDsW + w) % ST::kCols;
+            if (c < 16)
+                lds_copy16(rs, stg + c * kChunkL,
+                           (uint32_t)((c >> 3) * p.nkb128 * 16 + ss * 8 + (c & 7)) * kChunkG + (uint32_t)lane * 16u);
+            else
+                lds_copy16(rk, stg + (c - 16 + 16) * kChunkL,
+                           (uint32_t)(ss * (DKP / 8) + c - 16) * kChunkG + (uint32_t)lane * 16u);
+        }
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int j = 0; j < DT; ++j) acc[j] = zero16();
+
+    for (int seg = 0; seg < p.nkb128; seg += kDsList) {
+        // a key block is listed when either step sees it; bit s of its class: step s does
+        const int count = build_live_list<kDsW>(sList, sCount, seg, min(seg + kDsList, p.nkb128), tid, lane, w,
+                                                [&](int kb) {
+            int live = 0;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                if (s2 < nst && tile_class<kTR / kMapTile, 128 / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
+                                                                           (it0 + s2) * (kTR / kMapTile),
+                                                                           kb * (128 / kMapTile)) != kTileSkip)
+                    live |= 1 << s2;
+            return live;
+        });
+        const int nss = 2 * count;   // two 64-key steps per listed key block
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < nss) issue(2 * (sList[i >> 1] >> 2) + (i & 1), i);
+        for (int li = 0; li < nss; ++li) {
+            wait_vm_steps<CH>(min(nss - 1 - li, NS - 2));   // step li has landed (this wave)
+            __syncthreads();                                  // ... for every wave; stage li-1 is free
+            const int nx = li + NS - 1;
+            if (nx < nss) issue(2 * (sList[nx >> 1] >> 2) + (nx & 1), nx % NS);
+            // the dS^T tile of a step that does not see this key block was never
+            // written: its copy is ignored
+            if (!((sList[li >> 1] >> sw) & 1)) continue;
+            const char *Sb = sSK + (li % NS) * ST::kBytes + sw * ST::kS;
+            const char *Kb = sSK + (li % NS) * ST::kBytes + 2 * ST::kS;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const bf16x8 a = lds_tr8(Sb + tr_off + 4608 * qh + 512 * kk + 256 * u);
+                    bf16x8 bk[DT];
+#pragma unroll
+                    for (int j = 0; j < DT; ++j)
+                        if (2 * j + dh < NDT) bk[j] = lds_tr8(Kb + tr_off + 4608 * (2 * j + dh) + 512 * kk + 256 * u);
+#pragma unroll
+                    for (int j = 0; j < DT; ++j)
+                        if (2 * j + dh < NDT) acc[j] = mfma_bf16(a, bk[j], acc[j]);
+                }
+        }
+        __syncthreads();   // every wave is done with the stages before they are refilled
+    }
+
+    // ---- store dQ (scaled): lane = head-dim column, slot r = query column
+    // crow(r, half) of this wave's 32, in the dS^T column order (ds_query)
+    float *dqh = p.dq + (size_t)p.N * p.DK * hb;
+#pragma unroll
+    for (int j = 0; j < DT; ++j) {
+        const int col = (2 * j + dh) * 32 + l32;
+        if (2 * j + dh < NDT && col < p.DK)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = (it0 + sw) * kTR + ds_query(32 * qh + crow(r, half));
+                if (n < p.N) dqh[(size_t)n * p.DK + col] = acc[j][r] * p.scale;
+            }
+    }
+}
+
 namespace {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+template <int DKP, int DVP, bool BF16>
+hipError_t run_dq_ds(const DqsArgs &a, hipStream_t s)
+{
+    if constexpr (!BF16) {
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((dq_ds_kernel<DKP>), dim3((a.Np / kTR + 1) / 2 * a.H * a.B), dim3(kDsNT), 0, s, a);
+        return hipGetLastError();
+    }
+}
 
 template <int DKP, int DVP, bool BF16>
 hipError_t run_dq(const DqArgs &a, hipStream_t s)
@@ -655,6 +811,20 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_dq, a, s, hd, true);
+}
+
+hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
+                             int Mp, const Dims &d, hipStream_t s)
+{
+    HeadDims hd;
+    if (!pick_head_dims(d.DK, d.DV, &hd) || !ds || !dq_from_ds(d, Np, hd.dk, hd.dv)) return hipErrorInvalidValue;
+    DqsArgs a;
+    a.ds = ds; a.k16 = k16; a.map = map; a.dq = dq;
+    a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.nkb128 = ceil_div(d.M, 128);
+    a.causal = d.causal;
+    a.scale = scale;
+    FAB_DISPATCH_HEAD_DIMS(run_dq_ds, a, s, hd, true);
 }
 
 }  // namespace fab

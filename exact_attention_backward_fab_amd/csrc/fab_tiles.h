@@ -31,6 +31,13 @@ __host__ __device__ __forceinline__ size_t tile_elem(int row, int c, int DP)
 // or past N), [64, 128) D = rowsum(dO o O).
 constexpr int kStatsTile = 128;
 
+// dS^T tiles (written by the dK/dV kernel, read by the dQ product): 64 key rows
+// per tile and the 64 queries of a step as 8 chunk columns.  Chunk c = 4 qq +
+// 2 u + half holds, at position e, the dS value of query 32 qq + 16 u + 8 (e >> 2)
+// + 4 half + (e & 3) -- the matrix-core k order in which the dK product consumes
+// it.  Column p = 8 c + e is thus query p with bits 2 and 3 swapped.
+__host__ __device__ __forceinline__ int ds_query(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
 // Per-lane byte offsets inside an LDS tile (see the tile layout above):
 //   row operand   16 bytes of row l32 (+32 kk), chunk column 2t + half:
 //                 row_off + 512 kk + 2304 t

@@ -130,9 +130,10 @@ SMALL = [
     ("one_key", Shape(1, 2, 1, 17, 1, 16, 16), None, 47),
     ("one_query", Shape(1, 2, 2, 1, 130, 64, 64), "random", 48),
     ("workload1", fi.WORKLOADS[1].shape, None, 1),
-    # 16 x 33 = 528 query blocks of 128: above the two-share dQ split's limit (512),
-    # so dQ runs one work-group per block (every other case here is split)
-    ("dq_unsplit_528_blocks", Shape(1, 33, 3, 2000, 600, 32, 32), "causal", 49),
+    # head dims 192 take dQ from the recompute kernel: 16 x 33 = 528 query blocks of
+    # 128 is above its two-share split's limit (512), so it runs one work-group per
+    # block (the other 192-wide cases here are split)
+    ("dq_unsplit_528_blocks", Shape(1, 33, 3, 2000, 200, 192, 128), "causal", 49),
 ]
 
 
@@ -316,6 +317,36 @@ def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mki
     ref = oracle_full(s, qr, kr, vr, dr, mask, scale)
     total = fab.blob_layout(fab.Shape(*s.astuple()))[3]
     check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"bf16 inputs {name}", mask=mask)
+
+
+@pytest.mark.parametrize("supplied", [False, True], ids=["own_forward", "o_lse_supplied"])
+@pytest.mark.parametrize("name,s,mkind,seed", [
+    ("causal_d64", Shape(1, 4, 2, 333, 333, 64, 64), "causal", 61),
+    ("random_d128", Shape(2, 2, 1, 200, 300, 128, 128), "random", 62),
+], ids=["causal_d64", "random_d128"])
+def test_bf16_stale_workspace_is_not_read(torch_dev, name, s, mkind, seed, supplied):
+    """bf16 mode stores dS^T only for the (key block, query step) pairs the block
+    map does not skip, and the dQ product reads only those: a workspace full of NaN
+    bit patterns (0xFF bytes) gives the oracle's result, identical to a zeroed one."""
+    torch, dev = torch_dev
+    fab = fabmod()
+    q, k, v, d = make_qkvd(s, seed)
+    mask = small_mask(mkind, s, seed)
+    scale = float(np.float32(1 / math.sqrt(s.DK)))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    tm = to_dev(torch, dev, mask)
+    O = lse = None
+    if supplied:
+        O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode="bf16")
+    blobs = []
+    for fill in (255, 0):
+        ws, _ = fab.alloc_workspace(fab.Shape(*s.astuple()), "bf16", True, supplied, dev)
+        ws.fill_(fill)
+        blobs.append(fab.backward(t[0], t[1], t[2], t[3], scale, mask=tm, mode="bf16", O=O, lse=lse, ws=ws))
+    torch.cuda.synchronize()
+    b0, b1 = (x.cpu().numpy() for x in blobs)
+    assert np.array_equal(b0, b1)
+    check_blob(s, b0, oracle_full(s, q, k, v, d, mask, scale), "bf16", name, mask)
 
 
 def test_caller_stream_is_used(torch_dev):
