@@ -240,6 +240,31 @@ __device__ __forceinline__ int ticket_take(int *t)
     return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------- work order
+// Work-group -> (query block, head) of the query-block-outer kernels.  Heads are
+// dealt to the XCDs in contiguous ranges (a work-group's XCD is its index mod 8),
+// so the heads of a key/value group share that XCD's L2.  Query blocks go latest
+// first: under a causal mask those see the most keys, so on a grid of several
+// rounds the longest blocks start first.  When the whole grid is resident at once
+// (fold), the dispatcher gives every CU its first work-group before any its
+// second, so the second half of the order shares CUs with the first; running
+// that half from the earliest block up puts long and short blocks together on a
+// CU.
+__device__ __forceinline__ void query_block_work(int bid, int nqt, int HB, int fold, int *qt, int *hb)
+{
+    int sl;
+    if (HB % 8 == 0) {
+        const int xcd = bid % 8, j = bid / 8, per = HB / 8;
+        sl = j / per;
+        *hb = xcd * per + j % per;
+    } else {
+        sl = bid / HB;
+        *hb = bid % HB;
+    }
+    const int hn = (nqt + 1) / 2;
+    *qt = (!fold || sl < hn) ? nqt - 1 - sl : sl - hn;
+}
+
 // ---------------------------------------------------------------- reductions
 // Butterfly sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float x, int width)

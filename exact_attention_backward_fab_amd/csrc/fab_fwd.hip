@@ -20,32 +20,9 @@ struct FwdArgs {
     int B, H, Hkv, N, M, DK, DV;
     int nqb, nkb, vecK, vecV;
     int causal;                     // causal rule as a flag (no mask, no map)
-    int fold;                       // the whole grid is resident at once (see fwd_f32_work)
+    int fold;                       // the whole grid is resident at once (query_block_work)
     float scale;
 };
-
-// Work-group -> (query block, head).  Heads are dealt to the XCDs in contiguous
-// ranges (a work-group's XCD is its index mod 8).  Query blocks go latest first:
-// under a causal mask those see the most keys, so on a grid of several rounds
-// the longest blocks start first.  When the whole grid is resident at once
-// (fold), the dispatcher gives every CU its first work-group before any its
-// second, so the second half of the order shares CUs with the first; running
-// that half from the earliest block up puts long and short blocks together on
-// a CU (on the 16-block, 32-head causal case, 690 -> 500 us).
-__device__ __forceinline__ void fwd_f32_work(int bid, int nqt, int HB, int fold, int *qt, int *hb)
-{
-    int sl;
-    if (HB % 8 == 0) {
-        const int xcd = bid % 8, j = bid / 8, per = HB / 8;
-        sl = j / per;
-        *hb = xcd * per + j % per;
-    } else {
-        sl = bid / HB;
-        *hb = bid % HB;
-    }
-    const int hn = (nqt + 1) / 2;
-    *qt = (!fold || sl < hn) ? nqt - 1 - sl : sl - hn;
-}
 
 template <int DKP, int DVP>
 struct FwdCfg {
@@ -77,7 +54,7 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
     const int nqt = (p.N + BR - 1) / BR;
     int qt, hb;
-    fwd_f32_work(blockIdx.x, nqt, p.H * p.B, p.fold, &qt, &hb);
+    query_block_work(blockIdx.x, nqt, p.H * p.B, p.fold, &qt, &hb);
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int n = qt * BR + w * 32 + l32;  // this lane's query (C-layout column)
     const bool nok = n < p.N;

@@ -47,24 +47,14 @@ struct QStages {
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-// Work-group -> (query tile, head).  Consecutive work-groups are dealt round-robin
-// to the 8 XCDs; when the heads split evenly over the XCDs, each XCD gets a
-// contiguous range of heads (the heads of a key/value group share its K/V rows in
-// that XCD's L2) and walks it latest query tile first, heads fastest.
+// Work-group -> (query tile, head): query_block_work (fab_common.h).
 struct QWork {
     int qt, hb;
 };
-__device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB)
+__device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB, int fold = 0)
 {
     QWork r;
-    if (HB % 8 == 0) {
-        const int xcd = bid % 8, j = bid / 8, per = HB / 8;
-        r.qt = nqt - 1 - j / per;
-        r.hb = xcd * per + j % per;
-    } else {
-        r.qt = nqt - 1 - bid / HB;
-        r.hb = bid % HB;
-    }
+    query_block_work(bid, nqt, HB, fold, &r.qt, &r.hb);
     return r;
 }
 
@@ -233,6 +223,7 @@ struct FwdArgs16 {
     int64_t pad_lo[3], pad_hi[3];
     int *zero;
     int nzero, Np;
+    int fold;                       // the whole grid is resident at once (query_block_work)
 };
 
 template <int DKP, int DVP, bool PREP>
@@ -248,7 +239,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
     const int nqt = (p.N + kQBQ - 1) / kQBQ;
-    const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B);   // latest queries first (most keys if causal)
+    const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B, p.fold);   // latest queries first (most keys if causal)
     const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int q0 = qt * kQBQ;
@@ -589,6 +580,7 @@ struct DqsArgs {
     float *dq;                      // [DK,N,H,B] slice of the result blob
     int B, H, Hkv, N, Np, M, Mp, DK, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
+    int fold;                       // the whole grid is resident at once (query_block_work)
     float scale;
 };
 
@@ -629,7 +621,7 @@ void dq_ds_kernel(DqsArgs p)
     const int tr_off = tile_tr_off(lane);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sSK;
     const int nqt = p.Np / kTR, HB = p.H * p.B;
-    const QWork wk = qouter_work(blockIdx.x, (nqt + 1) / 2, HB);   // latest queries first (most keys if causal)
+    const QWork wk = qouter_work(blockIdx.x, (nqt + 1) / 2, HB, p.fold);   // latest queries first (most keys if causal)
     const int it0 = 2 * wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int nst = min(2, nqt - it0);                                // steps of this pair inside Np
@@ -726,7 +718,11 @@ hipError_t run_dq_ds(const DqsArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((dq_ds_kernel<DKP>), dim3((a.Np / kTR + 1) / 2 * a.H * a.B), dim3(kDsNT), 0, s, a);
+        const int grid = (a.Np / kTR + 1) / 2 * a.H * a.B;
+        static ResidentCache slots;
+        DqsArgs b = a;
+        b.fold = grid <= slots.get(reinterpret_cast<const void *>(&dq_ds_kernel<DKP>), kDsNT);
+        hipLaunchKernelGGL((dq_ds_kernel<DKP>), dim3(grid), dim3(kDsNT), 0, s, b);
         return hipGetLastError();
     }
 }
@@ -749,11 +745,16 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        const dim3 grid(ceil_div(a.N, kQBQ) * a.H * a.B);
-        if (a.dO)
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), grid, dim3(kQNT), 0, s, a);
-        else
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), grid, dim3(kQNT), 0, s, a);
+        const int grid = ceil_div(a.N, kQBQ) * a.H * a.B;
+        static ResidentCache slots_prep, slots_fwd;
+        FwdArgs16 b = a;
+        if (a.dO) {
+            b.fold = grid <= slots_prep.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, true>), kQNT);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), dim3(grid), dim3(kQNT), 0, s, b);
+        } else {
+            b.fold = grid <= slots_fwd.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, false>), kQNT);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), dim3(grid), dim3(kQNT), 0, s, b);
+        }
         return hipGetLastError();
     }
 }
