@@ -98,13 +98,20 @@ def kernel_work(s, causal, mode, has_mask):
                     if s.DK <= a and s.DV <= b)
     mp = (s.M + 63) // 64 * 64
     np_ = (s.N + 63) // 64 * 64
+    dq_from_ds = bf16 and dkp + dvp <= 256 and s.B * s.H * (np_ // 64) * math.ceil(s.M / 128) * 16384 <= 4 << 30
     w = {
         # S = Q K^T and O = P V
         "forward": (2.0 * pairs * (s.DK + s.DV), "flop"),
         # bf16: S, dP, dV, dK; f32: also dQ (atomics)
         "backward": (2.0 * pairs * ((2 * s.DK + 2 * s.DV) if bf16 else (3 * s.DK + 2 * s.DV)), "flop"),
-        # S, dP, dQ
-        "dq": (2.0 * pairs * (2 * s.DK + s.DV), "flop"),
+        # dQ: from the dS^T tiles the dK/dV kernel stores (head-dim pairs up to
+        # 128/128 and tiles within 4 GiB, as the library decides) a memory-bound
+        # product that reads 2 bytes of dS per visited pair and writes dQ, with the
+        # grouped-query reduction of dK and dV in the same launch; otherwise S, dP
+        # and dQ by the recompute kernel
+        "dq": ((2.0 * pairs + 4.0 * rows * s.DK
+                + (4.0 * s.M * (s.DK + s.DV) * s.B * (s.H + s.Hkv) if s.H > s.Hkv else 0.0), "byte")
+               if dq_from_ds else (2.0 * pairs * (2 * s.DK + s.DV), "flop")),
         "block_map": (2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32), "byte"),
         # bf16: read d, O and the LSE, write the bf16 dO tiles and the LSE/D blocks;
         # f32: read d and O, write D and zero the dQ slice

@@ -520,8 +520,10 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
         FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, dst,
                                                    pl.gqa ? 1 : 0, pl.np, pl.mp, pl.d, s),
                    "backward launch");
-        if (pl.ds)
-            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.d, s), "dQ launch");
+        if (pl.ds)   // with the grouped-query reduction of dK and dV in the same launch
+            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.gqa ? dk : nullptr,
+                                                   blob + pl.off_k, pl.gqa ? dv : nullptr, blob + pl.off_v, pl.d, s),
+                       "dQ launch");
         else
             FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
                                            pl.d, s),
@@ -533,7 +535,7 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
                                                   pl.gqa ? 1 : 0, pl.d, s),
                    "backward launch");
     }
-    if (pl.gqa) {
+    if (pl.gqa && !pl.ds) {
         FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, s),
                    "dK/dV reduce launch");
     }

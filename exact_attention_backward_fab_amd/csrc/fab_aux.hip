@@ -389,29 +389,6 @@ hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __
 // ============================================================== GQA reduce
 // dK and dV in one launch: work items [0, n0) reduce job 0, the rest job 1; each
 // sums the rk2 per-query-head partials of a group in head order.
-struct ReduceJob {
-    const float *part;
-    float *dst;
-    int64_t chunk;   // floats of one head's slice (D * M)
-    int vec;         // chunk % 4 == 0: float4 items
-    int64_t items;   // work items (float4 or float) over all groups
-};
-__device__ __forceinline__ void reduce_item(const ReduceJob &r, int rk2, int64_t i)
-{
-    if (r.vec) {
-        const int64_t c4 = r.chunk / 4, gb = i / c4, off = i - gb * c4;
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(r.part) + gb * rk2 * c4 + off;
-        f32x4 s = src[0];
-        for (int k = 1; k < rk2; ++k) s += src[k * c4];
-        reinterpret_cast<f32x4 *>(r.dst)[i] = s;
-    } else {
-        const int64_t gb = i / r.chunk, off = i - gb * r.chunk;
-        const float *src = r.part + gb * rk2 * r.chunk + off;
-        float s = src[0];
-        for (int k = 1; k < rk2; ++k) s += src[k * r.chunk];
-        r.dst[i] = s;
-    }
-}
 __global__ __launch_bounds__(256) void gqa_reduce_kernel(ReduceJob j0, ReduceJob j1, int rk2)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -458,19 +435,8 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
 
 hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s)
 {
-    const int rk2 = d.H / d.Hkv;
-    const int64_t groups = (int64_t)d.Hkv * d.B;
     ReduceJob j[2];
-    const float *part[2] = {pk, pv};
-    float *dst[2] = {dk, dv};
-    const int D[2] = {d.DK, d.DV};
-    for (int t = 0; t < 2; ++t) {
-        j[t].part = part[t];
-        j[t].dst = dst[t];
-        j[t].chunk = (int64_t)D[t] * d.M;
-        j[t].vec = (j[t].chunk % 4 == 0);
-        j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;
-    }
+    const int rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, j);
     const int64_t work = j[0].items + j[1].items;
     if (work == 0) return hipSuccess;
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);

@@ -7,6 +7,8 @@
 
 #include <type_traits>
 
+#include "fab_launch.h"
+
 namespace fab {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -263,6 +265,26 @@ __device__ __forceinline__ void query_block_work(int bid, int nqt, int HB, int f
     }
     const int hn = (nqt + 1) / 2;
     *qt = (!fold || sl < hn) ? nqt - 1 - sl : sl - hn;
+}
+
+// ---------------------------------------------------------------- grouped-query reduction
+// Item i of a ReduceJob (fab_launch.h): the sum of the rk2 query-head partials of
+// one float4 (or float) of a key/value head's dK or dV slice, in head order.
+__device__ __forceinline__ void reduce_item(const ReduceJob &r, int rk2, int64_t i)
+{
+    if (r.vec) {
+        const int64_t c4 = r.chunk / 4, gb = i / c4, off = i - gb * c4;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(r.part) + gb * rk2 * c4 + off;
+        f32x4 s = src[0];
+        for (int k = 1; k < rk2; ++k) s += src[k * c4];
+        reinterpret_cast<f32x4 *>(r.dst)[i] = s;
+    } else {
+        const int64_t gb = i / r.chunk, off = i - gb * r.chunk;
+        const float *src = r.part + gb * rk2 * r.chunk + off;
+        float s = src[0];
+        for (int k = 1; k < rk2; ++k) s += src[k * r.chunk];
+        r.dst[i] = s;
+    }
 }
 
 // ---------------------------------------------------------------- reductions

@@ -154,9 +154,12 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
                                 float *dv, __bf16 *ds, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
 
 // dq [DK,N,H,B] = scale dS K from the dS^T tiles of launch_backward_bf16 and the
-// bf16 K tiles; every element written once.
+// bf16 K tiles; every element written once.  With pk (H > Hkv) the same launch
+// also runs the grouped-query reduction of launch_gqa_reduce (extra work-groups
+// that take the CU slots the short query blocks free).
 hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
-                             int Mp, const Dims &d, hipStream_t s);
+                             int Mp, const float *pk, float *dk, const float *pv, float *dv, const Dims &d,
+                             hipStream_t s);
 
 // dQ work split.  Query blocks have kDqBlock rows.  A grid of at most
 // kDqSplitBlocks blocks fills one round of two work-groups per CU on the 256 CUs
@@ -177,8 +180,34 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
                      const uint16_t *mask, const uint8_t *map, float scale, float *dq, float *part, int *ticket,
                      int Np, int Mp, const Dims &d, hipStream_t s);
 
-// dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b] (r in order) for dK
-// (pk -> dk) and dV (pv -> dv), one launch.
+// Grouped-query reduction: dst[c, m, g, b] = sum_{r < rk2} part[c, m, g*rk2 + r, b]
+// (r in order) for dK (pk -> dk) and dV (pv -> dv).  One job per tensor: items
+// are float4 (chunk % 4 == 0) or single floats, numbered over all groups.
+struct ReduceJob {
+    const float *part;
+    float *dst;
+    int64_t chunk;   // floats of one head's slice (D * M)
+    int vec;         // chunk % 4 == 0: float4 items
+    int64_t items;   // work items (float4 or float) over all groups
+};
+// Fills the two jobs; returns rk2 = H / Hkv.
+inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, ReduceJob j[2])
+{
+    const int64_t groups = (int64_t)d.Hkv * d.B;
+    const float *part[2] = {pk, pv};
+    float *dst[2] = {dk, dv};
+    const int D[2] = {d.DK, d.DV};
+    for (int t = 0; t < 2; ++t) {
+        j[t].part = part[t];
+        j[t].dst = dst[t];
+        j[t].chunk = (int64_t)D[t] * d.M;
+        j[t].vec = (j[t].chunk % 4 == 0);
+        j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;
+    }
+    return d.H / d.Hkv;
+}
+
+// The reduction above, one launch.
 hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s);
 
 // Fill n floats with zero.

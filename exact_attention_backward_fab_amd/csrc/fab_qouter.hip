@@ -582,6 +582,9 @@ struct DqsArgs {
     int causal;                     // causal rule as a flag (no mask, no map)
     int fold;                       // the whole grid is resident at once (query_block_work)
     float scale;
+    // grouped-query reduction run by the work-groups past the dQ grid (nred of them)
+    ReduceJob red[2];
+    int rk2, ndq, nred;
 };
 
 constexpr int kDsW = 8, kDsNT = 64 * kDsW;
@@ -616,7 +619,19 @@ void dq_ds_kernel(DqsArgs p)
     __shared__ int sCount[kDsW + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    if ((int)blockIdx.x >= p.ndq) {
+        // grouped-query reduction of dK and dV: these work-groups come after the dQ
+        // grid and take the CU slots that the short query blocks free
+        const int64_t total = p.red[0].items + p.red[1].items;
+        for (int64_t i = (int64_t)(blockIdx.x - p.ndq) * kDsNT + tid; i < total; i += (int64_t)p.nred * kDsNT) {
+            if (i < p.red[0].items)
+                reduce_item(p.red[0], p.rk2, i);
+            else
+                reduce_item(p.red[1], p.rk2, i - p.red[0].items);
+        }
+        return;
+    }
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;   // wave index (uniform, < 8)
     const int sw = (w >> 1) & 1, qh = w & 1, dh = w >> 2;       // step of the pair, query half, head-dim parity
     const int tr_off = tile_tr_off(lane);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sSK;
@@ -718,11 +733,15 @@ hipError_t run_dq_ds(const DqsArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        const int grid = (a.Np / kTR + 1) / 2 * a.H * a.B;
         static ResidentCache slots;
         DqsArgs b = a;
-        b.fold = grid <= slots.get(reinterpret_cast<const void *>(&dq_ds_kernel<DKP>), kDsNT);
-        hipLaunchKernelGGL((dq_ds_kernel<DKP>), dim3(grid), dim3(kDsNT), 0, s, b);
+        b.ndq = (a.Np / kTR + 1) / 2 * a.H * a.B;
+        const int res = slots.get(reinterpret_cast<const void *>(&dq_ds_kernel<DKP>), kDsNT);
+        b.fold = b.ndq <= res;
+        // one round of reduction work-groups over the chip, fewer for small reductions
+        const int64_t items = a.red[0].items + a.red[1].items;
+        b.nred = (int)std::min<int64_t>((items + kDsNT - 1) / kDsNT, std::max(res / 2, 1));
+        hipLaunchKernelGGL((dq_ds_kernel<DKP>), dim3(b.ndq + b.nred), dim3(kDsNT), 0, s, b);
         return hipGetLastError();
     }
 }
@@ -815,7 +834,8 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
 }
 
 hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
-                             int Mp, const Dims &d, hipStream_t s)
+                             int Mp, const float *pk, float *dk, const float *pv, float *dv, const Dims &d,
+                             hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd) || !ds || !dq_from_ds(d, Np, hd.dk, hd.dv)) return hipErrorInvalidValue;
@@ -825,6 +845,12 @@ hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t 
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.nkb128 = ceil_div(d.M, 128);
     a.causal = d.causal;
     a.scale = scale;
+    if (pk) {
+        a.rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, a.red);
+    } else {
+        a.rk2 = 1;
+        a.red[0] = a.red[1] = ReduceJob{nullptr, nullptr, 0, 0, 0};
+    }
     FAB_DISPATCH_HEAD_DIMS(run_dq_ds, a, s, hd, true);
 }
 
