@@ -59,10 +59,12 @@ struct KvArgs {
     const uint8_t *map;
     float *dk, *dv;
     // dS^T of every visited (key block, query step) pair for the dQ product, or
-    // NULL: bf16 tiles [B,H,Np/64,nkb128] of 128 keys x 64 queries (16 KiB), each
-    // two 64-key tiles in the layout of fab_tiles.h (rows = keys; the 16-byte
-    // chunk c = 4 qq + 2 u + half holds the 8 queries of one matrix-core operand,
-    // see ds_query in fab_tiles.h).  Pairs the block map skips are not written.
+    // NULL: 64-key x 64-query bf16 tiles in the layout of fab_tiles.h (rows = keys;
+    // the 16-byte chunk c = 4 qq + 2 u + half holds the 8 queries of one
+    // matrix-core operand, see ds_query in fab_tiles.h), ordered
+    // [B,H,ceil(Np/128)][nkb128][2 key tiles][2 query steps]: the two query steps
+    // of a pair sit side by side, so the dQ product reads one contiguous stream.
+    // Pairs the block map skips are not written.
     __bf16 *ds;
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
     int part_heads, nqb, nkb, nkb128;
@@ -272,7 +274,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // products so that the stores complete behind them (the next step's
                 // vmcnt wait counts them too); streaming stores, which leave the L2 to
                 // the Q and dO tiles this kernel re-reads
-                __bf16 *t = p.ds + (((size_t)hb * nqt + it) * p.nkb128 + kb) * 8192 + (kw >> 1) * 4096 +
+                __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
+                                    (kw >> 1) * 2 + (it & 1)) * 4096 +
                             (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8;
                 __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
                 __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));

@@ -134,11 +134,11 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
 // (launch_dq_from_ds: a plain product, no recompute) or, for the wide head dims
 // and for shapes whose tiles would pass kDsMaxBytes, from the query-block-outer
 // kernel that recomputes S and dP (launch_dq).  The tiles are bf16, 128 keys x
-// 64 queries per (batch, head, query step, key block), dense over all pairs.
+// 128 queries per (batch, head, query-step pair, key block), dense over all pairs.
 constexpr int64_t kDsMaxBytes = int64_t(4) << 30;
 inline int64_t ds_bytes(const Dims &d, int Np)
 {
-    return (int64_t)d.B * d.H * (Np / 64) * ((d.M + 127) / 128) * 16384;
+    return (int64_t)d.B * d.H * ((Np / 64 + 1) / 2) * ((d.M + 127) / 128) * 32768;
 }
 inline bool dq_from_ds(const Dims &d, int Np, int dkp, int dvp)
 {

@@ -574,7 +574,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 // queries 32 (w & 3).. of the pair and the head-dim tiles of parity w >> 2.  Each
 // dQ element is written once (zero when no key block is live).
 struct DqsArgs {
-    const __bf16 *ds;               // dS^T tiles [B,H,Np/64,nkb128][128 keys x 64 queries]
+    const __bf16 *ds;               // dS^T tiles [B,H,ceil(Np/128),nkb128][2 key tiles][2 query steps][64 x 64]
     const __bf16 *k16;              // bf16 tiles [B,Hkv,Mp,DKP], rows >= M zero
     const uint8_t *map;
     float *dq;                      // [DK,N,H,B] slice of the result blob
@@ -641,20 +641,19 @@ void dq_ds_kernel(DqsArgs p)
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int nst = min(2, nqt - it0);                                // steps of this pair inside Np
     const rsrc_t rk = make_rsrc(p.k16 + (size_t)(g + p.Hkv * b) * p.Mp * DKP, (uint32_t)(p.Mp * DKP) * 2u);
-    // this pair's rows of dS^T tiles (nst x nkb128 x 16 KiB)
-    const rsrc_t rs = make_rsrc(p.ds + ((size_t)hb * nqt + it0) * p.nkb128 * 8192,
-                                (uint32_t)(nst * p.nkb128) * 16384u);
+    // this pair's dS^T tiles: 2 nkb128 key tiles x 2 query steps of 8 KiB, in that order
+    const rsrc_t rs = make_rsrc(p.ds + ((size_t)hb * ((nqt + 1) / 2) + wk.qt) * p.nkb128 * 16384,
+                                (uint32_t)p.nkb128 * 32768u);
 
-    // copies of 64-key step ss (key tile ss: dS^T bytes 8192 ss.. of each step's row,
-    // K tile ss) into stage bf
+    // copies of 64-key step ss (key tile ss: the 16 KiB of both query steps' dS^T at
+    // 16384 ss.., K tile ss) into stage bf
     auto issue = [&](int ss, int bf) {
         const uint32_t stg = lds0 + (uint32_t)(bf * ST::kBytes);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = (i * kDsW + w) % ST::kCols;
             if (c < 16)
-                lds_copy16(rs, stg + c * kChunkL,
-                           (uint32_t)((c >> 3) * p.nkb128 * 16 + ss * 8 + (c & 7)) * kChunkG + (uint32_t)lane * 16u);
+                lds_copy16(rs, stg + c * kChunkL, (uint32_t)(ss * 16 + c) * kChunkG + (uint32_t)lane * 16u);
             else
                 lds_copy16(rk, stg + (c - 16 + 16) * kChunkL,
                            (uint32_t)(ss * (DKP / 8) + c - 16) * kChunkG + (uint32_t)lane * 16u);
