@@ -37,6 +37,30 @@ def test_strerror_covers_every_status():
     assert L.fab_strerror(-99).decode() == "unknown status"
 
 
+def _ds_bytes(s):
+    # bf16 dS of every (query, key) pair, both extents rounded up to 128
+    return 2 * s.B * s.H * (-(-s.N // 128) * 128) * (-(-s.M // 128) * 128)
+
+
+def test_bf16_workspace_holds_ds_within_its_limit():
+    """bf16 mode with head dims up to 128 keeps the bf16 dS tiles in the backward's
+    workspace while they fit 4 GiB; the 192-wide heads, f32 mode and larger shapes
+    compute dQ without them (the header's statement of fab_workspace_bytes)."""
+    s = fab.Shape(1, 16, 4, 8192, 8192, 128, 128)
+    bf, f32 = fab.workspace_bytes(s, "bf16", False, True), fab.workspace_bytes(s, "f32", False, True)
+    assert bf >= _ds_bytes(s) > f32
+    # odd extents: one query step and a partial key block still take whole 128 x 128 blocks
+    small = fab.Shape(1, 2, 1, 37, 29, 3, 5)
+    assert fab.workspace_bytes(small, "bf16", False, True) >= _ds_bytes(small)
+    # 192-wide heads: recompute, no dS room
+    wide = fab.Shape(4, 16, 16, 512, 4096, 192, 128)
+    assert fab.workspace_bytes(wide, "bf16", False, True) < _ds_bytes(wide)
+    # past 4 GiB of tiles: recompute
+    big = fab.Shape(1, 40, 8, 8192, 8192, 128, 128)
+    assert _ds_bytes(big) > 4 << 30
+    assert fab.workspace_bytes(big, "bf16", False, True) < _ds_bytes(big)
+
+
 @pytest.mark.parametrize("shape", [
     fab.Shape(2, 4, 2, 2, 4, 3, 5), fab.Shape(1, 2, 1, 3, 5, 3, 5), fab.Shape(1, 1, 1, 1, 1, 1, 1),
     fab.Shape(1, 32, 8, 2048, 2048, 128, 128), fab.Shape(4, 16, 16, 512, 4096, 192, 128),
