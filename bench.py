@@ -17,7 +17,9 @@ kernels: `ms_per_step_with_kernel_events`) for every kernel's time per step
 and its algorithmic rate (TFLOP/s for the matrix-core kernels, GB/s for the
 memory-bound ones) and the `roofline` object of the dominant kernel.  The line
 also reports the backward alone (O and LSE supplied by a prior forward, the
-usual training convention) and the forward alone, and (`other_workloads`,
+usual training convention; with its own per-kernel breakdown, whose "pack" is
+the one launch that packs Q, K, V and preps d, O and the LSE) and the forward
+alone, and (`other_workloads`,
 --also) the whole step and the backward alone of further workloads, by
 default the long-context one.  Causal workloads are also timed with the causal
 rule passed as a flag instead of the mask tensor (`causal_flag_instead_of_mask`:
@@ -123,6 +125,13 @@ def kernel_work(s, causal, mode, has_mask):
                  + ((2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32)) if has_mask else 0.0), "byte"),
         # read per-query-head partials, write per-group sums
         "gqa_reduce": (4.0 * s.M * (s.DK + s.DV) * s.B * (s.H + s.Hkv), "byte"),
+        # (the backward alone, bf16) the pack of Q, K, V (f32 read, bf16 tiles
+        # written) with the block map, and the prep of d, O and the LSE (dO tiles
+        # and LSE/D blocks written), one launch
+        "pack_prep": (s.B * (s.H * 4.0 * s.N * s.DK + s.Hkv * 4.0 * s.M * (s.DK + s.DV))
+                      + s.B * (s.H * 2.0 * np_ * dkp + s.Hkv * 2.0 * mp * (dkp + dvp))
+                      + ((2.0 * s.M * s.N + math.ceil(s.N / 32) * math.ceil(s.M / 32)) if has_mask else 0.0)
+                      + rows * (8.0 * s.DV + 4.0) + s.H * s.B * (np_ * dvp * 2.0 + np_ / 64 * 512.0), "byte"),
     }
     return w
 
@@ -279,25 +288,41 @@ def main():
     step_fwd()
     torch.cuda.synchronize()
     ms_bwd = time_loop(torch, step_bwd, args.steps, args.warmup, stream, args.min_warm_s)
+    # per-kernel durations of the backward alone (events around every launch, as above)
+    fab.profile_reset()
+    fab.profile_enable(True)
+    time_loop(torch, step_bwd, args.steps, 0, stream, min_warm_s=0.0, repeats=1)
+    prof_bwd = fab.profile_read()
+    fab.profile_enable(False)
+    fab.profile_reset()
     ms_fwd = time_loop(torch, step_fwd, args.steps, args.warmup, stream, args.min_warm_s)
 
     F_f, F_b = fwd_flops(s, causal), bwd_flops(s, causal)
     peak = PEAK_TFLOPS[mode]
     work = kernel_work(s, causal, mode, mask is not None)
-    kernels = {}
-    for name, (tot_ms, launches) in prof.items():
-        if not launches:
-            continue
-        ms = tot_ms / args.steps                       # per step (all launches of the kernel)
-        amount, kind = work[name]
-        if kind == "flop":
-            rate = amount / (ms * 1e-3) / 1e12
-            kernels[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
+
+    def per_kernel(pr, work):
+        out = {}
+        for name, (tot_ms, launches) in pr.items():
+            if not launches:
+                continue
+            ms = tot_ms / args.steps                       # per step (all launches of the kernel)
+            amount, kind = work[name]
+            if kind == "flop":
+                rate = amount / (ms * 1e-3) / 1e12
+                out[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
                              "achieved": round(rate, 2), "unit": "TFLOP/s", "frac": round(rate / peak, 4)}
-        else:
-            rate = amount / (ms * 1e-3) / 1e9
-            kernels[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
+            else:
+                rate = amount / (ms * 1e-3) / 1e9
+                out[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
                              "achieved": round(rate, 1), "unit": "GB/s", "frac": round(rate / HBM_GBS, 4)}
+        return out
+
+    kernels = per_kernel(prof, work)
+    # in the backward alone, "pack" is the launch that packs Q, K, V and builds the
+    # block map together with the prep of the supplied O and LSE (bf16), and "prep"
+    # is D alone (f32)
+    kernels_bwd = per_kernel(prof_bwd, dict(work, pack=work["pack_prep"]))
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dom_launch_ms = prof[dom][0] / prof[dom][1]
     dom_amount, dom_kind = work[dom]
@@ -333,7 +358,7 @@ def main():
         "frac_of_peak": round((F_f + F_b) / (ms_step * 1e-3) / 1e12 / peak, 4),
         "backward_only": {"ms": round(ms_bwd, 4), "tflops": round(F_b / (ms_bwd * 1e-3) / 1e12, 3),
                           "frac_of_peak": round(F_b / (ms_bwd * 1e-3) / 1e12 / peak, 4),
-                          "flops_counted": F_b},
+                          "flops_counted": F_b, "kernels": kernels_bwd},
         "forward_only": {"ms": round(ms_fwd, 4), "tflops": round(F_f / (ms_fwd * 1e-3) / 1e12, 3),
                          "frac_of_peak": round(F_f / (ms_fwd * 1e-3) / 1e12 / peak, 4)},
         "kernels": kernels,
