@@ -46,6 +46,8 @@ struct Plan {
     int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
     bool ds;       // bf16 mode: dQ from the stored dS^T tiles (else the recompute kernel)
+    int hpw;       // query heads per work-group of the dK/dV kernel (its partials per head unit)
+    bool part;     // dK/dV go through per-unit partials and the grouped-query reduction
 };
 
 // Shape checks: the asserts of "Function ggml_flash_attn_back" restated for the
@@ -106,7 +108,7 @@ int check_shape(const fab_shape *s, Plan *pl)
 //   stats      LSE / D blocks [B][H][Np/64][128]               (backward, bf16 mode)
 //   dqp, tick  dQ partials of split query blocks and counters  (backward, bf16 mode, dQ by recompute, few blocks)
 //   ds         bf16 dS^T tiles [B,H,Np/64,ceil(M/128)][128x64]  (backward, bf16 mode, dQ from dS)
-//   pk, pv     per-query-head dK / dV partials                 (backward, H > Hkv)
+//   pk, pv     dK / dV partials per head unit                  (backward, H > Hkv * hpw)
 // ws_fwd is the end of the part the forward alone uses.
 void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
 {
@@ -145,6 +147,8 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         off = align_up(off + sizeof(float) * qrows / 64 * 128);
     }
     pl->ds = mode == FAB_MODE_BF16 && fab::dq_from_ds(d, pl->np, pl->dkp, pl->dvp);
+    pl->hpw = mode == FAB_MODE_BF16 ? fab::bwd_heads_per_wg(d, pl->dkp, pl->dvp) : 1;
+    pl->part = d.H / d.Hkv / pl->hpw > 1;
     pl->ws_dqp = off;
     pl->ws_tick = off;
     pl->ws_ds = off;
@@ -157,10 +161,10 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     }
     pl->ws_pk = off;
     pl->ws_pv = off;
-    if (pl->gqa) {
-        off = align_up(off + sizeof(float) * (size_t)d.DK * d.M * d.H * d.B);
+    if (pl->part) {   // one partial per head unit of hpw query heads
+        off = align_up(off + sizeof(float) * (size_t)d.DK * d.M * (d.H / pl->hpw) * d.B);
         pl->ws_pv = off;
-        off = align_up(off + sizeof(float) * (size_t)d.DV * d.M * d.H * d.B);
+        off = align_up(off + sizeof(float) * (size_t)d.DV * d.M * (d.H / pl->hpw) * d.B);
     }
     pl->ws_bytes = off;
 }
@@ -514,15 +518,16 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
                                            pl.nv, pl.total, pl.d, s),
                    "prep launch");
     }
-    float *dk = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
-    float *dv = pl.gqa ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
+    float *dk = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
+    float *dv = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
     if (bf16) {
         FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, dst,
-                                                   pl.gqa ? 1 : 0, pl.np, pl.mp, pl.d, s),
+                                                   pl.part ? 1 : 0, pl.np, pl.mp, pl.d, s),
                    "backward launch");
         if (pl.ds)   // with the grouped-query reduction of dK and dV in the same launch
-            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.gqa ? dk : nullptr,
-                                                   blob + pl.off_k, pl.gqa ? dv : nullptr, blob + pl.off_v, pl.d, s),
+            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.part ? dk : nullptr,
+                                                   blob + pl.off_k, pl.part ? dv : nullptr, blob + pl.off_v, pl.hpw,
+                                                   pl.d, s),
                        "dQ launch");
         else
             FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
@@ -532,11 +537,11 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
         FAB_LAUNCH(kBwd, fab::launch_backward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
                                                   static_cast<const float *>(v), static_cast<const float *>(d), mk,
                                                   map, lseu, delta, scale, blob, dk, dv,
-                                                  pl.gqa ? 1 : 0, pl.d, s),
+                                                  pl.part ? 1 : 0, pl.d, s),
                    "backward launch");
     }
-    if (pl.gqa && !pl.ds) {
-        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, s),
+    if (pl.part && !pl.ds) {
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, pl.hpw, s),
                    "dK/dV reduce launch");
     }
     return FAB_OK;

@@ -433,10 +433,11 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
     return hipGetLastError();
 }
 
-hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s)
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+                             hipStream_t s)
 {
     ReduceJob j[2];
-    const int rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, j);
+    const int rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, hpw, j);
     const int64_t work = j[0].items + j[1].items;
     if (work == 0) return hipSuccess;
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);

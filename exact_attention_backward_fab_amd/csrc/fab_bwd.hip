@@ -67,6 +67,7 @@ struct KvArgs {
     // Pairs the block map skips are not written.
     __bf16 *ds;
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
+    int hpw;                        // query heads of one group per work-group (1 or 2), summed in registers
     int part_heads, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
@@ -113,19 +114,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t qo_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sQO;
 
-    // ---- work-group -> (key block, head): first key blocks first (under a causal
-    // mask they see the most queries); heads dealt to the XCDs in contiguous ranges
-    const int HB = p.H * p.B;
-    int kb, hb;
-    if (HB % 8 == 0) {
-        const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HB / 8;
+    // ---- work-group -> (key block, head unit of hpw query heads of one group): first
+    // key blocks first (under a causal mask they see the most queries); units dealt to
+    // the XCDs in contiguous ranges
+    const int hpu = p.H / p.hpw, HU = hpu * p.B;
+    int kb, hu;
+    if (HU % 8 == 0) {
+        const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HU / 8;
         kb = jj / per;
-        hb = xcd * per + jj % per;
+        hu = xcd * per + jj % per;
     } else {
-        kb = blockIdx.x / HB;
-        hb = blockIdx.x % HB;
+        kb = blockIdx.x / HU;
+        hu = blockIdx.x % HU;
     }
-    const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
+    const int hp = hu % hpu, b = hu / hpu, g = hp * p.hpw / (p.H / p.Hkv);
     const int key0 = kb * kKBC;
     const int mykey = key0 + 32 * kw + l32;  // this lane's key in the C layout of S and dP
     const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
@@ -160,10 +162,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
 
-    const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // first tile row of this head
-    const rsrc_t rq = make_rsrc(p.q16 + qhead * DKP, (uint32_t)(p.Np * DKP) * 2u);
-    const rsrc_t ro = make_rsrc(p.o16 + qhead * DVP, (uint32_t)(p.Np * DVP) * 2u);
-    const rsrc_t rs = make_rsrc(p.stats + qhead / 64 * kStatsTile, (uint32_t)(p.Np / 64 * kStatsTile) * 4u);
+    // the current head's Q and dO tiles and LSE/D blocks
+    rsrc_t rq, ro, rs;
+    auto set_head = [&](int hb) {
+        const size_t qhead = (size_t)hb * p.Np;   // first tile row of this head
+        rq = make_rsrc(p.q16 + qhead * DKP, (uint32_t)(p.Np * DKP) * 2u);
+        ro = make_rsrc(p.o16 + qhead * DVP, (uint32_t)(p.Np * DVP) * 2u);
+        rs = make_rsrc(p.stats + qhead / 64 * kStatsTile, (uint32_t)(p.Np / 64 * kStatsTile) * 4u);
+    };
 
     // copies of query step it into stage bf: Q and dO chunk columns split over the
     // waves, lanes 0-7 of each wave copy a quarter of the LSE/D block
@@ -185,115 +191,119 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     const int nqt = p.Np / kKBR;
-    for (int seg = 0; seg < nqt; seg += kKList) {
-        const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
-            return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
-                              key0 / kMapTile);
-        });
-        if (count == 0) continue;
-#pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-            if (i < count) issue(sList[i] >> 2, i);
-        for (int li = 0; li < count; ++li) {
-            wait_vm_steps<PER>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
-            __syncthreads();                                    // ... for every wave; stage li-1 is free
-            if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
-            const int e = sList[li];
-            const int it = e >> 2, cls = e & 3;
-            const int q0 = it * kKBR;
-            const char *Qb = sQO + (li % NS) * ST::kBytes;
-            const char *Ob = Qb + ST::kQ;
-            const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
+    for (int hh = 0; hh < p.hpw; ++hh) {
+        const int hb = hp * p.hpw + hh + p.H * b;   // this head (h + H b)
+        set_head(hb);
+        for (int seg = 0; seg < nqt; seg += kKList) {
+            const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
+                return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
+                                  key0 / kMapTile);
+            });
+            if (count == 0) continue;
+    #pragma unroll
+            for (int i = 0; i < NS - 1; ++i)
+                if (i < count) issue(sList[i] >> 2, i);
+            for (int li = 0; li < count; ++li) {
+                wait_vm_steps<PER>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
+                __syncthreads();                                    // ... for every wave; stage li-1 is free
+                if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
+                const int e = sList[li];
+                const int it = e >> 2, cls = e & 3;
+                const int q0 = it * kKBR;
+                const char *Qb = sQO + (li % NS) * ST::kBytes;
+                const char *Ob = Qb + ST::kQ;
+                const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
 
-            // ---- S = Q K^T and dP = dO V^T for this wave's 32 queries (lane = key)
-            f32x16 sacc = zero16(), pacc = zero16();
-            {
-                bf16x8 a[DKP / 16];
-#pragma unroll
-                for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
-#pragma unroll
-                for (int t = 0; t < DKP / 16; ++t) sacc = mfma_bf16(a[t], lds_row8(Krow + 2304 * t), sacc);
-                bf16x8 o[DVP / 16];
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) pacc = mfma_bf16(o[t], lds_row8(Vrow + 2304 * t), pacc);
-            }
-
-            // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
-            // every key visible folds the scale into the exponent
-            const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
-            const float mul = fast ? sl2 : 1.f;
-            const int qb = q0 + 32 * qq;   // first query of this wave's half
-            if (!fast) {
-                const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float x = sacc[r] * sl2 + kbias;
-                    sacc[r] = (qb + crow(r, half) >= thr) ? x : -INFINITY;
+                // ---- S = Q K^T and dP = dO V^T for this wave's 32 queries (lane = key)
+                f32x16 sacc = zero16(), pacc = zero16();
+                {
+                    bf16x8 a[DKP / 16];
+    #pragma unroll
+                    for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
+    #pragma unroll
+                    for (int t = 0; t < DKP / 16; ++t) sacc = mfma_bf16(a[t], lds_row8(Krow + 2304 * t), sacc);
+                    bf16x8 o[DVP / 16];
+    #pragma unroll
+                    for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
+    #pragma unroll
+                    for (int t = 0; t < DVP / 16; ++t) pacc = mfma_bf16(o[t], lds_row8(Vrow + 2304 * t), pacc);
                 }
-                if (cls == kTileMixed) {
-                    const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
-#pragma unroll
+
+                // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
+                // every key visible folds the scale into the exponent
+                const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
+                const float mul = fast ? sl2 : 1.f;
+                const int qb = q0 + 32 * qq;   // first query of this wave's half
+                if (!fast) {
+                    const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
+    #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int n = min(qb + crow(r, half), p.N - 1);
-                        sacc[r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
+                        const float x = sacc[r] * sl2 + kbias;
+                        sacc[r] = (qb + crow(r, half) >= thr) ? x : -INFINITY;
+                    }
+                    if (cls == kTileMixed) {
+                        const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int n = min(qb + crow(r, half), p.N - 1);
+                            sacc[r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
+                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int qr = 32 * qq + 8 * r4 + 4 * half;
-                const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(Sb + qr);
-                const f32x4 del4 = *reinterpret_cast<const f32x4 *>(Sb + 64 + qr);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int r = 4 * r4 + c;
-                    const float P = fast_exp2(__builtin_fmaf(sacc[r], mul, -lse4[c]));
-                    sacc[r] = P;
-                    pacc[r] = P * (pacc[r] - del4[c]);
+    #pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int qr = 32 * qq + 8 * r4 + 4 * half;
+                    const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(Sb + qr);
+                    const f32x4 del4 = *reinterpret_cast<const f32x4 *>(Sb + 64 + qr);
+    #pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * r4 + c;
+                        const float P = fast_exp2(__builtin_fmaf(sacc[r], mul, -lse4[c]));
+                        sacc[r] = P;
+                        pacc[r] = P * (pacc[r] - del4[c]);
+                    }
                 }
-            }
 
-            // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
-            // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
-            bf16x8 pa[2], da[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float pv[8], dv8[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    pv[i] = sacc[8 * u + i];
-                    dv8[i] = pacc[8 * u + i];
+                // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
+                // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
+                bf16x8 pa[2], da[2];
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float pv[8], dv8[8];
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        pv[i] = sacc[8 * u + i];
+                        dv8[i] = pacc[8 * u + i];
+                    }
+                    pa[u] = to_bf16x8(pv);
+                    da[u] = to_bf16x8(dv8);
                 }
-                pa[u] = to_bf16x8(pv);
-                da[u] = to_bf16x8(dv8);
+                if (p.ds) {
+                    // the dS^T operands of this step, for dQ = scale dS K: stored before the
+                    // products so that the stores complete behind them (the next step's
+                    // vmcnt wait counts them too); streaming stores, which leave the L2 to
+                    // the Q and dO tiles this kernel re-reads
+                    __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
+                                        (kw >> 1) * 2 + (it & 1)) * 4096 +
+                                (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8;
+                    __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
+                    __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));
+                }
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    bf16x8 bo[DVP / 32], bq[DKP / 32];
+    #pragma unroll
+                    for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
+    #pragma unroll
+                    for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa[u], bo[dt], dvacc[dt]);
+    #pragma unroll
+                    for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
+    #pragma unroll
+                    for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da[u], bq[dt], dkacc[dt]);
+                }
             }
-            if (p.ds) {
-                // the dS^T operands of this step, for dQ = scale dS K: stored before the
-                // products so that the stores complete behind them (the next step's
-                // vmcnt wait counts them too); streaming stores, which leave the L2 to
-                // the Q and dO tiles this kernel re-reads
-                __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
-                                    (kw >> 1) * 2 + (it & 1)) * 4096 +
-                            (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8;
-                __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
-                __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bf16x8 bo[DVP / 32], bq[DKP / 32];
-#pragma unroll
-                for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
-#pragma unroll
-                for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa[u], bo[dt], dvacc[dt]);
-#pragma unroll
-                for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
-#pragma unroll
-                for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da[u], bq[dt], dkacc[dt]);
-            }
+            __syncthreads();   // every wave is done with the stages before they are refilled
         }
-        __syncthreads();   // every wave is done with the stages before they are refilled
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the K/V copies, also with no live step
 
@@ -329,8 +339,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int r = 0; r < 16; ++r) dvacc[dt][r] += xch[(16 * dt + r) * 64 + lane];
     }
 
-    // ---- store dK (scaled) and dV of this key block
-    const int hdd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
+    // ---- store dK (scaled) and dV of this key block: per head unit (partials) or,
+    // when a unit covers the whole group, into the result
+    const int hdd = p.part_heads ? hp : g, Hd = p.part_heads ? hpu : p.Hkv;
     float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
     float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
 #pragma unroll
@@ -899,7 +910,8 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else if constexpr (DKP + DVP <= 256) {
-        hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT), 0, s, a);
+        hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B), dim3(kKNT), 0,
+                           s, a);
         return hipGetLastError();
     } else {
         hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT4), 0, s,
@@ -937,6 +949,9 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     KvArgs a;
     a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.dk = dk; a.dv = dv; a.ds = ds; a.nkb128 = ceil_div(d.M, 128);
+    a.hpw = bwd_heads_per_wg(d, hd.dk, hd.dv);
+    // partials only while a head unit is smaller than its group
+    if (part_heads != (d.H / d.Hkv / a.hpw > 1 ? 1 : 0)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;

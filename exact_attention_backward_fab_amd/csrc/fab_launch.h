@@ -145,10 +145,22 @@ inline bool dq_from_ds(const Dims &d, int Np, int dkp, int dvp)
     return dkp + dvp <= 256 && ds_bytes(d, Np) <= kDsMaxBytes;
 }
 
+// Query heads per work-group of the bf16 dK/dV kernel (1 or 2): two heads of one
+// group share a work-group, their dK/dV summed in registers, when the one-head grid
+// has at least four rounds of work-groups on the 256 CUs (the grouped-query
+// partials and the per-work-group set-up then halve at no cost in balance).
+inline int bwd_heads_per_wg(const Dims &d, int dkp, int dvp)
+{
+    const int rk2 = d.H / d.Hkv;
+    return (dkp + dvp <= 256 && rk2 % 2 == 0 && (int64_t)((d.M + 127) / 128) * d.H * d.B >= 1024) ? 2 : 1;
+}
+
 // Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
 // (launch_pack_prep_bf16 or the forward of launch_forward_prep_bf16, Np rows per head), K, V (Mp rows per head)
-// and the LSE/D blocks; stored as in launch_backward_f32.  With ds (dq_from_ds
-// shapes only) it also stores the dS^T tiles of every pair it visits.
+// and the LSE/D blocks.  With part_heads, per head unit of hpw = bwd_heads_per_wg
+// query heads into dk/dv [D,M,H/hpw,B] partials; else (a unit covers its group)
+// into dk/dv [D,M,Hkv,B].  With ds (dq_from_ds shapes only) it also stores the
+// dS^T tiles of every pair it visits.
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
                                 float *dv, __bf16 *ds, int part_heads, int Np, int Mp, const Dims &d, hipStream_t s);
@@ -158,7 +170,7 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
 // also runs the grouped-query reduction of launch_gqa_reduce (extra work-groups
 // that take the CU slots the short query blocks free).
 hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
-                             int Mp, const float *pk, float *dk, const float *pv, float *dv, const Dims &d,
+                             int Mp, const float *pk, float *dk, const float *pv, float *dv, int hpw, const Dims &d,
                              hipStream_t s);
 
 // dQ work split.  Query blocks have kDqBlock rows.  A grid of at most
@@ -190,8 +202,10 @@ struct ReduceJob {
     int vec;         // chunk % 4 == 0: float4 items
     int64_t items;   // work items (float4 or float) over all groups
 };
-// Fills the two jobs; returns rk2 = H / Hkv.
-inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, ReduceJob j[2])
+// Fills the two jobs for partials of hpw query heads each; returns the partials
+// per group, H / Hkv / hpw.
+inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+                           ReduceJob j[2])
 {
     const int64_t groups = (int64_t)d.Hkv * d.B;
     const float *part[2] = {pk, pv};
@@ -204,11 +218,12 @@ inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *d
         j[t].vec = (j[t].chunk % 4 == 0);
         j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;
     }
-    return d.H / d.Hkv;
+    return d.H / d.Hkv / hpw;
 }
 
 // The reduction above, one launch.
-hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, hipStream_t s);
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+                             hipStream_t s);
 
 // Fill n floats with zero.
 hipError_t launch_zero(float *p, int64_t n, hipStream_t s);

@@ -134,6 +134,11 @@ SMALL = [
     # 128 is above its two-share split's limit (512), so it runs one work-group per
     # block (the other 192-wide cases here are split)
     ("dq_unsplit_528_blocks", Shape(1, 33, 3, 2000, 200, 192, 128), "causal", 49),
+    # 16 key blocks x 64 (batch, head) pairs = 1024 work-groups: the bf16 dK/dV kernel
+    # takes two query heads of a group per work-group; with 2 heads per group a unit is
+    # the whole group (dK/dV straight into the result), with 4 two partials per group
+    ("two_heads_per_wg_group_of_2", Shape(4, 16, 8, 100, 2048, 64, 64), "random", 50),
+    ("two_heads_per_wg_group_of_4", Shape(2, 32, 8, 70, 2048, 128, 128), None, 51),
 ]
 
 
