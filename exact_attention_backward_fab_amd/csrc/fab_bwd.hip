@@ -12,10 +12,12 @@
 // matrix cores: bf16 operands with f32 accumulation (v_mfma_f32_32x32x16_bf16)
 // or f32 operands (v_mfma_f32_32x32x2_f32).
 //
-// dQ = scale dS K: in bf16 mode a separate query-block-outer kernel
-// (fab_qouter.hip) recomputes S and dP by query blocks and writes each dQ row
-// once; in f32 mode this kernel adds every key block's share with f32 atomics
-// into the result blob.
+// dQ = scale dS K: in bf16 mode this kernel stores the bf16 dS^T operands of
+// its dK product, and a query-outer kernel (fab_qouter.hip) forms dQ from them
+// as a plain product, writing each dQ row once (for the 192-wide heads and for
+// shapes whose dS would pass 4 GiB that kernel recomputes S and dP instead); in
+// f32 mode this kernel adds every key block's share with f32 atomics into the
+// result blob.
 //
 // Wave layout: a wave owns 32 keys of the block (the bf16 kernel: 8 waves, 4
 // key sub-blocks x 2 query halves of each 64-query step; the f32 and the wide-head

@@ -8,13 +8,18 @@
 //                          it stores no O but, from the O in registers, the
 //                          inputs of the backward kernels: D = rowsum(dO o O),
 //                          the bf16 Q and dO tiles and the LSE/D blocks
-//   dq_bf16_kernel         dQ = scale dS K by query blocks: a work-group owns 128
-//                          queries of one (batch, head) and streams the key
-//                          blocks that see them (block map), recomputing
-//                          S^T = K Q^T and dP^T = V dO^T on the matrix cores,
-//                          P = exp(scale S + mask - LSE), dS = P o (dP - D)
-//                          (labml "Flash Attention", "Backward pass"), and
-//                          accumulating dQ in registers.  Every dQ element is
+//   dq_ds_kernel           dQ = scale dS K from the bf16 dS^T tiles the dK/dV
+//                          kernel stores: a memory-bound product by pairs of
+//                          query steps, each dQ element written once; the same
+//                          launch runs the grouped-query reduction of dK and dV
+//   dq_bf16_kernel         dQ = scale dS K by query blocks without stored dS (the
+//                          192-wide heads, and shapes whose dS would pass 4 GiB):
+//                          a work-group owns 128 queries of one (batch, head) and
+//                          streams the key blocks that see them (block map),
+//                          recomputing S^T = K Q^T and dP^T = V dO^T on the
+//                          matrix cores, P = exp(scale S + mask - LSE), dS = P o
+//                          (dP - D) (labml "Flash Attention", "Backward pass"),
+//                          and accumulating dQ in registers.  Every dQ element is
 //                          written once; no atomics on dQ.  Small grids run each
 //                          query block as two work-groups on alternate key steps
 //                          whose partial sums meet through a per-block counter.
@@ -58,7 +63,7 @@ __device__ __forceinline__ QWork qouter_work(int bid, int nqt, int HB, int fold 
     return r;
 }
 
-// Work-group -> (query block index for qouter_work, share) of the dQ kernel.
+// Work-group -> (query block index for qouter_work, share) of the recompute dQ kernel.
 // With split == 2 each query block is run by two work-groups (shares) that take
 // alternate live key steps; the shares of a block are 8 work-groups apart, so
 // the round-robin dispatch over the XCDs puts them on one XCD, one shortly after
