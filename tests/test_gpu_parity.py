@@ -478,6 +478,55 @@ def sample_ids(s, wid, rng):
     return np.array(rows, dtype=np.int64), np.array(keys, dtype=np.int64)
 
 
+def test_bf16_large_shape_recomputes_dq(torch_dev):
+    """Head dims up to 128 whose bf16 dS tiles would pass 4 GiB (here 5.4 GB; the tiles
+    are dense over all pairs, whatever the mask) take dQ from the recompute kernel, the
+    grouped-query reduction as its own launch, and (groups of 10, 4608 work-groups) two
+    query heads per dK/dV work-group.  A causal mask with M > N keeps the oracle cheap:
+    sampled rows, keys just below N and keys past N (exactly zero), and sums that hold
+    at any size."""
+    torch, dev = torch_dev
+    from oracle import oracle as orc
+    fab = fabmod()
+    s = Shape(1, 40, 4, 4096, 16384, 64, 64)
+    print(f"[parity] large recompute {s}", flush=True)
+    assert 2 * s.B * s.H * s.N * s.M > 4 << 30
+    q, k, v, d = make_qkvd(s, 52)
+    mask = causal_mask(s.N, s.M)
+    scale = float(np.float32(1 / math.sqrt(s.DK)))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    blob = fab.backward(*t, scale, mask=to_dev(torch, dev, mask), mode="bf16")
+    torch.cuda.synchronize()
+    blob = blob.cpu().numpy()
+    _, off_k, off_v, total = fab.blob_layout(fab.Shape(*s.astuple()))
+    nq, nk, nv = q.size, k.size, v.size
+    assert np.all(np.isfinite(blob))
+    dq = blob[:nq].reshape(s.q_shape)
+    dk = blob[off_k:off_k + nk].reshape(s.k_shape)
+    dv = blob[off_v:off_v + nv].reshape(s.v_shape)
+    assert np.all(dk[:, :, s.N:] == 0) and np.all(dv[:, :, s.N:] == 0)   # keys no query sees
+    rng = np.random.default_rng(152)
+    rows = np.concatenate([rng.choice(s.B * s.H * s.N, 24, replace=False), [0, s.B * s.H * s.N - 1]])
+    keys = [int(m + s.M * g) for g in range(s.Hkv) for m in rng.choice(np.arange(s.N - 256, s.N), 3, replace=False)]
+    keys += [s.N + 5, s.M - 1]
+    rdq, rdk, rdv = orc.backward_sampled(s, q, k, v, mask, d, scale, rows, keys)
+    gdq = np.stack([dq[r // (s.N * s.H), (r // s.N) % s.H, r % s.N] for r in rows])
+    gdk = np.stack([dk[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
+    gdv = np.stack([dv[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
+    for name, got, ref in (("dq", gdq, rdq), ("dk", gdk, rdk), ("dv", gdv, rdv)):
+        e = rel_err(got, ref)
+        print(f"  sampled {name} max-rel {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], name
+    # sum_m dK[:, m] = 0 per group; sum_m dV[:, m] = the group's sum of d over all rows
+    tol = TOL["bf16"]
+    dk_sum = dk.astype(np.float64).sum(axis=2)
+    assert np.max(np.abs(dk_sum) / np.abs(dk.astype(np.float64)).sum(axis=2)) <= tol
+    rk2 = s.H // s.Hkv
+    expect = d.astype(np.float64).sum(axis=1).reshape(s.B, s.Hkv, rk2, s.DV).sum(axis=2)
+    got = dv.astype(np.float64).sum(axis=2)
+    assert np.max(np.abs(got - expect)) <= tol * np.max(np.abs(dv.astype(np.float64)).sum(axis=2))
+
+
 WL_CASES = [(1, "f32"), (2, "f32"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (5, "f32"), (5, "bf16")]
 
 
