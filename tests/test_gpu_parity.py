@@ -139,6 +139,9 @@ SMALL = [
     # the whole group (dK/dV straight into the result), with 4 two partials per group
     ("two_heads_per_wg_group_of_2", Shape(4, 16, 8, 100, 2048, 64, 64), "random", 50),
     ("two_heads_per_wg_group_of_4", Shape(2, 32, 8, 70, 2048, 128, 128), None, 51),
+    # 128 key blocks x 10 heads: two heads per work-group, 5 head units (not a multiple
+    # of the 8 XCDs: the plain work-group order)
+    ("two_heads_per_wg_5_units", Shape(1, 10, 5, 64, 16384, 64, 64), "random", 53),
 ]
 
 
