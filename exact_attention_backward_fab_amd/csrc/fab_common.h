@@ -268,8 +268,9 @@ __device__ __forceinline__ void query_block_work(int bid, int nqt, int HB, int f
 }
 
 // ---------------------------------------------------------------- grouped-query reduction
-// Item i of a ReduceJob (fab_launch.h): the sum of the rk2 query-head partials of
-// one float4 (or float) of a key/value head's dK or dV slice, in head order.
+// Item i of a ReduceJob (fab_launch.h): the sum of the rk2 partials of a group
+// (one per head unit) of one float4 (or float) of a key/value head's dK or dV
+// slice, in head order.
 __device__ __forceinline__ void reduce_item(const ReduceJob &r, int rk2, int64_t i)
 {
     if (r.vec) {
