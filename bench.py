@@ -2,32 +2,30 @@
 """Benchmark of the exact attention backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--mode bf16]
+    python bench.py --only backward|whole|forward ...   (one timed loop, for profilers)
 
-A step is one pass of the whole path over one batch of resident inputs: one
-fab_backward call with O and LSE left to the library (the op's own semantics:
-mask block map, bf16 copies of K and V, forward with row LSE, D = rowsum(dO o
-O), the key-block-outer dK/dV kernel, the query-block-outer dQ kernel, the
-grouped-query reduction and the blob packing).  `value` counts the work that
-pass must do: forward 2*N*M*(DK+DV)*H*B plus the backward 10*N*M*(DK+DV)/2*H*B,
-each halved under a causal mask, over K steps timed with two HIP events on the
-launch stream and nothing else in between (after at least W warm-up steps and
-1 s of warm-up; the median of three such runs, the fastest run beside it).  The same K steps are then run
-again with every kernel bracketed by HIP events (which adds gaps between the
-kernels: `ms_per_step_with_kernel_events`) for every kernel's time per step
-and its algorithmic rate (TFLOP/s for the matrix-core kernels, GB/s for the
-memory-bound ones) and the `roofline` object of the dominant kernel.  The line
-also reports the backward alone (O and LSE supplied by a prior forward, the
-usual training convention; with its own per-kernel breakdown, whose "pack" is
-the one launch that packs Q, K, V and preps d, O and the LSE) and the forward
-alone, and (`other_workloads`,
---also) the whole step and the backward alone of further workloads, by
-default the long-context one.  Causal workloads are also timed with the causal
-rule passed as a flag instead of the mask tensor (`causal_flag_instead_of_mask`:
-same result, no block map or mask reads), bf16 mode with q, k, v, d stored
-as bf16 (`bf16_inputs`: the values the matrix cores read), and the other
-arithmetic mode on the same workload (`other_mode`: f32 operands on the f32
-matrix cores, priced against the f32 peak).  `cpu_baseline` times the
-f64 CPU oracle on a bounded sample of the same workload on this host's cores.
+A step is one fab_backward call over one batch of resident inputs with O and the
+row LSE supplied by a prior fab_forward_lse (the usual training convention): the
+pack of Q, K, V to bf16 tiles with the block map of the mask and the prep of d, O
+and the LSE (D = rowsum(dO o O)), the key-block-outer dK/dV kernel, the dQ kernel,
+the grouped-query reduction and the blob packing.  `value` counts the backward's
+work, 10*N*M*(DK+DV)/2*H*B (halved under a causal mask), over K steps timed with
+two HIP events on the launch stream and nothing else in between (after at least W
+warm-up steps and 1 s of warm-up; the median of three such runs, the fastest run
+beside it), and `frac_of_peak` prices it against the dense matrix-core peak of the
+mode.  The same K steps are then run again with every kernel bracketed by HIP
+events on its launch stream (which adds gaps between the kernels) for every
+kernel's time and algorithmic rate (TFLOP/s for the matrix-core kernels, GB/s for
+the memory-bound ones) and the `roofline` object of the dominant kernel.
+
+Beside it: `whole_path`, the op's own semantics (O = lse = NULL: the forward runs
+inside fab_backward, counted as forward plus backward flops); `forward_only`;
+causal workloads with the causal rule passed as a flag instead of the mask tensor
+(`causal_flag_instead_of_mask`); bf16 mode with q, k, v, d stored as bf16
+(`bf16_inputs`); and `configs`: every other (workload, mode) pair of the five
+workloads, each with its backward alone (and kernel split), whole path and
+fraction of its mode's peak.  `cpu_baseline` times the f64 CPU oracle on a
+bounded sample of the headline workload on this host's cores.
 
 Prints exactly one JSON line.
 """
@@ -100,7 +98,7 @@ def kernel_work(s, causal, mode, has_mask):
                     if s.DK <= a and s.DV <= b)
     mp = (s.M + 63) // 64 * 64
     np_ = (s.N + 63) // 64 * 64
-    dq_from_ds = bf16 and dkp + dvp <= 256 and s.B * s.H * (np_ // 64) * math.ceil(s.M / 128) * 16384 <= 4 << 30
+    dq_from_ds = bf16 and dkp + dvp <= 256 and s.B * s.H * (np_ // 64) * math.ceil(s.M / 128) * 16384 < 4 << 30
     w = {
         # S = Q K^T and O = P V
         "forward": (2.0 * pairs * (s.DK + s.DV), "flop"),
@@ -144,8 +142,12 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, choices=sorted(fi.WORKLOADS))
     ap.add_argument("--mode", default=None, choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--also", default="4",
-                    help="comma-separated workloads also timed (whole step and backward alone), '' for none")
+    ap.add_argument("--configs", default="all",
+                    help="(workload:mode) pairs also timed, comma-separated, e.g. '2:f32,5:bf16'; "
+                         "'all' for every pair the five workloads list, '' for none")
+    ap.add_argument("--only", default=None, choices=["backward", "whole", "forward"],
+                    help="run only the warm-up and K timed steps of one call (backward alone, whole path "
+                         "or forward) and print its time: the command profilers wrap")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--min-warm-s", type=float, default=1.0,
                     help="warm-up of every timed loop lasts at least this long (seconds of GPU work)")
@@ -186,8 +188,9 @@ def cpu_baseline(s, q, k, v, d, mask, scale, causal, budget_s):
     """The oracle, as it stands, on a bounded sample of the workload: whole
     key/value groups (b, g) with all their H/Hkv query heads, as many as fit the
     time budget (all of them when they do), else the first queries of group 0.
-    Counted like `value`: forward plus backward flops of the (query, key) pairs
-    attended."""
+    Counted like `value`: the backward's flops of the (query, key) pairs attended
+    (the oracle also recomputes the forward it needs, as the GPU path's supplied O
+    and LSE spare it)."""
     from oracle import oracle as orc
     rk2 = s.H // s.Hkv
     cores = orc.default_threads()
@@ -224,13 +227,94 @@ def cpu_baseline(s, q, k, v, d, mask, scale, causal, budget_s):
     else:
         pairs = n_keep * s.M
     pairs *= rk2 * len(units)
-    flops = pairs * (2.0 * (s.DK + s.DV) + 5.0 * (s.DK + s.DV))
+    flops = pairs * 5.0 * (s.DK + s.DV)   # the backward's count per attended pair, as `value`
     what = (f"{len(units)} of {len(units) if n_keep < s.N else s.B * s.Hkv} key/value groups" if n_keep == s.N
             else f"key/value group 0, queries 0..{n_keep - 1} of {s.N}")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"{what} ({rk2} query heads each, all {s.M} keys); f64 forward + backward, "
-                      f"counted as the forward plus the backward flops of the attended pairs"}
+            "sample": f"{what} ({rk2} query heads each, all {s.M} keys); f64 forward recompute + backward, "
+                      f"counted as `value` counts the backward: 10*(DK+DV)/2 flops per attended pair"}
+
+
+def per_kernel(pr, work, steps, peak):
+    out = {}
+    for name, (tot_ms, launches) in pr.items():
+        if not launches:
+            continue
+        ms = tot_ms / steps                            # per step (all launches of the kernel)
+        amount, kind = work[name]
+        if kind == "flop":
+            rate = amount / (ms * 1e-3) / 1e12
+            out[name] = {"ms": round(ms, 4), "launches_per_step": launches // steps,
+                         "achieved": round(rate, 2), "unit": "TFLOP/s", "frac": round(rate / peak, 4)}
+        else:
+            rate = amount / (ms * 1e-3) / 1e9
+            out[name] = {"ms": round(ms, 4), "launches_per_step": launches // steps,
+                         "achieved": round(rate, 1), "unit": "GB/s", "frac": round(rate / HBM_GBS, 4)}
+    return out
+
+
+def profiled(torch, fab, fn, steps, stream):
+    """The same steps once more with every kernel bracketed by HIP events on its
+    launch stream: {kernel: (total_ms, launches)} and the step time of that pass."""
+    fab.profile_reset()
+    fab.profile_enable(True)
+    ms = time_loop(torch, fn, steps, 0, stream, min_warm_s=0.0, repeats=1)
+    pr = fab.profile_read()
+    fab.profile_enable(False)
+    fab.profile_reset()
+    return pr, ms
+
+
+class Case:
+    """Device inputs and buffers of one (workload, mode) pair, and its three calls."""
+
+    def __init__(self, torch, fab, dev, wid, mode):
+        w = fi.WORKLOADS[wid]
+        self.w, self.mode, self.causal = w, mode, w.mask == "causal"
+        s, q, k, v, d, mask, scale = fi.workload_inputs(wid)
+        self.s, self.scale, self.host = s, scale, (q, k, v, d, mask)
+        self.t = [torch.from_numpy(x).to(dev) for x in (q, k, v, d)]
+        self.tm = None if mask is None else torch.from_numpy(mask.view(np.int16)).to(dev)
+        self.fs = fab.Shape(*s.astuple())
+        self.blob = torch.empty(fab.blob_layout(self.fs)[3], dtype=torch.float32, device=dev)
+        self.O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
+        self.ws_full, _ = fab.alloc_workspace(self.fs, mode, self.tm is not None, False, dev)
+        self.ws_bwd, _ = fab.alloc_workspace(self.fs, mode, self.tm is not None, True, dev)
+        self.fab = fab
+        self.fwd()
+
+    def fwd(self):
+        t = self.t
+        self.fab.forward_lse(t[0], t[1], t[2], self.scale, mask=self.tm, mode=self.mode, O=self.O, lse=self.lse,
+                             ws=self.ws_bwd)
+
+    def bwd(self):
+        self.fab.backward(*self.t, self.scale, mask=self.tm, mode=self.mode, O=self.O, lse=self.lse, blob=self.blob,
+                          ws=self.ws_bwd)
+
+    def whole(self):
+        self.fab.backward(*self.t, self.scale, mask=self.tm, mode=self.mode, blob=self.blob, ws=self.ws_full)
+
+    def flops(self):
+        return fwd_flops(self.s, self.causal), bwd_flops(self.s, self.causal)
+
+
+def pair_summary(torch, fab, c, args, stream):
+    """Backward alone (with its kernel split), whole path and forward of one pair."""
+    F_f, F_b = c.flops()
+    peak = PEAK_TFLOPS[c.mode]
+    ms_b = time_loop(torch, c.bwd, args.steps, args.warmup, stream, args.min_warm_s)
+    pr, _ = profiled(torch, fab, c.bwd, args.steps, stream)
+    ms_w = time_loop(torch, c.whole, args.steps, args.warmup, stream, args.min_warm_s)
+    work = kernel_work(c.s, c.causal, c.mode, c.tm is not None)
+    return {"workload": c.w.name, "mode": c.mode, "peak": peak,
+            "backward_only": {"ms": round(ms_b, 4), "tflops": round(F_b / (ms_b * 1e-3) / 1e12, 3),
+                              "frac_of_peak": round(F_b / (ms_b * 1e-3) / 1e12 / peak, 4),
+                              "kernels": per_kernel(pr, dict(work, pack=work["pack_prep"]), args.steps, peak)},
+            "whole_path": {"ms": round(ms_w, 4), "tflops": round((F_f + F_b) / (ms_w * 1e-3) / 1e12, 3),
+                           "frac_of_peak": round((F_f + F_b) / (ms_w * 1e-3) / 1e12 / peak, 4)}}
 
 
 def main():
@@ -242,30 +326,22 @@ def main():
     import torch
     import exact_attention_backward_fab_amd as fab
 
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
     w = fi.WORKLOADS[args.workload]
     mode = args.mode or ("bf16" if "bf16" in w.modes else w.modes[0])
-    causal = w.mask == "causal"
-    s, q, k, v, d, mask, scale = fi.workload_inputs(args.workload)
-    dev = torch.device("cuda:0")
-    tq, tk, tv, td = (torch.from_numpy(x).to(dev) for x in (q, k, v, d))
-    tm = None if mask is None else torch.from_numpy(mask.view(np.int16)).to(dev)
-    fs = fab.Shape(*s.astuple())
-    total = fab.blob_layout(fs)[3]
-    blob = torch.empty(total, dtype=torch.float32, device=dev)
-    O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
-    lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
-    ws_full, _ = fab.alloc_workspace(fs, mode, tm is not None, False, dev)
-    ws_bwd, _ = fab.alloc_workspace(fs, mode, tm is not None, True, dev)
-    stream = torch.cuda.current_stream()
+    c = Case(torch, fab, dev, args.workload, mode)
+    s, causal = c.s, c.causal
+    F_f, F_b = c.flops()
+    peak = PEAK_TFLOPS[mode]
 
-    def step_full():
-        fab.backward(tq, tk, tv, td, scale, mask=tm, mode=mode, blob=blob, ws=ws_full)
-
-    def step_bwd():
-        fab.backward(tq, tk, tv, td, scale, mask=tm, mode=mode, O=O, lse=lse, blob=blob, ws=ws_bwd)
-
-    def step_fwd():
-        fab.forward_lse(tq, tk, tv, scale, mask=tm, mode=mode, O=O, lse=lse, ws=ws_bwd)
+    if args.only:
+        fn, flops = {"backward": (c.bwd, F_b), "whole": (c.whole, F_f + F_b), "forward": (c.fwd, F_f)}[args.only]
+        ms = time_loop(torch, fn, args.steps, args.warmup, stream, args.min_warm_s, repeats=1)
+        print(json.dumps({"only": args.only, "workload": w.name, "mode": mode, "steps": args.steps,
+                          "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3)}),
+              flush=True)
+        return
 
     if args.calib_copy:
         a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
@@ -274,62 +350,27 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # ---- timed region: the whole path, K steps with nothing but the launches
-    st_step, st_bwd = {}, {}
-    ms_step = time_loop(torch, step_full, args.steps, args.warmup, stream, args.min_warm_s, stats=st_step)
-    # ---- the same K steps again with every kernel bracketed by HIP events on its
-    # launch stream: per-kernel durations (the event records add gaps between the
-    # kernels, so this pass is not the one `value` is taken from)
-    fab.profile_reset()
-    fab.profile_enable(True)
-    ms_step_prof = time_loop(torch, step_full, args.steps, 0, stream, min_warm_s=0.0, repeats=1)
-    prof = fab.profile_read()
-    fab.profile_enable(False)
-    fab.profile_reset()
+    # ---- timed region: the backward alone, K steps with nothing but its launches
+    st_bwd, st_whole = {}, {}
+    ms_bwd = time_loop(torch, c.bwd, args.steps, args.warmup, stream, args.min_warm_s, stats=st_bwd)
+    # ---- the same K steps with every kernel bracketed by HIP events (per-kernel times)
+    prof_bwd, ms_bwd_prof = profiled(torch, fab, c.bwd, args.steps, stream)
+    # ---- the whole path (forward inside the call) and the forward alone
+    ms_whole = time_loop(torch, c.whole, args.steps, args.warmup, stream, args.min_warm_s, stats=st_whole)
+    prof_whole, _ = profiled(torch, fab, c.whole, args.steps, stream)
+    ms_fwd = time_loop(torch, c.fwd, args.steps, args.warmup, stream, args.min_warm_s)
 
-    # ---- the backward alone (O, LSE from a prior forward) and the forward alone
-    step_fwd()
-    torch.cuda.synchronize()
-    ms_bwd = time_loop(torch, step_bwd, args.steps, args.warmup, stream, args.min_warm_s, stats=st_bwd)
-    # per-kernel durations of the backward alone (events around every launch, as above)
-    fab.profile_reset()
-    fab.profile_enable(True)
-    time_loop(torch, step_bwd, args.steps, 0, stream, min_warm_s=0.0, repeats=1)
-    prof_bwd = fab.profile_read()
-    fab.profile_enable(False)
-    fab.profile_reset()
-    ms_fwd = time_loop(torch, step_fwd, args.steps, args.warmup, stream, args.min_warm_s)
-
-    F_f, F_b = fwd_flops(s, causal), bwd_flops(s, causal)
-    peak = PEAK_TFLOPS[mode]
-    work = kernel_work(s, causal, mode, mask is not None)
-
-    def per_kernel(pr, work):
-        out = {}
-        for name, (tot_ms, launches) in pr.items():
-            if not launches:
-                continue
-            ms = tot_ms / args.steps                       # per step (all launches of the kernel)
-            amount, kind = work[name]
-            if kind == "flop":
-                rate = amount / (ms * 1e-3) / 1e12
-                out[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
-                             "achieved": round(rate, 2), "unit": "TFLOP/s", "frac": round(rate / peak, 4)}
-            else:
-                rate = amount / (ms * 1e-3) / 1e9
-                out[name] = {"ms": round(ms, 4), "launches_per_step": launches // args.steps,
-                             "achieved": round(rate, 1), "unit": "GB/s", "frac": round(rate / HBM_GBS, 4)}
-        return out
-
-    kernels = per_kernel(prof, work)
-    # in the backward alone, "pack" is the launch that packs Q, K, V and builds the
-    # block map together with the prep of the supplied O and LSE (bf16), and "prep"
-    # is D alone (f32)
-    kernels_bwd = per_kernel(prof_bwd, dict(work, pack=work["pack_prep"]))
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    dom_launch_ms = prof[dom][0] / prof[dom][1]
-    dom_amount, dom_kind = work[dom]
-    per_launch = dom_amount / max(prof[dom][1] // args.steps, 1)
+    work = kernel_work(s, causal, mode, c.tm is not None)
+    # in the backward alone "pack" is the launch that packs Q, K, V and builds the
+    # block map together with the prep of the supplied O and LSE (bf16); "prep" is D
+    # alone (f32)
+    work_bwd = dict(work, pack=work["pack_prep"])
+    kernels_bwd = per_kernel(prof_bwd, work_bwd, args.steps, peak)
+    kernels_whole = per_kernel(prof_whole, work, args.steps, peak)
+    dom = max(kernels_bwd, key=lambda n: kernels_bwd[n]["ms"])
+    dom_launch_ms = prof_bwd[dom][0] / prof_bwd[dom][1]
+    dom_amount, dom_kind = work_bwd[dom]
+    per_launch = dom_amount / max(prof_bwd[dom][1] // args.steps, 1)
     if dom_kind == "flop":
         ach = per_launch / (dom_launch_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
@@ -338,127 +379,96 @@ def main():
     else:
         ach = per_launch / (dom_launch_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_GBS, 4), "traffic": measured_traffic(dom, w.name), "per_launch_bytes": per_launch,
-                "avg_launch_ms": round(dom_launch_ms, 5)}
+                "frac": round(ach / HBM_GBS, 4), "traffic": measured_traffic(dom, w.name),
+                "per_launch_bytes": per_launch, "avg_launch_ms": round(dom_launch_ms, 5)}
 
+    value = F_b / (ms_bwd * 1e-3) / 1e12
     out = {
         "metric": METRIC,
-        "value": round((F_f + F_b) / (ms_step * 1e-3) / 1e12, 3),
+        "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "ms_per_step_min": round(st_step["min"], 4),
-        "ms_per_step_with_kernel_events": round(ms_step_prof, 4),
+        "ms_per_step": round(ms_bwd, 4),
+        "ms_per_step_min": round(st_bwd["min"], 4),
+        "ms_per_step_with_kernel_events": round(ms_bwd_prof, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": mode,
         "data": "synthetic",
         "config": {"workload": w.name, "B": s.B, "H": s.H, "Hkv": s.Hkv, "N": s.N, "M": s.M,
-                   "DK": s.DK, "DV": s.DV, "mask": w.mask, "mode": mode, "scale": scale,
-                   "step": "fab_backward with internal forward (whole path)"},
-        "frac_of_peak": round((F_f + F_b) / (ms_step * 1e-3) / 1e12 / peak, 4),
-        "backward_only": {"ms": round(ms_bwd, 4), "ms_min": round(st_bwd["min"], 4),
-                          "tflops": round(F_b / (ms_bwd * 1e-3) / 1e12, 3),
-                          "frac_of_peak": round(F_b / (ms_bwd * 1e-3) / 1e12 / peak, 4),
-                          "flops_counted": F_b, "kernels": kernels_bwd},
+                   "DK": s.DK, "DV": s.DV, "mask": w.mask, "mode": mode, "scale": c.scale,
+                   "step": "fab_backward with O and LSE supplied (the backward alone)",
+                   "flops_counted": F_b},
+        "frac_of_peak": round(value / peak, 4),
+        "kernels": kernels_bwd,
+        "roofline": roof,
+        "whole_path": {"ms": round(ms_whole, 4), "ms_min": round(st_whole["min"], 4),
+                       "tflops": round((F_f + F_b) / (ms_whole * 1e-3) / 1e12, 3),
+                       "frac_of_peak": round((F_f + F_b) / (ms_whole * 1e-3) / 1e12 / peak, 4),
+                       "flops_counted": F_f + F_b, "kernels": kernels_whole},
         "forward_only": {"ms": round(ms_fwd, 4), "tflops": round(F_f / (ms_fwd * 1e-3) / 1e12, 3),
                          "frac_of_peak": round(F_f / (ms_fwd * 1e-3) / 1e12 / peak, 4)},
-        "kernels": kernels,
-        "roofline": roof,
     }
-    # ---- the same step with the causal rule given as a flag instead of the mask
-    # tensor (identical result; no block map, no mask reads)
-    mask_free = None
+    tq, tk, tv, td = c.t
+    # ---- the causal rule given as a flag instead of the mask tensor (identical
+    # result; no block map, no mask reads), backward alone and whole path
     if causal:
-        ws_c, _ = fab.alloc_workspace(fs, mode, False, False, dev, causal=True)
-        ms_c = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mode=mode, blob=blob, ws=ws_c,
-                                                     causal=True), args.steps, args.warmup, stream, args.min_warm_s)
-        mask_free = {"ms_per_step": round(ms_c, 4), "value": round((F_f + F_b) / (ms_c * 1e-3) / 1e12, 3),
-                     "frac_of_peak": round((F_f + F_b) / (ms_c * 1e-3) / 1e12 / peak, 4)}
-        del ws_c
-
-    # ---- the same step with q, k, v, d stored as bf16 (bf16 mode: the values the
-    # matrix cores read; the f32 inputs rounded once beforehand, outside the timing)
-    bf16_in = None
+        ws_c, _ = fab.alloc_workspace(c.fs, mode, False, True, dev, causal=True)
+        ws_cw, _ = fab.alloc_workspace(c.fs, mode, False, False, dev, causal=True)
+        ms_c = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, c.scale, mode=mode, O=c.O, lse=c.lse,
+                                                     blob=c.blob, ws=ws_c, causal=True),
+                         args.steps, args.warmup, stream, args.min_warm_s)
+        ms_cw = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, c.scale, mode=mode, blob=c.blob, ws=ws_cw,
+                                                      causal=True), args.steps, args.warmup, stream, args.min_warm_s)
+        out["causal_flag_instead_of_mask"] = {
+            "backward_only": {"ms": round(ms_c, 4), "tflops": round(F_b / (ms_c * 1e-3) / 1e12, 3),
+                              "frac_of_peak": round(F_b / (ms_c * 1e-3) / 1e12 / peak, 4)},
+            "whole_path": {"ms": round(ms_cw, 4), "tflops": round((F_f + F_b) / (ms_cw * 1e-3) / 1e12, 3)}}
+        del ws_c, ws_cw
+        c.fwd()
+    # ---- q, k, v, d stored as bf16 (bf16 mode: the values the matrix cores read; the
+    # f32 inputs rounded once beforehand, outside the timing)
     if mode == "bf16":
         tb = [x.to(torch.bfloat16) for x in (tq, tk, tv, td)]
-        ms_b = time_loop(torch, lambda: fab.backward(*tb, scale, mask=tm, mode=mode, blob=blob, ws=ws_full),
+        ms_b = time_loop(torch, lambda: fab.backward(*tb, c.scale, mask=c.tm, mode=mode, O=c.O, lse=c.lse,
+                                                     blob=c.blob, ws=c.ws_bwd),
                          args.steps, args.warmup, stream, args.min_warm_s)
-        bf16_in = {"ms_per_step": round(ms_b, 4), "value": round((F_f + F_b) / (ms_b * 1e-3) / 1e12, 3),
-                   "frac_of_peak": round((F_f + F_b) / (ms_b * 1e-3) / 1e12 / peak, 4)}
+        out["bf16_inputs"] = {"backward_only": {"ms": round(ms_b, 4), "tflops": round(F_b / (ms_b * 1e-3) / 1e12, 3),
+                                                "frac_of_peak": round(F_b / (ms_b * 1e-3) / 1e12 / peak, 4)}}
         del tb
 
-    # ---- the other arithmetic mode on the same workload (f32 operands on the f32
-    # matrix cores, priced against the f32 peak), whole step and backward alone
-    other_mode = None
-    om = "f32" if mode == "bf16" else "bf16"
-    if om in w.modes or om == "f32":
-        ws_o, _ = fab.alloc_workspace(fs, om, tm is not None, False, dev)
-        ws_ob, _ = fab.alloc_workspace(fs, om, tm is not None, True, dev)
-        O_o, lse_o = fab.forward_lse(tq, tk, tv, scale, mask=tm, mode=om, ws=ws_ob)
-        ms_o = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mask=tm, mode=om, blob=blob, ws=ws_o),
-                         args.steps, args.warmup, stream, args.min_warm_s)
-        ms_ob = time_loop(torch, lambda: fab.backward(tq, tk, tv, td, scale, mask=tm, mode=om, O=O_o, lse=lse_o,
-                                                      blob=blob, ws=ws_ob), args.steps, args.warmup, stream,
-                          args.min_warm_s)
-        pk = PEAK_TFLOPS[om]
-        other_mode = {"mode": om, "ms_per_step": round(ms_o, 4),
-                      "value": round((F_f + F_b) / (ms_o * 1e-3) / 1e12, 3),
-                      "frac_of_peak": round((F_f + F_b) / (ms_o * 1e-3) / 1e12 / pk, 4), "peak": pk,
-                      "backward_only": {"ms": round(ms_ob, 4), "tflops": round(F_b / (ms_ob * 1e-3) / 1e12, 3),
-                                        "frac_of_peak": round(F_b / (ms_ob * 1e-3) / 1e12 / pk, 4)}}
-        del ws_o, ws_ob, O_o, lse_o
-
-    # ---- other workloads (e.g. the long-context one), same protocol, same mode
-    also = {}
-    for wid in [int(x) for x in args.also.split(",") if x.strip()]:
-        if wid == args.workload:
+    # ---- every other (workload, mode) pair, same protocol
+    pairs = []
+    if args.configs == "all":
+        pairs = [(wid, m) for wid in sorted(fi.WORKLOADS) for m in fi.WORKLOADS[wid].modes]
+        if (args.workload, "f32") not in pairs:
+            pairs.append((args.workload, "f32"))   # the headline workload in the other mode too
+    elif args.configs:
+        pairs = [(int(x.split(":")[0]), x.split(":")[1]) for x in args.configs.split(",") if x.strip()]
+    headline_host = c.host
+    del c
+    torch.cuda.empty_cache()
+    configs = {}
+    for wid, m in pairs:
+        if (wid, m) == (args.workload, mode):
             continue
-        w2 = fi.WORKLOADS[wid]
-        if mode not in w2.modes:
-            continue
-        s2, q2, k2, v2, d2, mask2, scale2 = fi.workload_inputs(wid)
-        c2 = w2.mask == "causal"
-        t2 = [torch.from_numpy(x).to(dev) for x in (q2, k2, v2, d2)]
-        tm2 = None if mask2 is None else torch.from_numpy(mask2.view(np.int16)).to(dev)
-        fs2 = fab.Shape(*s2.astuple())
-        blob2 = torch.empty(fab.blob_layout(fs2)[3], dtype=torch.float32, device=dev)
-        ws2, _ = fab.alloc_workspace(fs2, mode, tm2 is not None, False, dev)
-        ws2b, _ = fab.alloc_workspace(fs2, mode, tm2 is not None, True, dev)
-        O2, lse2 = fab.forward_lse(t2[0], t2[1], t2[2], scale2, mask=tm2, mode=mode, ws=ws2b)
-        ms2 = time_loop(torch, lambda: fab.backward(*t2, scale2, mask=tm2, mode=mode, blob=blob2, ws=ws2),
-                        args.steps, args.warmup, stream, args.min_warm_s)
-        ms2b = time_loop(torch, lambda: fab.backward(*t2, scale2, mask=tm2, mode=mode, O=O2, lse=lse2, blob=blob2,
-                                                     ws=ws2b), args.steps, args.warmup, stream, args.min_warm_s)
-        ms2c = None
-        if c2:
-            ws2c, _ = fab.alloc_workspace(fs2, mode, False, False, dev, causal=True)
-            ms2c = time_loop(torch, lambda: fab.backward(*t2, scale2, mode=mode, blob=blob2, ws=ws2c, causal=True),
-                             args.steps, args.warmup, stream, args.min_warm_s)
-            del ws2c
-        Ff2, Fb2 = fwd_flops(s2, c2), bwd_flops(s2, c2)
-        also[w2.name] = {"ms_per_step": round(ms2, 4), "value": round((Ff2 + Fb2) / (ms2 * 1e-3) / 1e12, 3),
-                         "frac_of_peak": round((Ff2 + Fb2) / (ms2 * 1e-3) / 1e12 / peak, 4),
-                         "backward_only": {"ms": round(ms2b, 4), "tflops": round(Fb2 / (ms2b * 1e-3) / 1e12, 3),
-                                           "frac_of_peak": round(Fb2 / (ms2b * 1e-3) / 1e12 / peak, 4)}}
-        if ms2c:
-            also[w2.name]["causal_flag_instead_of_mask"] = {
-                "ms_per_step": round(ms2c, 4), "value": round((Ff2 + Fb2) / (ms2c * 1e-3) / 1e12, 3)}
-        del t2, tm2, blob2, ws2, ws2b, O2, lse2
-    if mask_free:
-        out["causal_flag_instead_of_mask"] = mask_free
-    if bf16_in:
-        out["bf16_inputs"] = bf16_in
-    if other_mode:
-        out["other_mode"] = other_mode
-    if also:
-        out["other_workloads"] = also
+        c2 = Case(torch, fab, dev, wid, m)
+        configs[f"{wid}:{m}"] = pair_summary(torch, fab, c2, args, stream)
+        del c2
+        torch.cuda.empty_cache()
+    if configs:
+        out["configs"] = configs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(s, q, k, v, d, mask, scale, causal, args.cpu_budget_s)
+        q, k, v, d, mask = headline_host
+        out["cpu_baseline"] = cpu_baseline(s, q, k, v, d, mask, c_scale(args.workload), causal, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
+
+
+def c_scale(wid):
+    return fi.WORKLOADS[wid].scale_f32()
 
 
 if __name__ == "__main__":

@@ -164,17 +164,44 @@ def _input_dtype(*ts):
     return dt
 
 
-def _check_tensor(t, name, shape, device, dtypes=None):
+def _check_tensor(t, name, shape, dtypes=None):
+    """dtype, shape and contiguity of one tensor argument (the C ABI cannot check them:
+    it receives a bare pointer and reads or writes exactly the extent the shape implies)."""
     import torch
     dtypes = dtypes or (torch.float32,)
     if t.dtype not in dtypes:
         raise TypeError(f"{name} must be {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_devices(device, **tensors):
+    """Every given tensor on the one GPU device the call runs on."""
+    if device.type != "cuda":
+        raise ValueError(f"the tensors must be on a GPU device, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_mask(mask, s):
+    mask = _mask_arg(mask)
+    if mask is not None:
+        import torch
+        _check_tensor(mask, "mask", (s.N, s.M), (torch.int16, torch.uint16))
+    return mask
+
+
+def _check_ws(ws, need):
+    """A caller's workspace: contiguous, at least `need` bytes; returns its byte size."""
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"ws has {nbytes} bytes, {need} needed")
+    return nbytes
 
 
 def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device, causal=False):
@@ -182,6 +209,15 @@ def alloc_workspace(shape: Shape, mode, has_mask, have_o_lse, device, causal=Fal
     n = workspace_bytes(shape, mode, has_mask, have_o_lse, causal)
     # torch's caching allocator returns 512-byte aligned blocks
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def _on_stream(stream):
+    """Context in which the call's own buffers are allocated: the stream its kernels
+    run on, so that the caching allocator does not hand them to other work while those
+    kernels may still use them."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False):
@@ -192,21 +228,27 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     s = shape_of(q, k, v)
     dev = q.device
     bf16_in = _input_dtype(q, k, v) == torch.bfloat16
-    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev, (q.dtype,))
-    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev, (q.dtype,))
-    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev, (q.dtype,))
-    mask = _mask_arg(mask)
-    if O is None:
-        O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
-    else:
-        nbytes = ws.numel() * ws.element_size()
-    _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
-                                 float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(ws), nbytes,
-                                 _stream_handle(stream)))
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
+    mask = _check_mask(mask, s)
+    if O is not None:
+        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
+    if lse is not None:
+        _check_tensor(lse, "lse", (s.B, s.H, s.N))
+    if ws is not None:
+        nbytes = _check_ws(ws, workspace_bytes(s, mode, mask is not None, True, causal))
+    _check_devices(dev, k=k, v=v, mask=mask, O=O, lse=lse, ws=ws)
+    with _on_stream(stream):
+        if O is None:
+            O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
+        _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                     float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(ws),
+                                     nbytes, _stream_handle(stream)))
     return O, lse
 
 
@@ -214,26 +256,38 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
              stream=None, causal=False):
     """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
-    are float32, or bfloat16 (all four; mode "bf16")."""
+    are float32, or bfloat16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
+    float32, are both given (from forward_lse) or both None."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
     bf16_in = _input_dtype(q, k, v, d) == torch.bfloat16
-    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), dev, (q.dtype,))
-    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), dev, (q.dtype,))
-    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), dev, (q.dtype,))
-    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), dev, (q.dtype,))
-    mask = _mask_arg(mask)
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
+    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), (q.dtype,))
+    mask = _check_mask(mask, s)
+    if (O is None) != (lse is None):
+        raise ValueError("O and lse must be given together or both be None")
+    if O is not None:
+        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
+        _check_tensor(lse, "lse", (s.B, s.H, s.N))
     total = blob_layout(s)[3]
-    if blob is None:
-        blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
-    else:
-        nbytes = ws.numel() * ws.element_size()
-    _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                              float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
-                              _ptr(ws), nbytes, _stream_handle(stream)))
+    if blob is not None:
+        _check_tensor(blob, "blob", None)
+        if blob.numel() < total:
+            raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
+    if ws is not None:
+        nbytes = _check_ws(ws, workspace_bytes(s, mode, mask is not None, O is not None, causal))
+    _check_devices(dev, k=k, v=v, d=d, mask=mask, O=O, lse=lse, blob=blob, ws=ws)
+    with _on_stream(stream):
+        if blob is None:
+            blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
+        _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
+                                  float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
+                                  _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 
 

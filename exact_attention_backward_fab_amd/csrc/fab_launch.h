@@ -140,9 +140,11 @@ inline int64_t ds_bytes(const Dims &d, int Np)
 {
     return (int64_t)d.B * d.H * ((Np / 64 + 1) / 2) * ((d.M + 127) / 128) * 32768;
 }
+// (strictly below 4 GiB: one head's query-step-pair row of tiles, nkb128 * 32 KiB,
+// is then below 2^32 bytes too, the range of a buffer resource)
 inline bool dq_from_ds(const Dims &d, int Np, int dkp, int dvp)
 {
-    return dkp + dvp <= 256 && ds_bytes(d, Np) <= kDsMaxBytes;
+    return dkp + dvp <= 256 && ds_bytes(d, Np) < kDsMaxBytes;
 }
 
 // Query heads per work-group of the bf16 dK/dV kernel (1 or 2): two heads of one

@@ -59,6 +59,11 @@ def test_bf16_workspace_holds_ds_within_its_limit():
     big = fab.Shape(1, 40, 8, 8192, 8192, 128, 128)
     assert _ds_bytes(big) > 4 << 30
     assert fab.workspace_bytes(big, "bf16", False, True) < _ds_bytes(big)
+    # exactly 4 GiB of tiles in one row of 131072 key blocks (a buffer resource covers
+    # below 2^32 bytes): recompute
+    edge = fab.Shape(1, 1, 1, 127, (1 << 24) - 64, 32, 32)
+    assert _ds_bytes(edge) == 4 << 30
+    assert fab.workspace_bytes(edge, "bf16", False, True) < 4 << 30
 
 
 @pytest.mark.parametrize("shape", [

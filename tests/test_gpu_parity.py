@@ -8,6 +8,7 @@ five workloads at full size are compared on sampled rows and keys the oracle
 computes one by one, and through sums that hold at any size.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -142,6 +143,10 @@ SMALL = [
     # 128 key blocks x 10 heads: two heads per work-group, 5 head units (not a multiple
     # of the 8 XCDs: the plain work-group order)
     ("two_heads_per_wg_5_units", Shape(1, 10, 5, 64, 16384, 64, 64), "random", 53),
+    # two heads per work-group (64 key blocks x 16 heads = 1024) with a deep query loop:
+    # each work-group walks 16 query steps of 64 for each of its two heads, so every dK/dV
+    # element accumulates 2 x 1024 queries in registers before it is stored
+    ("two_heads_per_wg_deep_query_loop", Shape(1, 16, 4, 1024, 8192, 64, 64), None, 54),
 ]
 
 
@@ -375,6 +380,29 @@ def test_caller_stream_is_used(torch_dev):
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
 
 
+def test_side_stream_that_is_not_current_keeps_its_buffers(torch_dev):
+    # a stream passed without being made current: the call's own workspace and blob
+    # belong to that stream, so memory allocated and filled on the current stream
+    # right after the call (before any synchronisation) cannot take them over while
+    # the call's kernels still run
+    torch, dev = torch_dev
+    fab = fabmod()
+    s = Shape(1, 4, 2, 300, 300, 64, 64)
+    q, k, v, d = make_qkvd(s, 73)
+    mask = to_dev(torch, dev, causal_mask(s.N, s.M))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    ref = fab.backward(*t, 0.125, mask=mask, mode="bf16").clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = fab.backward(*t, 0.125, mask=mask, mode="bf16", stream=side)
+    junk = [torch.full((1 << 22,), float("nan"), device=dev) for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
 @pytest.mark.parametrize("mode", ["bf16", "f32"])
 def test_graph_capture_replays(torch_dev, mode):
     # fab_backward captured into a graph (no memset nodes: every zeroing is a
@@ -459,26 +487,20 @@ def workload(wid):
 
 
 def sample_ids(s, wid, rng):
-    """Rows (n + N*(h + H*b)) and keys (m + M*(g + Hkv*b)) the oracle evaluates one by one."""
+    """Rows (n + N*(h + H*b)) and keys (m + M*(g + Hkv*b)) the oracle evaluates one by one.
+    Keys cover the whole key range of several groups: the tile edges 0, 63, 64, 127, 128,
+    the middle, the last key and random ones -- under the causal rule key m is seen by
+    every query from m on, so the first keys carry the deepest dK/dV accumulation."""
     R = s.B * s.H * s.N
     rows = list(rng.choice(R, 24, replace=False)) + [0, R - 1]
-    if wid in (3, 4):
-        # causal: a key is seen by the queries at or after it; keys near the end keep
-        # the oracle cheap, plus a few spread ones for the smaller workload
-        lo = s.M - (256 if wid == 4 else 1024)
-        keys = []
-        for gb in rng.choice(s.Hkv * s.B, 3, replace=False):
-            for m in rng.choice(np.arange(lo, s.M), 4, replace=False):
-                keys.append(int(m + s.M * gb))
-        if wid == 3:
-            keys.append(int(5 + s.M * 1))
-    else:
-        keys = []
-        for gb in rng.choice(s.Hkv * s.B, 3, replace=False):
-            for m in rng.choice(s.M, 5, replace=False):
-                keys.append(int(m + s.M * gb))
-        keys.append(int(s.M - 1))   # beyond the padding cut for workload 5: exactly zero
-    return np.array(rows, dtype=np.int64), np.array(keys, dtype=np.int64)
+    fixed = [0, 63, 64, 127, 128, s.M // 2 - 1, s.M // 2, s.M - 129, s.M - 1]
+    fixed = [m for m in fixed if 0 <= m < s.M]
+    ngroups = 2 if wid == 4 else 3
+    keys = []
+    for gb in rng.choice(s.Hkv * s.B, min(ngroups, s.Hkv * s.B), replace=False):
+        ms = fixed + list(rng.choice(s.M, 6, replace=False))
+        keys += [int(m + s.M * gb) for m in ms]
+    return np.array(rows, dtype=np.int64), np.array(sorted(set(keys)), dtype=np.int64)
 
 
 def test_bf16_large_shape_recomputes_dq(torch_dev):
@@ -530,24 +552,43 @@ def test_bf16_large_shape_recomputes_dq(torch_dev):
     assert np.max(np.abs(got - expect)) <= tol * np.max(np.abs(dv.astype(np.float64)).sum(axis=2))
 
 
-WL_CASES = [(1, "f32"), (2, "f32"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (5, "f32"), (5, "bf16")]
+WL_CASES = [(1, "f32"), (2, "f32"), (2, "bf16"), (3, "bf16"), (3, "f32"), (4, "bf16"), (5, "f32"), (5, "bf16")]
+_oracle_cache = {}
 
 
+def sampled_oracle(wid, s, q, k, v, mask, d, scale):
+    if wid not in _oracle_cache:
+        from oracle import oracle as orc
+        rows, keys = sample_ids(s, wid, np.random.default_rng(100 + wid))
+        t0 = time.perf_counter()
+        ref = orc.backward_sampled(s, q, k, v, mask, d, scale, rows, keys)
+        print(f"  oracle: {len(rows)} rows, {len(keys)} keys in {time.perf_counter() - t0:.1f} s", flush=True)
+        _oracle_cache[wid] = (rows, keys, ref)
+    return _oracle_cache[wid]
+
+
+@pytest.mark.parametrize("route", ["o_lse_supplied", "own_forward"])
 @pytest.mark.parametrize("wid,mode", WL_CASES, ids=[f"w{w}-{m}" for w, m in WL_CASES])
-def test_workload_full_size(torch_dev, wid, mode):
+def test_workload_full_size(torch_dev, wid, mode, route):
+    """Each workload at full size in both routes of fab_backward: O and LSE from a prior
+    fab_forward_lse (the benchmark's headline call) and O = lse = NULL (the forward inside
+    the call: in bf16 mode the forward kernel writes the tiles, LSE/D blocks and pads the
+    backward reads)."""
     torch, dev = torch_dev
     from oracle import oracle as orc
     s, q, k, v, d, mask, scale = workload(wid)
-    print(f"[parity] workload {wid} {mode} {s}", flush=True)
+    print(f"[parity] workload {wid} {mode} {route} {s}", flush=True)
     fab = fabmod()
     fs = fab.Shape(*s.astuple())
     t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
     tm = to_dev(torch, dev, mask)
-    # the benchmark's configuration: O and LSE from the forward, then the backward
-    O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode=mode)
+    O = lse = None
+    if route == "o_lse_supplied":
+        O, lse = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode=mode)
     blob = fab.backward(t[0], t[1], t[2], t[3], scale, mask=tm, mode=mode, O=O, lse=lse)
     torch.cuda.synchronize()
     blob = blob.cpu().numpy()
+    del t, O, lse
     _, off_k, off_v, total = fab.blob_layout(fs)
     nq, nk, nv = q.size, k.size, v.size
     assert np.all(np.isfinite(blob))
@@ -561,16 +602,17 @@ def test_workload_full_size(torch_dev, wid, mode):
     assert np.all(dq[:, :, dead_rows, :] == 0)
     assert np.all(dk[:, :, dead_keys, :] == 0) and np.all(dv[:, :, dead_keys, :] == 0)
     if wid in (1, 2):
-        ref = orc.backward(s, q, k, v, mask, d, scale)
+        key = ("full", wid)
+        if key not in _oracle_cache:
+            _oracle_cache[key] = orc.backward(s, q, k, v, mask, d, scale)
+        ref = _oracle_cache[key]
         for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
             e = rel_err(got, ref[name])
             print(f"  {name} max-rel {e:.3e}", flush=True)
             assert e <= tol, name
         return
 
-    rng = np.random.default_rng(100 + wid)
-    rows, keys = sample_ids(s, wid, rng)
-    rdq, rdk, rdv = orc.backward_sampled(s, q, k, v, mask, d, scale, rows, keys)
+    rows, keys, (rdq, rdk, rdv) = sampled_oracle(wid, s, q, k, v, mask, d, scale)
     gdq = np.stack([dq[r // (s.N * s.H), (r // s.N) % s.H, r % s.N] for r in rows])
     gdk = np.stack([dk[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
     gdv = np.stack([dv[r // (s.M * s.Hkv), (r // s.M) % s.Hkv, r % s.M] for r in keys])
