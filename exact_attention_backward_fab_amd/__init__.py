@@ -35,7 +35,7 @@ FAB_E_HIP = -5
 
 # every symbol include/fab.h declares
 EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
-           "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
+           "fab_backward_noalloc", "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
            "fab_strerror", "fab_last_error", "fab_version")
 KERNELS = ("block_map", "forward", "prep", "pack", "backward", "dq", "gqa_reduce")
 
@@ -72,6 +72,8 @@ def lib():
         L.fab_forward_lse.argtypes = [SP, P, P, P, P, ctypes.c_float, I, P, P, P, SZ, P]
         L.fab_backward.restype = I
         L.fab_backward.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, P, SZ, P]
+        L.fab_backward_noalloc.restype = I
+        L.fab_backward_noalloc.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, P]
         L.fab_strerror.restype = ctypes.c_char_p
         L.fab_strerror.argtypes = [I]
         L.fab_last_error.restype = ctypes.c_char_p
@@ -288,6 +290,40 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
         _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
                                   float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
                                   _ptr(ws), nbytes, _stream_handle(stream)))
+    return blob
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FAB_NOALLOC_SCRATCH_BYTES of include/fab.h
+
+
+def backward_noalloc(q, k, v, d, scale, blob, mask=None, mode="f32", O=None, lse=None, stream=None,
+                     causal=False):
+    """backward() through fab_backward_noalloc: the library's fixed scratch array serves
+    as the workspace, so the call allocates nothing; the caller passes the blob (f32,
+    at least blob_layout()[3] floats).  Shapes needing more than NOALLOC_SCRATCH_BYTES
+    of workspace raise FabError (FAB_E_UNSUPPORTED)."""
+    import torch
+    s = shape_of(q, k, v)
+    dev = q.device
+    bf16_in = _input_dtype(q, k, v, d) == torch.bfloat16
+    _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
+    _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
+    _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
+    _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), (q.dtype,))
+    mask = _check_mask(mask, s)
+    if (O is None) != (lse is None):
+        raise ValueError("O and lse must be given together or both be None")
+    if O is not None:
+        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
+        _check_tensor(lse, "lse", (s.B, s.H, s.N))
+    _check_tensor(blob, "blob", None)
+    total = blob_layout(s)[3]
+    if blob.numel() < total:
+        raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
+    _check_devices(dev, k=k, v=v, d=d, mask=mask, O=O, lse=lse, blob=blob)
+    _check(lib().fab_backward_noalloc(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
+                                      float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
+                                      _stream_handle(stream)))
     return blob
 
 

@@ -23,6 +23,7 @@ SOURCES = {
     # arithmetic work on them with plain VALU instructions
     "fab_qouter.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fab_api.cpp": [],
+    "fab_noalloc.hip": [],
 }
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -304,6 +304,15 @@ int launch_fwd(const Plan &pl, int bf16, const void *q, const void *k, const voi
 
 }  // namespace
 
+int fab::set_error(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
 extern "C" {
 
 int fab_profile_enable(int on)

@@ -227,6 +227,9 @@ inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *d
 hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
                              hipStream_t s);
 
+// Records the detail of an error for fab_last_error (thread-local) and returns code.
+int set_error(int code, const char *fmt, ...);
+
 // Fill n floats with zero.
 hipError_t launch_zero(float *p, int64_t n, hipStream_t s);
 

@@ -145,6 +145,28 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
                  const uint16_t *mask, const void *d, float scale, int mode, const float *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: fab_backward
+ * (same arguments, kernels and results, same validation and error codes) with
+ * its workspace taken from a fixed array of FAB_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of a caller's buffer.  The call allocates and frees nothing;
+ * the array is device memory that each GPU the library runs on holds from the
+ * time the library's code is loaded on it until the process ends.  The caller
+ * still passes every input and the blob.
+ *   Limit: shapes whose fab_workspace_bytes(.., has_mask = mask != NULL,
+ *   have_o_lse = O != NULL) exceeds FAB_NOALLOC_SCRATCH_BYTES return
+ *   FAB_E_UNSUPPORTED (nothing enqueued); e.g. B=2, H=8, N=M=1024, D=64 in bf16
+ *   mode needs about 41 MB.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *   last call's contents (the kernels write every workspace byte they read, so
+ *   nothing needs to start at zero).  Calls that overlap on one GPU -- on two
+ *   streams, or from two threads without ordering -- race on the array and give
+ *   undefined results; calls ordered on one stream are safe. */
+#define FAB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fab_backward_noalloc(const fab_shape *shape, const void *q, const void *k, const void *v,
+                         const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                         const float *lse, float *blob, void *stream);
+
 /* Measurement hooks (they compute nothing).  While enabled, every kernel
  * launch made by fab_forward_lse and fab_backward is bracketed by a pair of
  * HIP events recorded on the caller's stream.  fab_profile_read waits for the

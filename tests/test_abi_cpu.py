@@ -156,3 +156,20 @@ def test_forward_rejects_bad_arguments():
                            P(FAKE), None, 0, None)
     assert rc == fab.FAB_E_WORKSPACE   # a mask needs its block map workspace
     assert L.fab_blob_layout(None, None, None, None, None) == fab.FAB_E_INVAL
+
+
+def test_noalloc_rejects_before_device_work():
+    """fab_backward_noalloc checks the shape, the mode and its fixed scratch size on the
+    host before any HIP call (here, without a GPU, it must return the error code)."""
+    L = fab.lib()
+    P = ctypes.c_void_p
+    big = fab.FabShape(1, 32, 8, 2048, 2048, 128, 128)   # ~370 MB of bf16 workspace
+    rc = L.fab_backward_noalloc(ctypes.byref(big), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), 0.1,
+                                fab.FAB_MODE_BF16 | fab.FAB_CAUSAL, P(FAKE), P(FAKE), P(FAKE), None)
+    assert rc == fab.FAB_E_UNSUPPORTED
+    assert "scratch" in L.fab_last_error().decode()
+    bad = fab.FabShape(1, 3, 2, 8, 8, 16, 16)              # H % Hkv != 0
+    rc = L.fab_backward_noalloc(ctypes.byref(bad), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), 0.1, 0, None, None,
+                                P(FAKE), None)
+    assert rc == fab.FAB_E_INVAL
+    assert fab.NOALLOC_SCRATCH_BYTES == 64 << 20
