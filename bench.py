@@ -335,6 +335,13 @@ def main():
     F_f, F_b = c.flops()
     peak = PEAK_TFLOPS[mode]
 
+    if args.calib_copy:
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     if args.only:
         fn, flops = {"backward": (c.bwd, F_b), "whole": (c.whole, F_f + F_b), "forward": (c.fwd, F_f)}[args.only]
         ms = time_loop(torch, fn, args.steps, args.warmup, stream, args.min_warm_s, repeats=1)
@@ -342,13 +349,6 @@ def main():
                           "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3)}),
               flush=True)
         return
-
-    if args.calib_copy:
-        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
 
     # ---- timed region: the backward alone, K steps with nothing but its launches
     st_bwd, st_whole = {}, {}
