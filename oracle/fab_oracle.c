@@ -31,6 +31,14 @@
  *   derivative of sum(d * attn) for the forward above, so an all-masked row
  *   contributes nothing and has zero dQ.
  *
+ *   ALiBi (optional; the ggmlR test file names it only through `max_bias`, in its
+ *   block "the graph builder rejects attention features it cannot differentiate",
+ *   and gives no score function): with per-head slopes alibi[h] (NULL: none) the
+ *   score gains the linear bias alibi[h] * (m - n) after the scale, next to the
+ *   mask: s[m] = scale * (q . k) + alibi[h] * (m - n) + mask[m,n].  Everything else
+ *   (softmax, LSE, backward) is unchanged: the bias is a constant of the inputs,
+ *   so it only enters through P.
+ *
  *   Result packing, from PowerInfer's "Function ggml_flash_attn_back" (result
  *   sizing) and the ggmlR test's `fab_grads` unpacker: one f32 buffer
  *   [dQ | dK | dV], each slice padded to 16 bytes (4 floats), padding zero.
@@ -84,9 +92,11 @@ static inline int64_t idx_d(const oshape *s, int64_t dv, int64_t h, int64_t n, i
 static inline int64_t idx_row(const oshape *s, int64_t n, int64_t h, int64_t b)
 { return n + s->N * (h + s->H * b); }
 
-/* score s[m] of query row (b,h,n) against key m: scale first, then the mask */
+/* score s[m] of query row (b,h,n) against key m: scale first, then the ALiBi
+ * bias (when slopes are given) and the mask */
 static double score(const oshape *s, const double *q, const double *k, const uint16_t *mask,
-                    double scale, int64_t b, int64_t h, int64_t g, int64_t n, int64_t m)
+                    const double *alibi, double scale, int64_t b, int64_t h, int64_t g, int64_t n,
+                    int64_t m)
 {
     double acc = 0.0;
     const double *qr = q + idx_q(s, 0, n, h, b);
@@ -94,6 +104,8 @@ static double score(const oshape *s, const double *q, const double *k, const uin
     for (int64_t i = 0; i < s->DK; ++i)
         acc += qr[i] * kr[i];
     acc *= scale;
+    if (alibi)
+        acc += alibi[h] * (double)(m - n);
     if (mask)
         acc += fab_oracle_half_to_double(mask[m + s->M * n]);
     return acc;
@@ -103,6 +115,7 @@ typedef struct {
     const oshape *s;
     const double *q, *k, *v, *d;
     const uint16_t *mask;
+    const double *alibi;     /* per-head ALiBi slopes [H] or NULL */
     double scale;
     /* row pass outputs (any may be NULL) */
     double *O, *lse, *D, *rmax, *rsum, *dq;
@@ -138,7 +151,7 @@ static void row_work(job *j, int64_t r, double *sbuf, double *pbuf, double *dpbu
     int any = 0;
     double mx = -INFINITY;
     for (int64_t m = 0; m < s->M; ++m) {
-        sbuf[m] = score(s, j->q, j->k, j->mask, j->scale, b, h, g, n, m);
+        sbuf[m] = score(s, j->q, j->k, j->mask, j->alibi, j->scale, b, h, g, n, m);
         if (isfinite(sbuf[m])) {
             any = 1;
             if (sbuf[m] > mx)
@@ -229,7 +242,7 @@ static void key_work(job *j, int64_t r, double *kacc, double *vacc)
             int64_t row = idx_row(s, n, h, b);
             if (j->dead[row])
                 continue;
-            double sc = score(s, j->q, j->k, j->mask, j->scale, b, h, g, n, m);
+            double sc = score(s, j->q, j->k, j->mask, j->alibi, j->scale, b, h, g, n, m);
             if (!isfinite(sc))
                 continue;                    /* weight 0 */
             double P = exp(sc - j->rmax[row]) / j->rsum[row];
@@ -310,9 +323,11 @@ static int valid(const oshape *s)
     return s->H % s->Hkv == 0;
 }
 
-/* Forward only: O [DV,H,N,B] and LSE [N,H,B]. Returns 0 on success. */
-int fab_oracle_forward(const int64_t *shape7, const double *q, const double *k, const double *v,
-                       const uint16_t *mask, double scale, double *O, double *lse, int nthreads)
+/* Forward only: O [DV,H,N,B] and LSE [N,H,B]; alibi: per-head slopes [H] or NULL.
+ * Returns 0 on success. */
+int fab_oracle_forward_alibi(const int64_t *shape7, const double *q, const double *k, const double *v,
+                             const uint16_t *mask, const double *alibi, double scale, double *O, double *lse,
+                             int nthreads)
 {
     oshape s = {shape7[0], shape7[1], shape7[2], shape7[3], shape7[4], shape7[5], shape7[6]};
     if (!valid(&s))
@@ -320,22 +335,29 @@ int fab_oracle_forward(const int64_t *shape7, const double *q, const double *k, 
     job j;
     memset(&j, 0, sizeof j);
     pthread_mutex_init(&j.lock, NULL);
-    j.s = &s; j.q = q; j.k = k; j.v = v; j.mask = mask; j.scale = scale;
+    j.s = &s; j.q = q; j.k = k; j.v = v; j.mask = mask; j.alibi = alibi; j.scale = scale;
     j.O = O; j.lse = lse;
     run(&j, row_thread, nthreads);
     pthread_mutex_destroy(&j.lock);
     return 0;
 }
 
+int fab_oracle_forward(const int64_t *shape7, const double *q, const double *k, const double *v,
+                       const uint16_t *mask, double scale, double *O, double *lse, int nthreads)
+{
+    return fab_oracle_forward_alibi(shape7, q, k, v, mask, NULL, scale, O, lse, nthreads);
+}
+
 /*
  * Full backward: dq [DK,N,H,B], dk [DK,M,Hkv,B], dv [DV,M,Hkv,B]; optionally
- * O, lse and D (row statistics, [N,H,B]).  Returns 0, -1 on a bad shape, or -2
- * when the D = sum P dP self-check failed on some row.
+ * O, lse and D (row statistics, [N,H,B]); alibi: per-head slopes [H] or NULL.
+ * Returns 0, -1 on a bad shape, or -2 when the D = sum P dP self-check failed
+ * on some row.
  */
-int fab_oracle_backward(const int64_t *shape7, const double *q, const double *k, const double *v,
-                        const uint16_t *mask, const double *d, double scale,
-                        double *dq, double *dk, double *dv, double *O, double *lse, double *D,
-                        int nthreads)
+int fab_oracle_backward_alibi(const int64_t *shape7, const double *q, const double *k, const double *v,
+                              const uint16_t *mask, const double *alibi, const double *d, double scale,
+                              double *dq, double *dk, double *dv, double *O, double *lse, double *D,
+                              int nthreads)
 {
     oshape s = {shape7[0], shape7[1], shape7[2], shape7[3], shape7[4], shape7[5], shape7[6]};
     if (!valid(&s))
@@ -348,7 +370,7 @@ int fab_oracle_backward(const int64_t *shape7, const double *q, const double *k,
     job j;
     memset(&j, 0, sizeof j);
     pthread_mutex_init(&j.lock, NULL);
-    j.s = &s; j.q = q; j.k = k; j.v = v; j.d = d; j.mask = mask; j.scale = scale;
+    j.s = &s; j.q = q; j.k = k; j.v = v; j.d = d; j.mask = mask; j.alibi = alibi; j.scale = scale;
     j.O = O; j.lse = lse; j.D = rD; j.rmax = rmax; j.rsum = rsum; j.dead = dead; j.dq = dq;
     run(&j, row_thread, nthreads);
     j.dk = dk; j.dv = dv;
@@ -361,6 +383,14 @@ int fab_oracle_backward(const int64_t *shape7, const double *q, const double *k,
     return bad ? -2 : 0;
 }
 
+int fab_oracle_backward(const int64_t *shape7, const double *q, const double *k, const double *v,
+                        const uint16_t *mask, const double *d, double scale,
+                        double *dq, double *dk, double *dv, double *O, double *lse, double *D,
+                        int nthreads)
+{
+    return fab_oracle_backward_alibi(shape7, q, k, v, mask, NULL, d, scale, dq, dk, dv, O, lse, D, nthreads);
+}
+
 /*
  * Sampled backward for large problems.
  *   rows  : n_rows flat row ids r = n + N*(h + H*b); dq_out gets DK doubles per row.
@@ -369,11 +399,11 @@ int fab_oracle_backward(const int64_t *shape7, const double *q, const double *k,
  * The row statistics needed by the keys are computed only for the rows that see
  * a finite score at one of the requested keys.
  */
-int fab_oracle_backward_sampled(const int64_t *shape7, const double *q, const double *k,
-                                const double *v, const uint16_t *mask, const double *d,
-                                double scale, const int64_t *rows, int64_t n_rows, double *dq_out,
-                                const int64_t *keys, int64_t n_keys, double *dk_out,
-                                double *dv_out, int nthreads)
+int fab_oracle_backward_sampled_alibi(const int64_t *shape7, const double *q, const double *k,
+                                      const double *v, const uint16_t *mask, const double *alibi,
+                                      const double *d, double scale, const int64_t *rows, int64_t n_rows,
+                                      double *dq_out, const int64_t *keys, int64_t n_keys, double *dk_out,
+                                      double *dv_out, int nthreads)
 {
     oshape s = {shape7[0], shape7[1], shape7[2], shape7[3], shape7[4], shape7[5], shape7[6]};
     if (!valid(&s))
@@ -414,7 +444,7 @@ int fab_oracle_backward_sampled(const int64_t *shape7, const double *q, const do
     job j;
     memset(&j, 0, sizeof j);
     pthread_mutex_init(&j.lock, NULL);
-    j.s = &s; j.q = q; j.k = k; j.v = v; j.d = d; j.mask = mask; j.scale = scale;
+    j.s = &s; j.q = q; j.k = k; j.v = v; j.d = d; j.mask = mask; j.alibi = alibi; j.scale = scale;
     j.D = rD; j.rmax = rmax; j.rsum = rsum; j.dead = dead; j.dq = dq_full;
     j.items = need; j.n_items = n_need;
     run(&j, row_thread, nthreads);
@@ -432,6 +462,16 @@ int fab_oracle_backward_sampled(const int64_t *shape7, const double *q, const do
     pthread_mutex_destroy(&j.lock);
     free(rD); free(rmax); free(rsum); free(dead); free(need); free(flag);
     return bad ? -2 : 0;
+}
+
+int fab_oracle_backward_sampled(const int64_t *shape7, const double *q, const double *k,
+                                const double *v, const uint16_t *mask, const double *d,
+                                double scale, const int64_t *rows, int64_t n_rows, double *dq_out,
+                                const int64_t *keys, int64_t n_keys, double *dk_out,
+                                double *dv_out, int nthreads)
+{
+    return fab_oracle_backward_sampled_alibi(shape7, q, k, v, mask, NULL, d, scale, rows, n_rows, dq_out,
+                                             keys, n_keys, dk_out, dv_out, nthreads);
 }
 
 /* Blob layout from the pages: offsets in floats, each slice padded to 4 floats. */

@@ -61,6 +61,14 @@ def _load(path):
     L.fab_oracle_backward_sampled.restype = ctypes.c_int
     L.fab_oracle_backward_sampled.argtypes = [P, P, P, P, P, P, ctypes.c_double, P, I64, P,
                                               P, I64, P, P, ctypes.c_int]
+    L.fab_oracle_forward_alibi.restype = ctypes.c_int
+    L.fab_oracle_forward_alibi.argtypes = [P, P, P, P, P, P, ctypes.c_double, P, P, ctypes.c_int]
+    L.fab_oracle_backward_alibi.restype = ctypes.c_int
+    L.fab_oracle_backward_alibi.argtypes = [P, P, P, P, P, P, P, ctypes.c_double, P, P, P, P, P, P,
+                                            ctypes.c_int]
+    L.fab_oracle_backward_sampled_alibi.restype = ctypes.c_int
+    L.fab_oracle_backward_sampled_alibi.argtypes = [P, P, P, P, P, P, P, ctypes.c_double, P, I64, P,
+                                                    P, I64, P, P, ctypes.c_int]
     L.fab_oracle_blob_layout.restype = ctypes.c_int
     L.fab_oracle_blob_layout.argtypes = [P, P]
     L.fab_oracle_pack.restype = ctypes.c_int
@@ -93,36 +101,49 @@ def _mask(mask):
     return np.ascontiguousarray(mask, dtype=np.uint16)
 
 
+def _alibi(shape, alibi):
+    """Per-head ALiBi slopes as f64 [H], or None."""
+    if alibi is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(alibi, dtype=np.float64).reshape(-1))
+    if a.size != shape.H:
+        raise ValueError(f"alibi needs {shape.H} slopes, got {a.size}")
+    return a
+
+
 def half_to_double(bits: int) -> float:
     return lib().fab_oracle_half_to_double(int(bits))
 
 
-def forward(shape, q, k, v, mask, scale, nthreads=None):
-    """O (B,N,H,DV) and LSE (B,H,N) in f64."""
+def forward(shape, q, k, v, mask, scale, nthreads=None, alibi=None):
+    """O (B,N,H,DV) and LSE (B,H,N) in f64.  alibi: per-head slopes [H] or None
+    (score scale*q.k + alibi[h]*(m - n) + mask)."""
     s = shape
     O = np.zeros((s.B, s.N, s.H, s.DV))
     lse = np.zeros((s.B, s.H, s.N))
     q, k, v, m = _f64(q), _f64(k), _f64(v), _mask(mask)
+    a = _alibi(s, alibi)
     sh = _shape7(s)
-    rc = lib().fab_oracle_forward(_ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), float(scale),
-                                  _ptr(O), _ptr(lse), nthreads or default_threads())
+    rc = lib().fab_oracle_forward_alibi(_ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(a), float(scale),
+                                        _ptr(O), _ptr(lse), nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle forward rejected the shape ({rc})")
     return O, lse
 
 
-def backward(shape, q, k, v, mask, d, scale, nthreads=None):
-    """dict with dq, dk, dv (ne-shaped f64), O, lse, D."""
+def backward(shape, q, k, v, mask, d, scale, nthreads=None, alibi=None):
+    """dict with dq, dk, dv (ne-shaped f64), O, lse, D.  alibi as for forward()."""
     s = shape
     out = dict(
         dq=np.zeros(s.q_shape), dk=np.zeros(s.k_shape), dv=np.zeros(s.v_shape),
         O=np.zeros(s.d_shape), lse=np.zeros((s.B, s.H, s.N)), D=np.zeros((s.B, s.H, s.N)))
     q, k, v, d, m = _f64(q), _f64(k), _f64(v), _f64(d), _mask(mask)
+    a = _alibi(s, alibi)
     sh = _shape7(s)
-    rc = lib().fab_oracle_backward(_ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(d),
-                                   float(scale), _ptr(out["dq"]), _ptr(out["dk"]),
-                                   _ptr(out["dv"]), _ptr(out["O"]), _ptr(out["lse"]),
-                                   _ptr(out["D"]), nthreads or default_threads())
+    rc = lib().fab_oracle_backward_alibi(_ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(a), _ptr(d),
+                                         float(scale), _ptr(out["dq"]), _ptr(out["dk"]),
+                                         _ptr(out["dv"]), _ptr(out["O"]), _ptr(out["lse"]),
+                                         _ptr(out["D"]), nthreads or default_threads())
     if rc == -2:
         raise AssertionError("oracle self-check D = dO.O = sum P dP failed")
     if rc != 0:
@@ -130,7 +151,7 @@ def backward(shape, q, k, v, mask, d, scale, nthreads=None):
     return out
 
 
-def backward_sampled(shape, q, k, v, mask, d, scale, rows, keys, nthreads=None):
+def backward_sampled(shape, q, k, v, mask, d, scale, rows, keys, nthreads=None, alibi=None):
     """dQ rows for flat row ids (n + N*(h + H*b)) and dK/dV rows for flat key ids
     (m + M*(g + Hkv*b)).  Returns (dq [len(rows), DK], dk [len(keys), DK], dv [len(keys), DV])."""
     s = shape
@@ -140,9 +161,10 @@ def backward_sampled(shape, q, k, v, mask, d, scale, rows, keys, nthreads=None):
     dk = np.zeros((len(keys), s.DK))
     dv = np.zeros((len(keys), s.DV))
     q, k, v, d, m = _f64(q), _f64(k), _f64(v), _f64(d), _mask(mask)
+    a = _alibi(s, alibi)
     sh = _shape7(s)
-    rc = lib().fab_oracle_backward_sampled(
-        _ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(d), float(scale),
+    rc = lib().fab_oracle_backward_sampled_alibi(
+        _ptr(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(a), _ptr(d), float(scale),
         _ptr(rows), len(rows), _ptr(dq), _ptr(keys), len(keys), _ptr(dk), _ptr(dv),
         nthreads or default_threads())
     if rc == -2:
@@ -170,13 +192,13 @@ def pack(shape, dq, dk, dv):
     return blob[:total]
 
 
-def loss(shape, q, k, v, mask, d, scale):
+def loss(shape, q, k, v, mask, d, scale, alibi=None):
     """sum(d * attn(q, k, v)) in f64: the scalar whose gradient the backward returns."""
-    O, _ = forward(shape, q, k, v, mask, scale, nthreads=1)
+    O, _ = forward(shape, q, k, v, mask, scale, nthreads=1, alibi=alibi)
     return float(np.sum(_f64(d) * O))
 
 
-def num_grad(shape, q, k, v, mask, d, scale, which, eps=1e-3):
+def num_grad(shape, q, k, v, mask, d, scale, which, eps=1e-3, alibi=None):
     """Central-difference gradient of sum(d * attn) w.r.t. q, k or v (f64 inputs)."""
     vals = {"q": _f64(q).copy(), "k": _f64(k).copy(), "v": _f64(v).copy()}
     x = vals[which]
@@ -185,9 +207,9 @@ def num_grad(shape, q, k, v, mask, d, scale, which, eps=1e-3):
     for i in range(x.size):
         orig = flat[i]
         flat[i] = orig + eps
-        fh = loss(shape, vals["q"], vals["k"], vals["v"], mask, d, scale)
+        fh = loss(shape, vals["q"], vals["k"], vals["v"], mask, d, scale, alibi)
         flat[i] = orig - eps
-        fl = loss(shape, vals["q"], vals["k"], vals["v"], mask, d, scale)
+        fl = loss(shape, vals["q"], vals["k"], vals["v"], mask, d, scale, alibi)
         flat[i] = orig
         g[i] = (fh - fl) / (2 * eps)
     return g.reshape(x.shape)

@@ -3,7 +3,9 @@
 Each mutant is a one-line change to oracle/fab_oracle.c of the kind the pins are
 meant to catch: a wrong sign or a dropped term in dS (labml "Flash Attention",
 section "Backward pass"), a wrong grouped-query head map or the mask added before
-the scale (ggmlR test file's `attn_ref`), a missing scale, a transposed layout.
+the scale (ggmlR test file's `attn_ref`), a missing scale, a transposed layout, and
+for the ALiBi bias a flipped sign, the key/value head's slope in place of the query
+head's, and the bias added before the scale.
 The unmodified source must pass the same checks.
 """
 import math
@@ -24,12 +26,18 @@ MUTANTS = {
     "dS_sign": ("double dS = P * (dP - j->D[row]);", "double dS = P * (dP + j->D[row]);"),
     "dS_drop_D": ("double dS = pbuf[m] * (dpbuf[m] - D);", "double dS = pbuf[m] * dpbuf[m];"),
     "head_map": ("int64_t g = h / (s->H / s->Hkv);", "int64_t g = h % s->Hkv;"),
-    "mask_before_scale": ("    acc *= scale;\n    if (mask)\n        acc += fab_oracle_half_to_double(mask[m + s->M * n]);",
-                          "    if (mask)\n        acc += fab_oracle_half_to_double(mask[m + s->M * n]);\n    acc *= scale;"),
+    # the mask added before the scale: scale * (q.k + mask)
+    "mask_before_scale": ("        acc += fab_oracle_half_to_double(mask[m + s->M * n]);\n    return acc;",
+                          "        acc += scale * fab_oracle_half_to_double(mask[m + s->M * n]);\n    return acc;"),
     "dk_no_scale": ("kacc[i] += j->scale * dS * qr[i];", "kacc[i] += dS * qr[i];"),
     "d_layout": ("{ return dv + s->DV * (h + s->H * (n + s->N * b)); }",
                  "{ return dv + s->DV * (n + s->N * (h + s->H * b)); }"),
     "mask_transposed": ("mask[m + s->M * n]", "mask[n + s->N * m]"),
+    # ALiBi: the bias of query n at key m is slope_h * (m - n), after the scale
+    "alibi_sign": ("acc += alibi[h] * (double)(m - n);", "acc += alibi[h] * (double)(n - m);"),
+    "alibi_head_is_kv_head": ("acc += alibi[h] * (double)(m - n);", "acc += alibi[g] * (double)(m - n);"),
+    "alibi_before_scale": ("    acc *= scale;\n    if (alibi)\n        acc += alibi[h] * (double)(m - n);",
+                           "    if (alibi)\n        acc += alibi[h] * (double)(m - n);\n    acc *= scale;"),
 }
 
 
@@ -64,6 +72,8 @@ def _pins_pass():
         fd = orc.num_grad(s, q, k, v, mask, d, scale, nm)
         if np.max(np.abs(an - fd)) > 1e-5:
             return False
+    slopes = np.array([0.3, -0.2, 0.05, 0.6])
+    ga = orc.backward(s, q, k, v, mask, d, scale, alibi=slopes)
     rk2 = s.H // s.Hkv
     tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
     tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
@@ -72,9 +82,19 @@ def _pins_pass():
     S = scale * torch.matmul(tq, tk.repeat_interleave(rk2, 1).transpose(-1, -2)) + tm
     O = torch.matmul(torch.softmax(S, -1), tv.repeat_interleave(rk2, 1))
     (O * torch.tensor(d, dtype=torch.float64).permute(0, 2, 1, 3)).sum().backward()
-    return (np.max(np.abs(tq.grad.numpy() - g["dq"])) < 1e-12 and
-            np.max(np.abs(tk.grad.numpy() - g["dk"])) < 1e-12 and
-            np.max(np.abs(tv.grad.numpy() - g["dv"])) < 1e-12)
+    ok = (np.max(np.abs(tq.grad.numpy() - g["dq"])) < 1e-12 and
+          np.max(np.abs(tk.grad.numpy() - g["dk"])) < 1e-12 and
+          np.max(np.abs(tv.grad.numpy() - g["dv"])) < 1e-12)
+    # the same with per-head ALiBi slopes (bias slope_h * (m - n) after the scale)
+    tq.grad = tk.grad = tv.grad = None
+    rel = torch.arange(s.M, dtype=torch.float64)[None, :] - torch.arange(s.N, dtype=torch.float64)[:, None]
+    S = scale * torch.matmul(tq, tk.repeat_interleave(rk2, 1).transpose(-1, -2)) + \
+        torch.tensor(slopes)[:, None, None] * rel[None] + tm
+    O = torch.matmul(torch.softmax(S, -1), tv.repeat_interleave(rk2, 1))
+    (O * torch.tensor(d, dtype=torch.float64).permute(0, 2, 1, 3)).sum().backward()
+    return ok and (np.max(np.abs(tq.grad.numpy() - ga["dq"])) < 1e-12 and
+                   np.max(np.abs(tk.grad.numpy() - ga["dk"])) < 1e-12 and
+                   np.max(np.abs(tv.grad.numpy() - ga["dv"])) < 1e-12)
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))

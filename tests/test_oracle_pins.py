@@ -389,3 +389,127 @@ def test_thread_count_does_not_change_the_result():
     b = orc.backward(s, q, k, v, None, d, 0.3, nthreads=7)
     for key in a:
         assert np.array_equal(a[key], b[key])
+
+
+# ---------------------------------------------------------------- ALiBi (per-head linear bias)
+# The ggmlR test file names ALiBi only through `max_bias`, in the block "the graph
+# builder rejects attention features it cannot differentiate"; the reading taken here
+# is a caller-given slope per query head and the bias slope_h * (m - n) added to the
+# score after the scale, next to the mask.  The pins below restate that definition by
+# routes that do not go through the oracle's ALiBi code.
+
+def _alibi_mask_bits(slope, N, M, extra=None):
+    """f16 bits of slope * (m - n) (+ extra, f16 bits or None): the bias as an additive mask."""
+    n = np.arange(N)[:, None]
+    m = np.arange(M)[None, :]
+    bias = slope * (m - n).astype(np.float64)
+    assert np.array_equal(bias.astype(np.float16).astype(np.float64), bias), "bias must be exact in f16"
+    if extra is not None:
+        e = extra.view(np.float16).astype(np.float64)
+        bias = np.where(np.isneginf(e), -np.inf, bias + e)
+        assert np.array_equal(bias.astype(np.float16).astype(np.float64), bias)
+    return bias.astype(np.float16).view(np.uint16)
+
+
+def test_alibi_single_head_equals_the_additive_mask_of_its_bias():
+    # H = 1: the ALiBi bias slope * (m - n) is an additive mask, so the oracle with the
+    # slope and no mask equals the oracle with that mask and no slope (exactly: every
+    # bias value is an f16 number, and 0 is added in place of the other term)
+    s = Shape(2, 1, 1, 7, 11, 5, 3)
+    q, k, v, d = make_qkvd(s, 401)
+    a = orc.backward(s, q, k, v, None, d, 0.6, alibi=[0.25])
+    b = orc.backward(s, q, k, v, _alibi_mask_bits(0.25, s.N, s.M), d, 0.6)
+    for name in ("dq", "dk", "dv", "O", "lse"):
+        assert np.max(np.abs(a[name] - b[name])) <= 1e-13 * (1 + np.max(np.abs(b[name]))), name
+    # with a causal mask on top: the bias and the mask add
+    cm = causal_mask(s.N, s.M)
+    a = orc.backward(s, q, k, v, cm, d, 0.6, alibi=[-0.5])
+    b = orc.backward(s, q, k, v, _alibi_mask_bits(-0.5, s.N, s.M, cm), d, 0.6)
+    for name in ("dq", "dk", "dv", "O", "lse"):
+        assert np.max(np.abs(a[name] - b[name])) <= 1e-13 * (1 + np.max(np.abs(b[name]))), name
+
+
+def test_alibi_slope_belongs_to_the_query_head():
+    # grouped-query heads with different slopes: each query head h, run alone (H = 1,
+    # its key/value head, its slope as a mask) gives the same O and dQ as in the
+    # full problem; dK/dV of a group are the sums over its heads
+    s = Shape(1, 4, 2, 6, 9, 4, 4)
+    slopes = [0.5, -0.25, 0.125, 1.0]
+    q, k, v, d = make_qkvd(s, 402)
+    full = orc.backward(s, q, k, v, None, d, 0.5, alibi=slopes)
+    rk2 = s.H // s.Hkv
+    dk = np.zeros_like(full["dk"])
+    dv = np.zeros_like(full["dv"])
+    for h in range(s.H):
+        g = h // rk2
+        s1 = Shape(1, 1, 1, s.N, s.M, s.DK, s.DV)
+        one = orc.backward(s1, q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1],
+                           _alibi_mask_bits(slopes[h], s.N, s.M), d[:, :, h:h + 1], 0.5)
+        assert np.max(np.abs(one["dq"][0, 0] - full["dq"][0, h])) <= 1e-13
+        assert np.max(np.abs(one["O"][0, :, 0] - full["O"][0, :, h])) <= 1e-13
+        dk[:, g] += one["dk"][:, 0]
+        dv[:, g] += one["dv"][:, 0]
+    assert np.max(np.abs(dk - full["dk"])) <= 1e-12
+    assert np.max(np.abs(dv - full["dv"])) <= 1e-12
+
+
+def test_alibi_uniform_scores_closed_form():
+    # q = 0: the scores are the bias alone, slope * (m - n); the softmax of a row is that
+    # of slope * m (the -n term is the same for every key of the row), so
+    #   P[m] = exp(slope m) / sum exp(slope m'),  O_n = sum_m P[m] v_m for every n,
+    #   LSE_n = log sum_m exp(slope (m - n)),  dV[:, m] = P[m] sum_n d_n
+    s = Shape(1, 1, 1, 5, 8, 3, 4)
+    _, k, v, d = make_qkvd(s, 403)
+    q = np.zeros(s.q_shape, np.float32)
+    slope = 0.75
+    r = orc.backward(s, q, k, v, None, d, 0.9, alibi=[slope])
+    m = np.arange(s.M)
+    P = np.exp(slope * m) / np.exp(slope * m).sum()
+    O = P @ v[0, 0].astype(np.float64)
+    for n in range(s.N):
+        assert np.allclose(r["O"][0, n, 0], O, rtol=0, atol=1e-14)
+        assert abs(r["lse"][0, 0, n] - math.log(np.exp(slope * (m - n)).sum())) <= 1e-13
+    dsum = d[0, :, 0].astype(np.float64).sum(axis=0)
+    assert np.allclose(r["dv"][0, 0], P[:, None] * dsum[None, :], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("shape,seed,causal", [
+    (Shape(1, 1, 1, 3, 5, 4, 4), 11, False),
+    (Shape(1, 1, 1, 3, 4, 4, 4), 12, True),
+    (Shape(2, 4, 2, 2, 3, 4, 4), 13, False),
+], ids=["single_head", "causal", "gqa_batch"])
+def test_alibi_backward_matches_central_differences(shape, seed, causal):
+    # the ggmlR test's num_grad check (eps = 1e-3) of the backward against the forward,
+    # with per-head slopes: the bias enters the gradient only through P
+    s = shape
+    q, k, v, d = make_qkvd(s, seed)
+    mask = causal_mask(s.N, s.M) if causal else None
+    slopes = [0.5 - 0.3 * h for h in range(s.H)]
+    g = orc.backward(s, q, k, v, mask, d, 0.5, alibi=slopes)
+    for name, an in (("q", g["dq"]), ("k", g["dk"]), ("v", g["dv"])):
+        fd = orc.num_grad(s, q, k, v, mask, d, 0.5, name, alibi=slopes)
+        assert r_all_equal_rel(fd, an) <= 2e-2
+        assert np.max(np.abs(an - fd)) <= 1e-6, name
+
+
+def test_alibi_against_torch_float64_autograd():
+    torch = pytest.importorskip("torch")
+    s = Shape(2, 4, 2, 9, 13, 6, 5)
+    q, k, v, d = make_qkvd(s, 404)
+    mask = random_mask(s.N, s.M, 404, p_inf=0.2, full_rows=0, full_cols=1)
+    slopes = np.array([0.3, -0.2, 0.05, 0.6])
+    scale = 0.4
+    g = orc.backward(s, q, k, v, mask, d, scale, alibi=slopes)
+    rk2 = s.H // s.Hkv
+    tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    tm = torch.tensor(mask.view(np.float16).astype(np.float64))
+    rel = torch.arange(s.M, dtype=torch.float64)[None, :] - torch.arange(s.N, dtype=torch.float64)[:, None]
+    bias = torch.tensor(slopes)[:, None, None] * rel[None]                          # (H, N, M)
+    S = scale * torch.matmul(tq, tk.repeat_interleave(rk2, 1).transpose(-1, -2)) + bias + tm
+    O = torch.matmul(torch.softmax(S, -1), tv.repeat_interleave(rk2, 1))
+    (O * torch.tensor(d, dtype=torch.float64).permute(0, 2, 1, 3)).sum().backward()
+    assert np.max(np.abs(tq.grad.numpy() - g["dq"])) < 1e-12
+    assert np.max(np.abs(tk.grad.numpy() - g["dk"])) < 1e-12
+    assert np.max(np.abs(tv.grad.numpy() - g["dv"])) < 1e-12
