@@ -35,7 +35,7 @@ FAB_E_HIP = -5
 
 # every symbol include/fab.h declares
 EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
-           "fab_backward_noalloc", "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
+           "fab_forward_lse_alibi", "fab_backward_alibi", "fab_backward_noalloc", "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
            "fab_strerror", "fab_last_error", "fab_version")
 KERNELS = ("block_map", "forward", "prep", "pack", "backward", "dq", "gqa_reduce")
 
@@ -72,6 +72,10 @@ def lib():
         L.fab_forward_lse.argtypes = [SP, P, P, P, P, ctypes.c_float, I, P, P, P, SZ, P]
         L.fab_backward.restype = I
         L.fab_backward.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, P, SZ, P]
+        L.fab_forward_lse_alibi.restype = I
+        L.fab_forward_lse_alibi.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, SZ, P]
+        L.fab_backward_alibi.restype = I
+        L.fab_backward_alibi.argtypes = [SP, P, P, P, P, P, P, ctypes.c_float, I, P, P, P, P, SZ, P]
         L.fab_backward_noalloc.restype = I
         L.fab_backward_noalloc.argtypes = [SP, P, P, P, P, P, ctypes.c_float, I, P, P, P, P]
         L.fab_strerror.restype = ctypes.c_char_p
@@ -196,6 +200,13 @@ def _check_mask(mask, s):
     return mask
 
 
+def _check_alibi(alibi, s):
+    """Per-query-head ALiBi slopes: float32 (H,), contiguous, or None."""
+    if alibi is not None:
+        _check_tensor(alibi, "alibi", (s.H,))
+    return alibi
+
+
 def _check_ws(ws, need):
     """A caller's workspace: contiguous, at least `need` bytes; returns its byte size."""
     if not ws.is_contiguous():
@@ -222,10 +233,12 @@ def _on_stream(stream):
     return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
-def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False):
+def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False,
+                alibi=None):
     """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v.
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v
-    are float32, or bfloat16 (all three; mode "bf16")."""
+    are float32, or bfloat16 (all three; mode "bf16").  alibi: float32 (H,) per-head
+    slopes, adding alibi[h] * (m - n) to the score of query n at key m, or None."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
@@ -234,13 +247,14 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
     _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
     mask = _check_mask(mask, s)
+    alibi = _check_alibi(alibi, s)
     if O is not None:
         _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
     if lse is not None:
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
     if ws is not None:
         nbytes = _check_ws(ws, workspace_bytes(s, mode, mask is not None, True, causal))
-    _check_devices(dev, k=k, v=v, mask=mask, O=O, lse=lse, ws=ws)
+    _check_devices(dev, k=k, v=v, mask=mask, alibi=alibi, O=O, lse=lse, ws=ws)
     with _on_stream(stream):
         if O is None:
             O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
@@ -248,18 +262,19 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
             lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
-        _check(lib().fab_forward_lse(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
-                                     float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(ws),
-                                     nbytes, _stream_handle(stream)))
+        _check(lib().fab_forward_lse_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
+                                           float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse),
+                                           _ptr(ws), nbytes, _stream_handle(stream)))
     return O, lse
 
 
 def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=None, ws=None,
-             stream=None, causal=False):
+             stream=None, causal=False, alibi=None):
     """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
     are float32, or bfloat16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
-    float32, are both given (from forward_lse) or both None."""
+    float32, are both given (from forward_lse, with the same alibi) or both None.
+    alibi: float32 (H,) per-head ALiBi slopes or None (see forward_lse)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
@@ -269,6 +284,7 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
     _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
     _check_tensor(d, "d", (s.B, s.N, s.H, s.DV), (q.dtype,))
     mask = _check_mask(mask, s)
+    alibi = _check_alibi(alibi, s)
     if (O is None) != (lse is None):
         raise ValueError("O and lse must be given together or both be None")
     if O is not None:
@@ -281,15 +297,15 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
             raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
     if ws is not None:
         nbytes = _check_ws(ws, workspace_bytes(s, mode, mask is not None, O is not None, causal))
-    _check_devices(dev, k=k, v=v, d=d, mask=mask, O=O, lse=lse, blob=blob, ws=ws)
+    _check_devices(dev, k=k, v=v, d=d, mask=mask, alibi=alibi, O=O, lse=lse, blob=blob, ws=ws)
     with _on_stream(stream):
         if blob is None:
             blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
-        _check(lib().fab_backward(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                                  float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
-                                  _ptr(ws), nbytes, _stream_handle(stream)))
+        _check(lib().fab_backward_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
+                                        _ptr(d), float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse),
+                                        _ptr(blob), _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 
 

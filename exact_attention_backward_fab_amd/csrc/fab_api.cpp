@@ -196,6 +196,14 @@ int check_ptr(const void *p, int64_t elems, const char *name)
     return FAB_OK;
 }
 
+// ALiBi slopes: a device array of H floats, or NULL for none.
+int check_alibi(const float *alibi)
+{
+    if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u) != 0)
+        return fail(FAB_E_ALIGN, "alibi is not 4-byte aligned");
+    return FAB_OK;
+}
+
 int check_ws(const void *ws, size_t ws_bytes, size_t need)
 {
     if (need == 0) return FAB_OK;
@@ -403,9 +411,9 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     return FAB_OK;
 }
 
-int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
-                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
-                    size_t ws_bytes, void *stream)
+int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
+                          const uint16_t *mask, const float *alibi, float scale, int mode, float *O, float *lse,
+                          void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
@@ -413,8 +421,10 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
     bool causal, in_bf16;
     FAB_TRY(take_mode(&mode, &causal, &in_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
+    FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
     pl.d.in_bf16 = in_bf16;
+    pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     FAB_TRY(check_ptr(q, pl.nq, "q"));
     FAB_TRY(check_ptr(k, pl.nk, "k"));
@@ -442,9 +452,9 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
     return FAB_OK;
 }
 
-int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
-                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
-                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
+                       const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
+                       const float *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
@@ -452,8 +462,10 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
     bool causal, in_bf16;
     FAB_TRY(take_mode(&mode, &causal, &in_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
+    FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
     pl.d.in_bf16 = in_bf16;
+    pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     if ((O == nullptr) != (lse == nullptr))
         return fail(FAB_E_INVAL, "O and lse must be given together or both be NULL");
@@ -554,6 +566,20 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
                    "dK/dV reduce launch");
     }
     return FAB_OK;
+}
+
+int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
+                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
+                    size_t ws_bytes, void *stream)
+{
+    return fab_forward_lse_alibi(shape, q, k, v, mask, nullptr, scale, mode, O, lse, ws, ws_bytes, stream);
+}
+
+int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
+                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+{
+    return fab_backward_alibi(shape, q, k, v, mask, nullptr, d, scale, mode, O, lse, blob, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

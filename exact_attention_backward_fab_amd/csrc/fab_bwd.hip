@@ -42,6 +42,7 @@ struct BwdArgs {
     int part_heads, nqb, nkb, vecK, vecV;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
+    const float *alibi;             // per-head ALiBi slopes [H] or NULL
 };
 
 // ============================================================== bf16 mode
@@ -73,6 +74,7 @@ struct KvArgs {
     int part_heads, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
+    const float *alibi;             // per-head ALiBi slopes [H] or NULL
 };
 
 // 8 waves, two per SIMD: wave w owns keys 32 (w & 3).. of the block and the
@@ -94,7 +96,7 @@ struct KStages {
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(KvArgs p)
 {
     using ST = KStages<DKP, DVP>;
@@ -196,6 +198,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int hh = 0; hh < p.hpw; ++hh) {
         const int hb = hp * p.hpw + hh + p.H * b;   // this head (h + H b)
         set_head(hb);
+        const float slope2 = AB ? p.alibi[hb % p.H] * kLog2e : 0.f;   // ALiBi, log2 units
         for (int seg = 0; seg < nqt; seg += kKList) {
             const int count = build_live_list<kKW>(sList, sCount, seg, min(seg + kKList, nqt), tid, lane, w, [&](int it) {
                 return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
                 // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
                 // every key visible folds the scale into the exponent
-                const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
+                const bool fast = cls == kTileFree && key0 + kKBC <= p.M && (!AB || slope2 == 0.f);
                 const float mul = fast ? sl2 : 1.f;
                 const int qb = q0 + 32 * qq;   // first query of this wave's half
                 if (!fast) {
@@ -242,6 +245,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int r = 0; r < 16; ++r) {
                         const float x = sacc[r] * sl2 + kbias;
                         sacc[r] = (qb + crow(r, half) >= thr) ? x : -INFINITY;
+                    }
+                    if (AB && slope2 != 0.f) {   // ALiBi: + slope (key - query)
+                        const float ab = slope2 * (float)(mykey - qb);
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) sacc[r] += __builtin_fmaf(-slope2, (float)crow(r, half), ab);
                     }
                     if (cls == kTileMixed) {
                         const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
@@ -385,7 +393,7 @@ struct KStages4 {
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_w4_kernel(KvArgs p)
 {
     using ST = KStages4<DKP, DVP>;
@@ -419,6 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int mykey = key0 + 32 * w + l32;  // this lane's key in the C layout of S and dP
     const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
     const float sl2 = p.scale * kLog2e;
+    const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
 
     // ---- this lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[DKP / 16], vf[DVP / 16];
@@ -505,7 +514,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
             // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
             // every key visible folds the scale into the exponent
-            const bool fast = cls == kTileFree && key0 + kKBC <= p.M;
+            const bool fast = cls == kTileFree && key0 + kKBC <= p.M && (!AB || slope2 == 0.f);
             const float mul = fast ? sl2 : 1.f;
             if (!fast) {
                 const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
@@ -516,6 +525,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         const float x = sacc[qq][r] * sl2 + kbias;
                         sacc[qq][r] = (q0 + 32 * qq + crow(r, half) >= thr) ? x : -INFINITY;
                     }
+                if (AB && slope2 != 0.f) {   // ALiBi: + slope (key - query)
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq) {
+                        const float ab = slope2 * (float)(mykey - q0 - 32 * qq);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            sacc[qq][r] += __builtin_fmaf(-slope2, (float)crow(r, half), ab);
+                    }
+                }
                 if (cls == kTileMixed) {
                     const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
 #pragma unroll
@@ -614,7 +632,7 @@ struct F32Cfg {
     static constexpr int LK = DKP + 4, LV = DVP + 4, LQ = DKP + 4, LO = DVP + 4, LS = BC + 4;
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdArgs p)
 {
     using C = F32Cfg<DKP, DVP>;
@@ -663,6 +681,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
 #pragma unroll
     for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
     const float sl2 = p.scale * kLog2e;
+    const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const int nqt = (p.N + BR - 1) / BR;
 
     // Live query steps only.  Where the registers allow it (PF), the rows of the
@@ -786,6 +805,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             for (int c = 0; c < 4; ++c) {
                 const int r = 4 * r4 + c, n = q0 + qr + c;
                 float x = sacc[r] * sl2;
+                if (AB && slope2 != 0.f) x += slope2 * (float)(mykey - n);
                 if (cls == kTileCausal) {
                     x = (mykey <= n) ? x : -INFINITY;
                 } else if (cls == kTileMixed) {
@@ -900,8 +920,12 @@ hipError_t run_bwd_f32(const BwdArgs &a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         using C = F32Cfg<DKP, DVP>;
-        hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
-                           0, s, a);
+        if (a.alibi)
+            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, true>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
+                               0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, false>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
+                               0, s, a);
         return hipGetLastError();
     }
 }
@@ -912,12 +936,18 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else if constexpr (DKP + DVP <= 256) {
-        hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B), dim3(kKNT), 0,
-                           s, a);
+        const dim3 grid(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B);
+        if (a.alibi)
+            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, true>), grid, dim3(kKNT), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, false>), grid, dim3(kKNT), 0, s, a);
         return hipGetLastError();
     } else {
-        hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP>), dim3(ceil_div(a.M, kKBC) * a.H * a.B), dim3(kKNT4), 0, s,
-                           a);
+        const dim3 grid(ceil_div(a.M, kKBC) * a.H * a.B);
+        if (a.alibi)
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true>), grid, dim3(kKNT4), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false>), grid, dim3(kKNT4), 0, s, a);
         return hipGetLastError();
     }
 }
@@ -935,7 +965,7 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
     a.lse = lse; a.delta = delta; a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_bwd_f32, a, s, hd, false);
@@ -956,7 +986,7 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     if (part_heads != (d.H / d.Hkv / a.hpw > 1 ? 1 : 0)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_bwd_bf16, a, s, hd, true);
 }

@@ -22,6 +22,7 @@ struct FwdArgs {
     int causal;                     // causal rule as a flag (no mask, no map)
     int fold;                       // the whole grid is resident at once (query_block_work)
     float scale;
+    const float *alibi;             // per-head ALiBi slopes [H] or NULL
 };
 
 template <int DKP, int DVP>
@@ -41,7 +42,7 @@ struct FwdF32Occ {
     static constexpr int v = DKP + DVP <= 256 ? 2 : 1;
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__(256, (FwdF32Occ<DKP, DVP>::v))
 __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::v))) void fwd_f32_kernel(FwdArgs p)
 {
@@ -76,6 +77,7 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
     for (int i = 0; i < DVP / 32; ++i) oacc[i] = zero16();
     float m_run = -INFINITY, l_half = 0.f;
     const float sl2 = p.scale * kLog2e;
+    const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const int nkt_total = (p.M + BC - 1) / BC;
 
     for (int kt = 0; kt < nkt_total; ++kt) {
@@ -119,6 +121,7 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + kk * 32 + crow(r, half);
                 float x = s[kk][r] * sl2;
+                if (AB && slope2 != 0.f) x += slope2 * (float)(key - n);
                 if (cls == kTileMixed && nok && key < p.M)
                     x += half_bits_to_float(p.mask[key + (size_t)p.M * n]) * kLog2e;
                 if (key >= p.M || !nok || (cls == kTileCausal && key > n)) x = -INFINITY;
@@ -198,8 +201,12 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t s)
         const int grid = ceil_div(a.N, C::BR) * a.H * a.B;
         static ResidentCache slots;
         FwdArgs b = a;
-        b.fold = grid <= slots.get(reinterpret_cast<const void *>(&fwd_f32_kernel<DKP, DVP>), C::NT);
-        hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP>), dim3(grid), dim3(C::NT), 0, s, b);
+        // (both instantiations have the same resources: one occupancy query)
+        b.fold = grid <= slots.get(reinterpret_cast<const void *>(&fwd_f32_kernel<DKP, DVP, false>), C::NT);
+        if (a.alibi)
+            hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP, true>), dim3(grid), dim3(C::NT), 0, s, b);
+        else
+            hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP, false>), dim3(grid), dim3(C::NT), 0, s, b);
         return hipGetLastError();
     }
 }
@@ -214,7 +221,7 @@ hipError_t launch_forward_f32(const float *q, const float *k, const float *v, co
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.fold = 0;
     a.scale = scale;

@@ -14,6 +14,7 @@ struct Dims {
     int B, H, Hkv, N, M, DK, DV;
     int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
     int in_bf16 = 0;  // q, k, v and d are bf16 (bf16 mode only); otherwise f32
+    const float *alibi = nullptr;   // per-query-head ALiBi slopes [H] (device) or NULL: score += slope_h (m - n)
 };
 
 // Padded head dimensions (DKP, DVP) the kernels are instantiated for; a shape

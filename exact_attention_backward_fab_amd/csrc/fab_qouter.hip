@@ -167,12 +167,13 @@ __device__ __forceinline__ f32x16 st_tile(const char *Kb, const bf16x8 *qf, int 
 }
 
 // Scaled scores (log2 units) of NT 32-key sub-tiles from key0 on for the lane's
-// query: keys past lim get -inf; MIXED steps add the mask row of the query.  A
+// query myq: keys past lim get -inf; with ALiBi (slope2 != 0, log2 units) the
+// bias slope2 (key - myq) is added; MIXED steps add the mask row of the query.  A
 // lane's keys come in runs of 4 (slots 4j..4j+3), read as one 8-byte load when
 // vecM (M % 4 == 0).
-template <int NT>
+template <int NT, bool AB = false>
 __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bool mixed, const uint16_t *mrow, int M,
-                                               bool vecM, float sl2, int half)
+                                               bool vecM, float sl2, int half, float slope2 = 0.f, int myq = 0)
 {
 #pragma unroll
     for (int kk = 0; kk < NT; ++kk)
@@ -181,6 +182,13 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
             const float x = st[kk][r] * sl2;
             st[kk][r] = (key0 + kk * 32 + crow(r, half) <= lim) ? x : -INFINITY;
         }
+    if (AB && slope2 != 0.f) {   // ALiBi: + slope (key - query), in log2 units
+        const float ab = slope2 * (float)(key0 - myq);
+#pragma unroll
+        for (int kk = 0; kk < NT; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[kk][r] += __builtin_fmaf(slope2, (float)(kk * 32 + crow(r, half)), ab);
+    }
     if (mixed) {
         uint16_t m[NT][16];
 #pragma unroll
@@ -217,6 +225,7 @@ struct FwdArgs16 {
     int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK, vecV;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
+    const float *alibi;             // per-head ALiBi slopes [H] or NULL
     // The backward's own forward (PREP) writes, instead of O and lse, what the
     // backward kernels read: the bf16 tiles of Q and dO (rows >= N and columns
     // >= DK / DV zero), the LSE/D blocks (D = rowsum(dO o O)), and it zeroes the
@@ -231,7 +240,7 @@ struct FwdArgs16 {
     int fold;                       // the whole grid is resident at once (query_block_work)
 };
 
-template <int DKP, int DVP, bool PREP>
+template <int DKP, int DVP, bool PREP, bool AB>
 __global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
 __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
 {
@@ -275,6 +284,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     for (int i = 0; i < DVP / 32; ++i) oacc[i] = zero16();
     float m_run = -INFINITY, l_part = 0.f;   // reference max (log2 units), this half's running sum
     const float sl2 = p.scale * kLog2e;
+    const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const uint16_t *mrow = p.mask + (size_t)p.M * min(myq, p.N - 1);
 
     stream_key_steps<DKP, DVP>(
@@ -291,9 +301,10 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             // scores in log2 units = st * mul: a step with every key visible (FREE and
             // inside M) keeps the raw products and folds the scale into the exponent
             float mul = sl2;
-            if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f)) {
+            if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f && (!AB || slope2 == 0.f))) {
                 const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
-                scale_and_mask<2>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                scale_and_mask<2, AB>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half, slope2,
+                                  myq);
                 mul = 1.f;
             }
 
@@ -415,9 +426,10 @@ struct DqArgs {
     int causal;                     // causal rule as a flag (no mask, no map)
     int split;                      // work-groups per query block (1 or 2)
     float scale;
+    const float *alibi;             // per-head ALiBi slopes [H] or NULL
 };
 
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
 __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void dq_bf16_kernel(DqArgs p)
 {
@@ -471,6 +483,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 #pragma unroll
     for (int i = 0; i < DKP / 32; ++i) dqacc[i] = zero16();
     const float sl2 = p.scale * kLog2e;
+    const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const uint16_t *mrow = p.mask + (size_t)p.M * min(myq, p.N - 1);
 
     stream_key_steps<DKP, DVP>(
@@ -497,9 +510,10 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             // ---- P and dS; keys past M and (causal steps) keys after the query get -inf;
             // a step with every key visible folds the scale into the exponent
             float mul = sl2;
-            if (!(cls == kTileFree && key0 + kQBK <= p.M)) {
+            if (!(cls == kTileFree && key0 + kQBK <= p.M && (!AB || slope2 == 0.f))) {
                 const int lim = min(cls == kTileCausal ? myq : INT_MAX, p.M - 1);
-                scale_and_mask<2>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half);
+                scale_and_mask<2, AB>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half, slope2,
+                                  myq);
                 mul = 1.f;
             }
 #pragma unroll
@@ -756,8 +770,11 @@ hipError_t run_dq(const DqArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((dq_bf16_kernel<DKP, DVP>), dim3(ceil_div(a.N, kQBQ) * a.H * a.B * a.split), dim3(kQNT),
-                           0, s, a);
+        const dim3 grid(ceil_div(a.N, kQBQ) * a.H * a.B * a.split);
+        if (a.alibi)
+            hipLaunchKernelGGL((dq_bf16_kernel<DKP, DVP, true>), grid, dim3(kQNT), 0, s, a);
+        else
+            hipLaunchKernelGGL((dq_bf16_kernel<DKP, DVP, false>), grid, dim3(kQNT), 0, s, a);
         return hipGetLastError();
     }
 }
@@ -771,12 +788,21 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
         const int grid = ceil_div(a.N, kQBQ) * a.H * a.B;
         static ResidentCache slots_prep, slots_fwd;
         FwdArgs16 b = a;
+        // (the ALiBi instantiations share the plain ones' occupancy query)
         if (a.dO) {
-            b.fold = grid <= slots_prep.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, true>), kQNT);
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true>), dim3(grid), dim3(kQNT), 0, s, b);
+            b.fold = grid <= slots_prep.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, true, false>),
+                                            kQNT);
+            if (a.alibi)
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true, true>), dim3(grid), dim3(kQNT), 0, s, b);
+            else
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true, false>), dim3(grid), dim3(kQNT), 0, s, b);
         } else {
-            b.fold = grid <= slots_fwd.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, false>), kQNT);
-            hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false>), dim3(grid), dim3(kQNT), 0, s, b);
+            b.fold = grid <= slots_fwd.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, false, false>),
+                                           kQNT);
+            if (a.alibi)
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false, true>), dim3(grid), dim3(kQNT), 0, s, b);
+            else
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false, false>), dim3(grid), dim3(kQNT), 0, s, b);
         }
         return hipGetLastError();
     }
@@ -792,7 +818,7 @@ hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v
     FwdArgs16 a = {};
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
@@ -809,7 +835,7 @@ hipError_t launch_forward_prep_bf16(const void *q, const __bf16 *k16, const __bf
     FwdArgs16 a = {};
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
     a.scale = scale;
     a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
@@ -832,7 +858,7 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
     a.dq = dq; a.part = part; a.ticket = ticket; a.split = dq_split(d);
     if (a.split == 2 && (!part || !ticket)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
-    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal;
+    a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_dq, a, s, hd, true);
 }

@@ -145,6 +145,27 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
                  const uint16_t *mask, const void *d, float scale, int mode, const float *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
 
+/* ALiBi: fab_forward_lse and fab_backward with a linear per-head bias on the
+ * scores.  The ggmlR test file names ALiBi only through `max_bias`, in its block
+ * "the graph builder rejects attention features it cannot differentiate", and
+ * gives no score function; the reading taken here: the caller passes one slope
+ * per query head, and the score of query n at key m becomes
+ *     scale * (q . k) + alibi[h] * (m - n) + mask[m, n]
+ * (the bias after the scale, next to the mask; softmax, LSE and the backward
+ * formulas unchanged).  ggml's geometric slopes (from max_bias) or any others are
+ * the caller's choice.
+ *   alibi   device f32 [H] (read only, 4-byte aligned) or NULL: then these calls
+ *           are exactly fab_forward_lse / fab_backward.  Finite slopes only.
+ * Every other argument, the workspace and the errors are as for fab_forward_lse /
+ * fab_backward; O and lse passed to fab_backward_alibi must come from the forward
+ * with the same slopes. */
+int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
+                          const uint16_t *mask, const float *alibi, float scale, int mode, float *O, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
+                       const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
+                       const float *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
+
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: fab_backward
  * (same arguments, kernels and results, same validation and error codes) with

@@ -173,3 +173,15 @@ def test_noalloc_rejects_before_device_work():
                                 P(FAKE), None)
     assert rc == fab.FAB_E_INVAL
     assert fab.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_alibi_entry_points_reject_a_misaligned_slope_array():
+    L = fab.lib()
+    P = ctypes.c_void_p
+    sh = fab.FabShape(*GOOD)
+    rc = L.fab_backward_alibi(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE + 2), P(FAKE), 0.5, 0,
+                              None, None, P(FAKE), P(FAKE), 1 << 40, None)
+    assert rc == fab.FAB_E_ALIGN and "alibi" in L.fab_last_error().decode()
+    rc = L.fab_forward_lse_alibi(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE + 1), 0.5, 0, P(FAKE),
+                                 P(FAKE), P(FAKE), 1 << 40, None)
+    assert rc == fab.FAB_E_ALIGN

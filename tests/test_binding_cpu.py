@@ -42,6 +42,8 @@ BAD = [
     ("blob_strided", dict(blob=torch.zeros(20_000)[::2]), ValueError, "blob"),
     ("ws_strided", dict(ws=torch.zeros(1 << 20, dtype=torch.uint8)[::2]), ValueError, "ws"),
     ("ws_short", dict(ws=torch.zeros(16, dtype=torch.uint8)), ValueError, "ws"),
+    ("alibi_shape", dict(alibi=torch.zeros(S.H + 1)), ValueError, "alibi"),
+    ("alibi_dtype", dict(alibi=torch.zeros(S.H, dtype=torch.float64)), TypeError, "alibi"),
     ("cpu_tensors", dict(), ValueError, "GPU"),
 ]
 
