@@ -136,6 +136,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int mykey = key0 + 32 * kw + l32;  // this lane's key in the C layout of S and dP
     const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
     const float sl2 = p.scale * kLog2e;
+    const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
 
     // ---- the block's K and V rows (B operands of S = Q K^T and dP = dO V^T, one key
     // per lane) into LDS: 2 tiles of each, copied by chunk columns
@@ -219,26 +220,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const char *Ob = Qb + ST::kQ;
                 const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
 
+                const int qb = q0 + 32 * qq;   // first query of this wave's half
+
                 // ---- S = Q K^T and dP = dO V^T for this wave's 32 queries (lane = key)
                 f32x16 sacc = zero16(), pacc = zero16();
                 {
-                    bf16x8 a[DKP / 16];
+                    // the LDS operands run R products ahead of the matrix cores (a ring of
+                    // registers; the scheduling barriers keep the compiler from folding it back
+                    // into read-wait-multiply pairs), S and dP products alternating
+                    constexpr int TS = DKP / 16, TP = DVP / 16, T = TS > TP ? TS : TP, R = 2;
+                    bf16x8 qa[R], ka[R], oa[R], va[R];
+                    const char *Qrow = Qb + row_off + 512 * qq, *Orow = Ob + row_off + 512 * qq;
     #pragma unroll
-                    for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
-    #pragma unroll
-                    for (int t = 0; t < DKP / 16; ++t) sacc = mfma_bf16(a[t], lds_row8(Krow + 2304 * t), sacc);
-                    bf16x8 o[DVP / 16];
-    #pragma unroll
-                    for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
-    #pragma unroll
-                    for (int t = 0; t < DVP / 16; ++t) pacc = mfma_bf16(o[t], lds_row8(Vrow + 2304 * t), pacc);
+                    for (int t = 0; t < T + R; ++t) {
+                        if (t >= R) {
+                            const int u = t - R;
+                            if (u < TS) sacc = mfma_bf16(qa[u % R], ka[u % R], sacc);
+                            if (u < TP) pacc = mfma_bf16(oa[u % R], va[u % R], pacc);
+                        }
+                        if (t < TS) { qa[t % R] = lds_row8(Qrow + 2304 * t); ka[t % R] = lds_row8(Krow + 2304 * t); }
+                        if (t < TP) { oa[t % R] = lds_row8(Orow + 2304 * t); va[t % R] = lds_row8(Vrow + 2304 * t); }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
 
                 // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
                 // every key visible folds the scale into the exponent
                 const bool fast = cls == kTileFree && key0 + kKBC <= p.M && (!AB || slope2 == 0.f);
                 const float mul = fast ? sl2 : 1.f;
-                const int qb = q0 + 32 * qq;   // first query of this wave's half
                 if (!fast) {
                     const int thr = cls == kTileCausal ? mykey : INT_MIN;   // causal: query >= key
     #pragma unroll
@@ -251,14 +260,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     #pragma unroll
                         for (int r = 0; r < 16; ++r) sacc[r] += __builtin_fmaf(-slope2, (float)crow(r, half), ab);
                     }
-                    if (cls == kTileMixed) {
-                        const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
-    #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int n = min(qb + crow(r, half), p.N - 1);
-                            sacc[r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
-                        }
-                    }
+                    if (cls == kTileMixed)   // this lane's 16 mask entries, all loads in flight at once
+                        add_mask_column(sacc, rmask, mykey, qb, half, p.N, p.M);
                 }
     #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
@@ -299,17 +302,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
                     __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));
                 }
+                {
+                    // the transposed operands of both halves' dV and dK products in one
+                    // sequence, read R2 products ahead
+                    constexpr int NV = DVP / 32, NK = DKP / 32, NJ = 2 * (NV + NK), R2 = 3;
+                    bf16x8 br[R2];
     #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    bf16x8 bo[DVP / 32], bq[DKP / 32];
-    #pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
-    #pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa[u], bo[dt], dvacc[dt]);
-    #pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
-    #pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da[u], bq[dt], dkacc[dt]);
+                    for (int j = 0; j < NJ + R2; ++j) {
+                        if (j >= R2) {
+                            const int i = j - R2, u = i / (NV + NK), c = i % (NV + NK);
+                            if (c < NV) dvacc[c] = mfma_bf16(pa[u], br[i % R2], dvacc[c]);
+                            else dkacc[c - NV] = mfma_bf16(da[u], br[i % R2], dkacc[c - NV]);
+                        }
+                        if (j < NJ) {
+                            const int u = j / (NV + NK), c = j % (NV + NK);
+                            br[j % R2] = c < NV ? lds_tr8(Ob + tr_off + 4608 * c + 512 * qq + 256 * u)
+                                                : lds_tr8(Qb + tr_off + 4608 * (c - NV) + 512 * qq + 256 * u);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
             __syncthreads();   // every wave is done with the stages before they are refilled
@@ -428,6 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
     const float sl2 = p.scale * kLog2e;
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
+    const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
 
     // ---- this lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[DKP / 16], vf[DVP / 16];
@@ -494,22 +506,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const char *Ob = Qb + ST::kQ;
             const float *Sb = reinterpret_cast<const float *>(Ob + ST::kO);
 
-            // ---- S = Q K^T and dP = dO V^T for two 32-query sub-tiles (lane = key)
+            // ---- S = Q K^T and dP = dO V^T for two 32-query sub-tiles (lane = key); the Q
+            // and dO row operands run R products ahead of the matrix cores (a register ring
+            // held in place by scheduling barriers), S and dP products alternating
             f32x16 sacc[2], pacc[2];
+            {
+                constexpr int TS = DKP / 16, TP = DVP / 16, T = TS > TP ? TS : TP, R = 3, NJ = 2 * T;
+                bf16x8 qa[R], oa[R];
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                sacc[qq] = zero16();
-                pacc[qq] = zero16();
-                bf16x8 a[DKP / 16];
+                for (int qq = 0; qq < 2; ++qq) {
+                    sacc[qq] = zero16();
+                    pacc[qq] = zero16();
+                }
 #pragma unroll
-                for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
-#pragma unroll
-                for (int t = 0; t < DKP / 16; ++t) sacc[qq] = mfma_bf16(a[t], kf[t], sacc[qq]);
-                bf16x8 o[DVP / 16];
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) o[t] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) pacc[qq] = mfma_bf16(o[t], vf[t], pacc[qq]);
+                for (int j = 0; j < NJ + R; ++j) {
+                    if (j >= R) {
+                        const int i = j - R, qq = i / T, t = i % T;
+                        if (t < TS) sacc[qq] = mfma_bf16(qa[i % R], kf[t], sacc[qq]);
+                        if (t < TP) pacc[qq] = mfma_bf16(oa[i % R], vf[t], pacc[qq]);
+                    }
+                    if (j < NJ) {
+                        const int qq = j / T, t = j % T;
+                        if (t < TS) qa[j % R] = lds_row8(Qb + row_off + 512 * qq + 2304 * t);
+                        if (t < TP) oa[j % R] = lds_row8(Ob + row_off + 512 * qq + 2304 * t);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
 
             // ---- P = exp(scale S + mask - LSE) and dS = P o (dP - D), in f32; a step with
@@ -535,14 +557,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                 }
                 if (cls == kTileMixed) {
-                    const uint16_t *mcol = p.mask + min(mykey, p.M - 1);   // clamped: always in bounds
 #pragma unroll
-                    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int n = min(q0 + 32 * qq + crow(r, half), p.N - 1);
-                            sacc[qq][r] += half_bits_to_float(mcol[(size_t)p.M * n]) * kLog2e;
-                        }
+                    for (int qq = 0; qq < 2; ++qq) add_mask_column(sacc[qq], rmask, mykey, q0 + 32 * qq, half, p.N, p.M);
                 }
             }
 #pragma unroll
@@ -563,6 +579,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
             // ---- dV += P^T dO and dK += dS^T Q (lane = head-dim column, rows = keys):
             // A = P^T / dS^T in operand order, B = dO / Q by transposing reads
+            bf16x8 pa4[4], da4[4];   // index 2 qq + u
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
@@ -574,16 +591,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         dv8[i] = pacc[qq][8 * u + i];
                     }
                     const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
-                    bf16x8 bo[DVP / 32], bq[DKP / 32];
-#pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt) bo[dt] = lds_tr8(Ob + tr_off + 4608 * dt + 512 * qq + 256 * u);
-#pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt) dvacc[dt] = mfma_bf16(pa, bo[dt], dvacc[dt]);
-#pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt) bq[dt] = lds_tr8(Qb + tr_off + 4608 * dt + 512 * qq + 256 * u);
-#pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt) dkacc[dt] = mfma_bf16(da, bq[dt], dkacc[dt]);
+                    pa4[2 * qq + u] = pa;
+                    da4[2 * qq + u] = da;
                 }
+            {
+                // the transposed operands of the four (half, u) groups' dV and dK products in
+                // one sequence, read R2 products ahead
+                constexpr int NV = DVP / 32, NK = DKP / 32, NC = NV + NK, NJ = 4 * NC, R2 = 4;
+                bf16x8 br[R2];
+#pragma unroll
+                for (int j = 0; j < NJ + R2; ++j) {
+                    if (j >= R2) {
+                        const int i = j - R2, gq = i / NC, c = i % NC;
+                        if (c < NV) dvacc[c] = mfma_bf16(pa4[gq], br[i % R2], dvacc[c]);
+                        else dkacc[c - NV] = mfma_bf16(da4[gq], br[i % R2], dkacc[c - NV]);
+                    }
+                    if (j < NJ) {
+                        const int gq = j / NC, c = j % NC, qq = gq >> 1, u = gq & 1;
+                        br[j % R2] = c < NV ? lds_tr8(Ob + tr_off + 4608 * c + 512 * qq + 256 * u)
+                                            : lds_tr8(Qb + tr_off + 4608 * (c - NV) + 512 * qq + 256 * u);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
         __syncthreads();   // every wave is done with the stages before they are refilled
     }
@@ -682,6 +712,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
     const float sl2 = p.scale * kLog2e;
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
+    const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
     const int nqt = (p.N + BR - 1) / BR;
 
     // Live query steps only.  Where the registers allow it (PF), the rows of the
@@ -795,7 +826,11 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
                 for (int i = 0; i < 4; ++i) pacc = mfma_f32(a[i], bv[i], pacc);
             }
         }
-        // ---- P and dS
+        // ---- P and dS (scores in log2 units; a MIXED step adds the lane's mask column with
+        // all 16 loads in flight at once -- rows past N carry no weight through their LSE)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] *= sl2;
+        if (cls == kTileMixed) add_mask_column(sacc, rmask, mykey, q0 + 32 * qq, half, p.N, p.M);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int qr = 32 * qq + 8 * r4 + 4 * half;
@@ -804,13 +839,9 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int r = 4 * r4 + c, n = q0 + qr + c;
-                float x = sacc[r] * sl2;
+                float x = sacc[r];
                 if (AB && slope2 != 0.f) x += slope2 * (float)(mykey - n);
-                if (cls == kTileCausal) {
-                    x = (mykey <= n) ? x : -INFINITY;
-                } else if (cls == kTileMixed) {
-                    if (n < p.N && keyok) x += half_bits_to_float(p.mask[mykey + (size_t)p.M * n]) * kLog2e;
-                }
+                if (cls == kTileCausal) x = (mykey <= n) ? x : -INFINITY;
                 const float P = keyok ? fast_exp2(x - lse4[c]) : 0.f;
                 sacc[r] = P;
                 pacc[r] = P * (pacc[r] - del4[c]);

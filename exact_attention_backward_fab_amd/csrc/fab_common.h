@@ -117,6 +117,10 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
+__device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+}
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t byte_off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
@@ -221,6 +225,28 @@ __device__ __forceinline__ f32x4 load_row4_any(const void *base, int64_t elem_of
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// The mask [N][M] (f16 bits) as a buffer resource: it holds below 2^31 entries, so its
+// byte offsets fit 32 bits.
+__device__ __forceinline__ rsrc_t mask_rsrc(const uint16_t *mask, int N, int M)
+{
+    return make_rsrc(mask, mask ? (uint32_t)((size_t)N * M * 2u) : 0u);
+}
+
+// Key-outer kernels (C layout of S with one key per lane): adds, in log2 units, the
+// mask entries of the lane's key and the 16 queries q0 + crow(r, half) to s[r].
+// All 16 loads are issued before the first is used, so one latency is paid, not 16;
+// indices are clamped to the mask (entries past N or M carry no weight anyway).
+__device__ __forceinline__ void add_mask_column(f32x16 &s, rsrc_t rmask, int key, int q0, int half, int N, int M)
+{
+    const uint32_t kofs = 2u * (uint32_t)min(key, M - 1);
+    uint32_t mk[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        mk[r] = buf_load_u16(rmask, 2u * (uint32_t)M * (uint32_t)min(q0 + crow(r, half), N - 1) + kofs);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += half_bits_to_float((uint16_t)mk[r]) * kLog2e;
 }
 
 // Work-groups that meet on a shared result exchange partial results through
