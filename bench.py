@@ -98,14 +98,14 @@ def kernel_work(s, causal, mode, has_mask):
                     if s.DK <= a and s.DV <= b)
     mp = (s.M + 63) // 64 * 64
     np_ = (s.N + 63) // 64 * 64
-    dq_from_ds = bf16 and dkp + dvp <= 256 and s.B * s.H * (np_ // 64) * math.ceil(s.M / 128) * 16384 < 4 << 30
+    dq_from_ds = bf16 and s.B * s.H * (np_ // 64) * math.ceil(s.M / 128) * 16384 < 4 << 30
     w = {
         # S = Q K^T and O = P V
         "forward": (2.0 * pairs * (s.DK + s.DV), "flop"),
         # bf16: S, dP, dV, dK; f32: also dQ (atomics)
         "backward": (2.0 * pairs * ((2 * s.DK + 2 * s.DV) if bf16 else (3 * s.DK + 2 * s.DV)), "flop"),
-        # dQ: from the dS^T tiles the dK/dV kernel stores (head-dim pairs up to
-        # 128/128 and tiles within 4 GiB, as the library decides) a memory-bound
+        # dQ: from the dS^T tiles the dK/dV kernel stores (tiles within 4 GiB, as the
+        # library decides) a memory-bound
         # product that reads 2 bytes of dS per visited pair and writes dQ, with the
         # grouped-query reduction of dK and dV in the same launch; otherwise S, dP
         # and dQ by the recompute kernel

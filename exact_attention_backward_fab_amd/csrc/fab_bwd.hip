@@ -593,6 +593,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
                     pa4[2 * qq + u] = pa;
                     da4[2 * qq + u] = da;
+                    if (p.ds) {
+                        // the dS^T operands of this step for dQ = scale dS K, in the tile
+                        // layout bwd_bf16_kernel stores (streaming stores)
+                        __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
+                                            (w >> 1) * 2 + (it & 1)) * 4096 +
+                                    (4 * qq + half) * 512 + u * 1024 + (32 * (w & 1) + l32) * 8;
+                        __builtin_nontemporal_store(da, reinterpret_cast<bf16x8 *>(t));
+                    }
                 }
             {
                 // the transposed operands of the four (half, u) groups' dV and dK products in

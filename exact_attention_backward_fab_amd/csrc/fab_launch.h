@@ -132,9 +132,9 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
                                hipStream_t s);
 
 // dQ in bf16 mode comes either from the dS^T tiles the dK/dV kernel stores
-// (launch_dq_from_ds: a plain product, no recompute) or, for the wide head dims
-// and for shapes whose tiles would pass kDsMaxBytes, from the query-block-outer
-// kernel that recomputes S and dP (launch_dq).  The tiles are bf16, 128 keys x
+// (launch_dq_from_ds: a plain product, no recompute) or, for shapes whose tiles
+// would pass kDsMaxBytes, from the query-block-outer kernel that recomputes S and
+// dP (launch_dq).  The tiles are bf16, 128 keys x
 // 128 queries per (batch, head, query-step pair, key block), dense over all pairs.
 constexpr int64_t kDsMaxBytes = int64_t(4) << 30;
 inline int64_t ds_bytes(const Dims &d, int Np)
@@ -145,7 +145,9 @@ inline int64_t ds_bytes(const Dims &d, int Np)
 // is then below 2^32 bytes too, the range of a buffer resource)
 inline bool dq_from_ds(const Dims &d, int Np, int dkp, int dvp)
 {
-    return dkp + dvp <= 256 && ds_bytes(d, Np) < kDsMaxBytes;
+    (void)dkp;
+    (void)dvp;   // every head-dim pair: both dK/dV kernels store the tiles
+    return ds_bytes(d, Np) < kDsMaxBytes;
 }
 
 // Query heads per work-group of the bf16 dK/dV kernel (1 or 2): two heads of one

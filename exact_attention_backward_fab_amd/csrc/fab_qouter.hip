@@ -153,17 +153,68 @@ __device__ __forceinline__ void load_q_operand(bf16x8 *qf, const void *q, int64_
     }
 }
 
-// S^T for one 32-key sub-tile (rows 32 kk.. of the K tile at Kb): lane = query.
-template <int DKP>
-__device__ __forceinline__ f32x16 st_tile(const char *Kb, const bf16x8 *qf, int kk, int row_off)
+// S^T for both 32-key sub-tiles of a step (and, with VB, dP^T = V dO^T for both
+// from the V tile at Vb and the lane's dO operand of): the LDS row operands run R
+// products ahead of the matrix cores in a register ring that the scheduling barriers
+// hold in place (left to itself the compiler issues each product's reads, waits for
+// them and multiplies, one product at a time).
+template <int DKP, int DVP, bool VB, int R = 2>
+__device__ __forceinline__ void st_pt_pair(const char *Kb, const bf16x8 *qf, const char *Vb, const bf16x8 *of,
+                                           int row_off, f32x16 *st, f32x16 *pt)
 {
-    f32x16 acc = zero16();
-    bf16x8 a[DKP / 16];
+    constexpr int TS = DKP / 16, TP = VB ? DVP / 16 : 0, T = TS > TP ? TS : TP;
+    bf16x8 k0[R], k1[R], v0[R], v1[R];
 #pragma unroll
-    for (int t = 0; t < DKP / 16; ++t) a[t] = lds_row8(Kb + row_off + 512 * kk + 2304 * t);
+    for (int kk = 0; kk < 2; ++kk) {
+        st[kk] = zero16();
+        if (VB) pt[kk] = zero16();
+    }
 #pragma unroll
-    for (int t = 0; t < DKP / 16; ++t) acc = mfma_bf16(a[t], qf[t], acc);
-    return acc;
+    for (int j = 0; j < T + R; ++j) {
+        if (j >= R) {
+            const int t = j - R;
+            if (t < TS) {
+                st[0] = mfma_bf16(k0[t % R], qf[t], st[0]);
+                st[1] = mfma_bf16(k1[t % R], qf[t], st[1]);
+            }
+            if (t < TP) {
+                pt[0] = mfma_bf16(v0[t % R], of[t], pt[0]);
+                pt[1] = mfma_bf16(v1[t % R], of[t], pt[1]);
+            }
+        }
+        if (j < TS) {
+            k0[j % R] = lds_row8(Kb + row_off + 2304 * j);
+            k1[j % R] = lds_row8(Kb + row_off + 512 + 2304 * j);
+        }
+        if (j < TP) {
+            v0[j % R] = lds_row8(Vb + row_off + 2304 * j);
+            v1[j % R] = lds_row8(Vb + row_off + 512 + 2304 * j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// acc[c] += A(g) * B(g, c) over the four (sub-tile kk, operand half u) groups g = 2 kk + u
+// of a step, B by transposing reads of the tile at Tb (column tile c, rows of group g),
+// read R products ahead (ring and scheduling barriers as above).  SWAP: the transposed
+// operand is the A side (acc += B * A, the product order of O^T += V^T P^T).
+template <int NC, bool SWAP, int R = 3>
+__device__ __forceinline__ void tr_products(f32x16 *acc, const bf16x8 *a4, const char *Tb, int tr_off)
+{
+    constexpr int NJ = 4 * NC;
+    bf16x8 br[R];
+#pragma unroll
+    for (int j = 0; j < NJ + R; ++j) {
+        if (j >= R) {
+            const int i = j - R, g = i / NC, c = i % NC;
+            acc[c] = SWAP ? mfma_bf16(br[i % R], a4[g], acc[c]) : mfma_bf16(a4[g], br[i % R], acc[c]);
+        }
+        if (j < NJ) {
+            const int g = j / NC, c = j % NC;
+            br[j % R] = lds_tr8(Tb + tr_off + 4608 * c + 512 * (g >> 1) + 256 * (g & 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Scaled scores (log2 units) of NT 32-key sub-tiles from key0 on for the lane's
@@ -296,8 +347,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
         [&](int s, int cls, const char *Kb, const char *Vb) {
             const int key0 = s * kQBK;
             f32x16 st[2];
-            st[0] = st_tile<DKP>(Kb, qf, 0, row_off);
-            st[1] = st_tile<DKP>(Kb, qf, 1, row_off);
+            st_pt_pair<DKP, DVP, false>(Kb, qf, nullptr, nullptr, row_off, st, nullptr);
             // scores in log2 units = st * mul: a step with every key visible (FREE and
             // inside M) keeps the raw products and folds the scale into the exponent
             float mul = sl2;
@@ -342,6 +392,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 
             // ---- O^T += V^T P^T: A = V^T by transposing reads (key rows 16u + 4*half
             // (+8) of the sub-tile), B = P^T (lane = query, keys in operand order)
+            bf16x8 pb4[4];   // index 2 kk + u
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -349,14 +400,9 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
                     float pv[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) pv[i] = st[kk][8 * u + i];
-                    const bf16x8 pb = to_bf16x8(pv);
-                    bf16x8 av[DVP / 32];
-#pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt)
-                        av[dt] = lds_tr8(Vb + tr_off + 4608 * dt + 512 * kk + 256 * u);
-#pragma unroll
-                    for (int dt = 0; dt < DVP / 32; ++dt) oacc[dt] = mfma_bf16(av[dt], pb, oacc[dt]);
+                    pb4[2 * kk + u] = to_bf16x8(pv);
                 }
+            tr_products<DVP / 32, true>(oacc, pb4, Vb, tr_off);
         });
 
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
@@ -496,16 +542,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             const int key0 = s * kQBK;
             // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key sub-tiles (lane = query)
             f32x16 st[2], pt[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                st[kk] = st_tile<DKP>(Kb, qf, kk, row_off);
-                pt[kk] = zero16();
-                bf16x8 av[DVP / 16];
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) av[t] = lds_row8(Vb + row_off + 512 * kk + 2304 * t);
-#pragma unroll
-                for (int t = 0; t < DVP / 16; ++t) pt[kk] = mfma_bf16(av[t], of[t], pt[kk]);
-            }
+            st_pt_pair<DKP, DVP, true>(Kb, qf, Vb, of, row_off, st, pt);
 
             // ---- P and dS; keys past M and (causal steps) keys after the query get -inf;
             // a step with every key visible folds the scale into the exponent
@@ -526,6 +563,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 
             // ---- dQ += dS K: A = dS (lane = query, keys in operand order), B = K via
             // transposing reads (key rows 16u + 4*half (+8) of the sub-tile)
+            bf16x8 da4[4];   // index 2 kk + u
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -533,14 +571,9 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
                     float d8[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) d8[i] = pt[kk][8 * u + i];
-                    const bf16x8 da = to_bf16x8(d8);
-                    bf16x8 bk[DKP / 32];
-#pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt)
-                        bk[dt] = lds_tr8(Kb + tr_off + 4608 * dt + 512 * kk + 256 * u);
-#pragma unroll
-                    for (int dt = 0; dt < DKP / 32; ++dt) dqacc[dt] = mfma_bf16(da, bk[dt], dqacc[dt]);
+                    da4[2 * kk + u] = to_bf16x8(d8);
                 }
+            tr_products<DKP / 32, false>(dqacc, da4, Kb, tr_off);
         },
         share, p.split);
 

@@ -106,10 +106,10 @@ int fab_blob_layout(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int6
 /* Host only.  Workspace bytes that fab_forward_lse (have_o_lse ignored) or
  * fab_backward need for this shape, mode and mask presence.  have_o_lse != 0
  * means the caller will pass O and lse to fab_backward.  *bytes is written on
- * FAB_OK.  In bf16 mode with both head dims padded to at most 128 the backward's
- * workspace holds the bf16 dS of every (query, key) pair, 2 * B * H *
- * ceil(N/128)*128 * ceil(M/128)*128 bytes, as long as that is at most 4 GiB
- * (e.g. 2.1 GB for B=1, H=16, N=M=8192); larger shapes compute dQ without it. */
+ * FAB_OK.  In bf16 mode the backward's workspace holds the bf16 dS of every
+ * (query, key) pair, 2 * B * H * ceil(N/128)*128 * ceil(M/128)*128 bytes, as long
+ * as that is below 4 GiB (e.g. 2.1 GB for B=1, H=16, N=M=8192); larger shapes
+ * compute dQ without it. */
 int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have_o_lse,
                         size_t *bytes);
 
