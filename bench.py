@@ -22,7 +22,7 @@ Beside it: `whole_path`, the op's own semantics (O = lse = NULL: the forward run
 inside fab_backward, counted as forward plus backward flops); `forward_only`;
 causal workloads with the causal rule passed as a flag instead of the mask tensor
 (`causal_flag_instead_of_mask`); bf16 mode with q, k, v, d stored as bf16
-(`bf16_inputs`); and `configs`: every other (workload, mode) pair of the five
+(`bf16_inputs`) and with O stored as bf16 as well (`bf16_storage`); and `configs`: every other (workload, mode) pair of the five
 workloads, each with its backward alone (and kernel split), whole path and
 fraction of its mode's peak.  `cpu_baseline` times the f64 CPU oracle on a
 bounded sample of the headline workload on this host's cores.
@@ -438,7 +438,15 @@ def main():
                          args.steps, args.warmup, stream, args.min_warm_s)
         out["bf16_inputs"] = {"backward_only": {"ms": round(ms_b, 4), "tflops": round(F_b / (ms_b * 1e-3) / 1e12, 3),
                                                 "frac_of_peak": round(F_b / (ms_b * 1e-3) / 1e12 / peak, 4)}}
-        del tb
+        # ... and O stored as bf16 too (FAB_BF16_O, written so by the forward)
+        O16, lse16 = fab.forward_lse(tb[0], tb[1], tb[2], c.scale, mask=c.tm, mode=mode, o_bf16=True, ws=c.ws_bwd)
+        ms_o = time_loop(torch, lambda: fab.backward(*tb, c.scale, mask=c.tm, mode=mode, O=O16, lse=lse16,
+                                                     blob=c.blob, ws=c.ws_bwd),
+                         args.steps, args.warmup, stream, args.min_warm_s)
+        out["bf16_storage"] = {"what": "q, k, v, d and O stored as bf16",
+                               "backward_only": {"ms": round(ms_o, 4), "tflops": round(F_b / (ms_o * 1e-3) / 1e12, 3),
+                                                 "frac_of_peak": round(F_b / (ms_o * 1e-3) / 1e12 / peak, 4)}}
+        del tb, O16, lse16
 
     # ---- every other (workload, mode) pair, same protocol
     pairs = []

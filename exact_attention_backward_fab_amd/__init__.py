@@ -23,6 +23,7 @@ FAB_MODE_F32 = 0
 FAB_MODE_BF16 = 1
 FAB_CAUSAL = 0x100   # flag: the causal rule (key m seen by query n iff m <= n) without a mask
 FAB_BF16_INPUTS = 0x200   # flag: q, k, v, d are bf16 (bf16 mode only)
+FAB_BF16_O = 0x400        # flag: O is bf16 (bf16 mode only)
 MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
          FAB_MODE_BF16: FAB_MODE_BF16}
 
@@ -128,8 +129,9 @@ def blob_layout(shape: Shape):
     return tuple(x.value for x in o)
 
 
-def _mode(mode, causal, bf16_inputs=False):
-    return MODES[mode] | (FAB_CAUSAL if causal else 0) | (FAB_BF16_INPUTS if bf16_inputs else 0)
+def _mode(mode, causal, bf16_inputs=False, bf16_o=False):
+    return (MODES[mode] | (FAB_CAUSAL if causal else 0) | (FAB_BF16_INPUTS if bf16_inputs else 0)
+            | (FAB_BF16_O if bf16_o else 0))
 
 
 def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False, causal=False) -> int:
@@ -234,11 +236,12 @@ def _on_stream(stream):
 
 
 def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None, stream=None, causal=False,
-                alibi=None):
+                alibi=None, o_bf16=False):
     """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v.
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v
     are float32, or bfloat16 (all three; mode "bf16").  alibi: float32 (H,) per-head
-    slopes, adding alibi[h] * (m - n) to the score of query n at key m, or None."""
+    slopes, adding alibi[h] * (m - n) to the score of query n at key m, or None.  O is
+    float32, or bfloat16 (mode "bf16": a given bfloat16 O, or o_bf16=True)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
@@ -249,7 +252,8 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     mask = _check_mask(mask, s)
     alibi = _check_alibi(alibi, s)
     if O is not None:
-        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
+        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV), (torch.float32, torch.bfloat16))
+        o_bf16 = O.dtype == torch.bfloat16
     if lse is not None:
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
     if ws is not None:
@@ -257,13 +261,13 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
     _check_devices(dev, k=k, v=v, mask=mask, alibi=alibi, O=O, lse=lse, ws=ws)
     with _on_stream(stream):
         if O is None:
-            O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.float32, device=dev)
+            O = torch.empty((s.B, s.N, s.H, s.DV), dtype=torch.bfloat16 if o_bf16 else torch.float32, device=dev)
         if lse is None:
             lse = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev)
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
         _check(lib().fab_forward_lse_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
-                                           float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse),
+                                           float(scale), _mode(mode, causal, bf16_in, o_bf16), _ptr(O), _ptr(lse),
                                            _ptr(ws), nbytes, _stream_handle(stream)))
     return O, lse
 
@@ -273,7 +277,8 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
     """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
     are float32, or bfloat16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
-    float32, are both given (from forward_lse, with the same alibi) or both None.
+    (float32, or bfloat16 as forward_lse wrote it) are both given (from forward_lse,
+    with the same alibi) or both None.
     alibi: float32 (H,) per-head ALiBi slopes or None (see forward_lse)."""
     import torch
     s = shape_of(q, k, v)
@@ -287,9 +292,11 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
     alibi = _check_alibi(alibi, s)
     if (O is None) != (lse is None):
         raise ValueError("O and lse must be given together or both be None")
+    o_bf16 = False
     if O is not None:
-        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
+        _check_tensor(O, "O", (s.B, s.N, s.H, s.DV), (torch.float32, torch.bfloat16))
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
+        o_bf16 = O.dtype == torch.bfloat16
     total = blob_layout(s)[3]
     if blob is not None:
         _check_tensor(blob, "blob", None)
@@ -304,8 +311,8 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
         _check(lib().fab_backward_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
-                                        _ptr(d), float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse),
-                                        _ptr(blob), _ptr(ws), nbytes, _stream_handle(stream)))
+                                        _ptr(d), float(scale), _mode(mode, causal, bf16_in, o_bf16), _ptr(O),
+                                        _ptr(lse), _ptr(blob), _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 
 

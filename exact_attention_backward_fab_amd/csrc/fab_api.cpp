@@ -175,16 +175,19 @@ int check_mode(int mode)
     return FAB_OK;
 }
 
-// Splits the FAB_CAUSAL and FAB_BF16_INPUTS flags off the mode argument and
-// checks the rest.
-int take_mode(int *mode, bool *causal, bool *in_bf16)
+// Splits the FAB_CAUSAL, FAB_BF16_INPUTS and FAB_BF16_O flags off the mode argument
+// and checks the rest.
+int take_mode(int *mode, bool *causal, bool *in_bf16, bool *o_bf16 = nullptr)
 {
     *causal = (*mode & FAB_CAUSAL) != 0;
     *in_bf16 = (*mode & FAB_BF16_INPUTS) != 0;
-    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS);
+    const bool ob = (*mode & FAB_BF16_O) != 0;
+    if (o_bf16) *o_bf16 = ob;
+    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS | FAB_BF16_O);
     const int rc = check_mode(*mode);
     if (rc != FAB_OK) return rc;
     if (*in_bf16 && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS needs FAB_MODE_BF16");
+    if (ob && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_O needs FAB_MODE_BF16");
     return FAB_OK;
 }
 
@@ -296,7 +299,7 @@ int launch_pack(const Plan &pl, const void *q, const void *k, const void *v, __b
 }
 
 int launch_fwd(const Plan &pl, int bf16, const void *q, const void *k, const void *v, const __bf16 *k16,
-               const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *O, float *lse,
+               const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, void *O, float *lse,
                hipStream_t s)
 {
     if (bf16)
@@ -305,7 +308,8 @@ int launch_fwd(const Plan &pl, int bf16, const void *q, const void *k, const voi
     else
         FAB_LAUNCH(kFwd,
                    fab::launch_forward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
-                                           static_cast<const float *>(v), mask, map, scale, O, lse, pl.d, s),
+                                           static_cast<const float *>(v), mask, map, scale, static_cast<float *>(O),
+                                           lse, pl.d, s),
                    "forward launch");
     return FAB_OK;
 }
@@ -412,18 +416,19 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
 }
 
 int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
-                          const uint16_t *mask, const float *alibi, float scale, int mode, float *O, float *lse,
+                          const uint16_t *mask, const float *alibi, float scale, int mode, void *O, float *lse,
                           void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal, in_bf16;
-    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
+    bool causal, in_bf16, o_bf16;
+    FAB_TRY(take_mode(&mode, &causal, &in_bf16, &o_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
     pl.d.in_bf16 = in_bf16;
+    pl.d.o_bf16 = o_bf16;
     pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     FAB_TRY(check_ptr(q, pl.nq, "q"));
@@ -454,17 +459,18 @@ int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, 
 
 int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
                        const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
-                       const float *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+                       const void *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal, in_bf16;
-    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
+    bool causal, in_bf16, o_bf16;
+    FAB_TRY(take_mode(&mode, &causal, &in_bf16, &o_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
     pl.d.in_bf16 = in_bf16;
+    pl.d.o_bf16 = o_bf16;
     pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
     if ((O == nullptr) != (lse == nullptr))
@@ -527,7 +533,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
                    "pack and prep launch");
     } else {
         // f32: dQ is accumulated by atomics into a zeroed slice
-        const float *Ou = O;
+        const float *Ou = static_cast<const float *>(O);   // f32 mode: O is f32
         if (!have) {
             float *Ow = reinterpret_cast<float *>(wsb + pl.ws_O);
             float *lw = reinterpret_cast<float *>(wsb + pl.ws_lse);
@@ -569,14 +575,14 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
 }
 
 int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
-                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
+                    const uint16_t *mask, float scale, int mode, void *O, float *lse, void *ws,
                     size_t ws_bytes, void *stream)
 {
     return fab_forward_lse_alibi(shape, q, k, v, mask, nullptr, scale, mode, O, lse, ws, ws_bytes, stream);
 }
 
 int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
-                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                 const uint16_t *mask, const void *d, float scale, int mode, const void *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
 {
     return fab_backward_alibi(shape, q, k, v, mask, nullptr, d, scale, mode, O, lse, blob, ws, ws_bytes, stream);

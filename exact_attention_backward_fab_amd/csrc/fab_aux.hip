@@ -159,7 +159,8 @@ struct PackJob {
 
 // Extra outputs of the bf16-mode prep (second input O, LSE/D blocks, blob pads).
 struct PrepExtra {
-    const float *O;                   // rows like the job's src
+    const void *O;                    // rows like the job's src; f32, or bf16 when O_bf16
+    int O_bf16;
     const float *lse;                 // row LSE [N,H,B] (natural log)
     float *stats;                     // LSE/D blocks [heads][Mp/64][128]
     float *blob;                      // result blob whose pads are zeroed (work-group 0)
@@ -183,7 +184,7 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
     const int hd = bt / ntile, t = bt - hd * ntile;
     const int hh = hd % j.H, bb = hd / j.H;
     const int64_t head_off = hh * j.sh + bb * j.sb;
-    const float *obase = x ? x->O + head_off : nullptr;
+    const void *obase = x ? x->O : nullptr;   // with the head's offset head_off (elements)
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     // all loads of the tile first (independent, so they are in flight together)
     f32x4 xv[IT], yv[IT];
@@ -194,7 +195,7 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
         const int m = t * 64 + r;
         const bool ok = idx < 64 * C4 && m < j.M;
         xv[i] = ok ? load_row4_any(j.src, head_off + m * j.rs, col, j.D, j.vec, j.src_bf16) : z;
-        yv[i] = (ok && obase) ? load_row4(obase + m * j.rs, col, j.D, j.vec) : z;
+        yv[i] = (ok && obase) ? load_row4_any(obase, head_off + m * j.rs, col, j.D, j.vec, x->O_bf16) : z;
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -325,7 +326,7 @@ PackJobs pack_jobs(const void *q, const void *k, const void *v, __bf16 *q16, __b
     return a;
 }
 
-void prep_job(const void *dO, const float *O, const float *lse, __bf16 *dO16, float *stats, float *blob, int Np,
+void prep_job(const void *dO, const void *O, const float *lse, __bf16 *dO16, float *stats, float *blob, int Np,
               int64_t nq, int64_t off_k, int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero,
               const Dims &d, PackJob *pj, PrepExtra *px)
 {
@@ -336,7 +337,7 @@ void prep_job(const void *dO, const float *O, const float *lse, __bf16 *dO16, fl
     j.M = d.N; j.Mp = Np; j.D = d.DV; j.vec = (d.DV % 4 == 0);
     j.tiles = d.H * d.B * (Np / 64);
     PrepExtra x = {};
-    x.O = O; x.lse = lse; x.stats = stats; x.blob = blob;
+    x.O = O; x.O_bf16 = d.o_bf16; x.lse = lse; x.stats = stats; x.blob = blob;
     x.pad_lo[0] = nq; x.pad_hi[0] = off_k;
     x.pad_lo[1] = off_k + nk; x.pad_hi[1] = off_v;
     x.pad_lo[2] = off_v + nv; x.pad_hi[2] = total;
@@ -372,7 +373,7 @@ hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *
 }
 
 hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16,
-                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const float *O,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const void *O,
                                  const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
                                  int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
                                  int Mp, const Dims &d, hipStream_t s)

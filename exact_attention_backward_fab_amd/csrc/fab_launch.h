@@ -14,6 +14,7 @@ struct Dims {
     int B, H, Hkv, N, M, DK, DV;
     int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
     int in_bf16 = 0;  // q, k, v and d are bf16 (bf16 mode only); otherwise f32
+    int o_bf16 = 0;   // O is bf16 (bf16 mode only): written so by the forward, read so by the prep
     const float *alibi = nullptr;   // per-query-head ALiBi slopes [H] (device) or NULL: score += slope_h (m - n)
 };
 
@@ -85,7 +86,7 @@ hipError_t launch_forward_f32(const float *q, const float *k, const float *v, co
                               const uint8_t *map, float scale, float *O, float *lse, const Dims &d,
                               hipStream_t s);
 hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
-                               const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
+                               const uint8_t *map, float scale, void *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s);
 // The backward's own forward in bf16 mode: instead of O and the LSE it writes
 // what the backward kernels read, as launch_pack_prep_bf16 does
@@ -108,7 +109,7 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
 // result blob zeroed ([nq, off_k), [off_k + nk, off_v), [off_v + nv, total)) and
 // nzero ints of zero written.
 hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16,
-                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const float *O,
+                                 __bf16 *v16, const uint16_t *mask, uint8_t *map, const void *dO, const void *O,
                                  const float *lse, __bf16 *dO16, float *stats, float *blob, int64_t nq, int64_t off_k,
                                  int64_t nk, int64_t off_v, int64_t nv, int64_t total, int *zero, int nzero, int Np,
                                  int Mp, const Dims &d, hipStream_t s);

@@ -50,7 +50,7 @@ int scratch_ptr(void **out)
 extern "C" {
 
 int fab_backward_noalloc(const fab_shape *shape, const void *q, const void *k, const void *v,
-                         const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                         const uint16_t *mask, const void *d, float scale, int mode, const void *O,
                          const float *lse, float *blob, void *stream)
 {
     // shape and mode first (host only): the workspace this call needs

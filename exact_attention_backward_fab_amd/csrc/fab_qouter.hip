@@ -272,7 +272,9 @@ struct FwdArgs16 {
     const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
-    float *O, *lse;                 // O [DV,H,N,B], lse [N,H,B]
+    void *O;                        // O [DV,H,N,B]: f32, or bf16 when o_bf16
+    int o_bf16;
+    float *lse;                     // lse [N,H,B]
     int B, H, Hkv, N, M, Mp, DK, DV, nqb, nkb, vecK, vecV;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
@@ -436,7 +438,9 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
         return;
     }
     if (qok) {
-        float *orow = p.O + (size_t)p.DV * (h + p.H * (myq + (size_t)p.N * b));
+        const size_t ooff = (size_t)p.DV * (h + p.H * (myq + (size_t)p.N * b));
+        float *orow = static_cast<float *>(p.O) + ooff;
+        __bf16 *orow16 = static_cast<__bf16 *>(p.O) + ooff;   // o_bf16: the f32 values rounded to nearest even
 #pragma unroll
         for (int dt = 0; dt < DVP / 32; ++dt)
 #pragma unroll
@@ -446,7 +450,15 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
                 f32x4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = oacc[dt][4 * r4 + i] * inv;
-                if (p.vecV) {
+                if (p.o_bf16) {
+                    if (p.vecV) {
+                        *reinterpret_cast<bf16x4 *>(orow16 + c0) = to_bf16x4(o);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (c0 + i < p.DV) orow16[c0 + i] = (__bf16)o[i];
+                    }
+                } else if (p.vecV) {
                     *reinterpret_cast<f32x4 *>(orow + c0) = o;
                 } else {
 #pragma unroll
@@ -843,13 +855,13 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
 }  // namespace
 
 hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v16, const uint16_t *mask,
-                               const uint8_t *map, float scale, float *O, float *lse, int Mp, const Dims &d,
+                               const uint8_t *map, float scale, void *O, float *lse, int Mp, const Dims &d,
                                hipStream_t s)
 {
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
     FwdArgs16 a = {};
-    a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.lse = lse;
+    a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.o_bf16 = d.o_bf16; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;

@@ -85,9 +85,16 @@ typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
  * patterns, the same layouts) instead of f32 -- the storage the bf16 matrix
  * cores read anyway, so the values are those FAB_MODE_BF16 would round f32
  * inputs to, and the results equal those for the f32 inputs holding the same
- * values.  FAB_MODE_BF16 only (FAB_E_INVAL otherwise); O, lse and the blob stay
- * f32. */
+ * values.  FAB_MODE_BF16 only (FAB_E_INVAL otherwise); O (unless FAB_BF16_O),
+ * lse and the blob stay f32. */
 #define FAB_BF16_INPUTS 0x200
+
+/* Flag OR-ed into the mode argument: O is bf16 (16-bit bit patterns, layout
+ * [DV,H,N,B]) instead of f32 -- written so by fab_forward_lse (the f32 output
+ * rounded to nearest even) and read so by fab_backward (D = rowsum(dO o O) from
+ * those values, widened exactly).  FAB_MODE_BF16 only (FAB_E_INVAL otherwise);
+ * it combines with FAB_BF16_INPUTS.  lse and the blob stay f32. */
+#define FAB_BF16_O 0x400
 
 typedef enum fab_status {
     FAB_OK = 0,
@@ -119,14 +126,15 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
  *   mask      device f16 bits [M,N] or NULL for no mask (read only)
  *   scale     finite f32 softmax scale
  *   mode      fab_mode, optionally | FAB_CAUSAL (then mask must be NULL)
- *             | FAB_BF16_INPUTS (FAB_MODE_BF16 only)
- *   O         device f32 [DV,H,N,B] (written): softmax(scale*q.k + mask) v
+ *             | FAB_BF16_INPUTS, FAB_BF16_O (FAB_MODE_BF16 only)
+ *   O         device f32 (bf16 with FAB_BF16_O) [DV,H,N,B] (written):
+ *             softmax(scale*q.k + mask) v
  *   lse       device f32 [N,H,B] (written): natural-log log-sum-exp of the row's
  *             scores, -inf for an all-masked row
  *   ws        device workspace of ws_bytes >= fab_workspace_bytes(.., have_o_lse=1)
  *   stream    hipStream_t of the caller (NULL = default stream) */
 int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const void *v,
-                    const uint16_t *mask, float scale, int mode, float *O, float *lse, void *ws,
+                    const uint16_t *mask, float scale, int mode, void *O, float *lse, void *ws,
                     size_t ws_bytes, void *stream);
 
 /* The attention backward ("Function ggml_flash_attn_back"; ggmlR
@@ -136,13 +144,13 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
  *             of the attention output
  *   O, lse    either both NULL (the forward is recomputed internally, the
  *             pages' semantics) or both given: the output and row LSE of the
- *             same forward (as written by fab_forward_lse); exactly one NULL
- *             is FAB_E_INVAL
+ *             same forward (as written by fab_forward_lse; O f32, or bf16 with
+ *             FAB_BF16_O); exactly one NULL is FAB_E_INVAL
  *   blob      device f32, total_floats of fab_blob_layout (written in full)
  *   ws        device workspace, ws_bytes >= fab_workspace_bytes(.., have_o_lse)
  *   stream    hipStream_t of the caller */
 int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
-                 const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                 const uint16_t *mask, const void *d, float scale, int mode, const void *O,
                  const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
 
 /* ALiBi: fab_forward_lse and fab_backward with a linear per-head bias on the
@@ -160,11 +168,11 @@ int fab_backward(const fab_shape *shape, const void *q, const void *k, const voi
  * fab_backward; O and lse passed to fab_backward_alibi must come from the forward
  * with the same slopes. */
 int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
-                          const uint16_t *mask, const float *alibi, float scale, int mode, float *O, float *lse,
+                          const uint16_t *mask, const float *alibi, float scale, int mode, void *O, float *lse,
                           void *ws, size_t ws_bytes, void *stream);
 int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
                        const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
-                       const float *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
+                       const void *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: fab_backward
@@ -185,7 +193,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
  *   undefined results; calls ordered on one stream are safe. */
 #define FAB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int fab_backward_noalloc(const fab_shape *shape, const void *q, const void *k, const void *v,
-                         const uint16_t *mask, const void *d, float scale, int mode, const float *O,
+                         const uint16_t *mask, const void *d, float scale, int mode, const void *O,
                          const float *lse, float *blob, void *stream);
 
 /* Measurement hooks (they compute nothing).  While enabled, every kernel

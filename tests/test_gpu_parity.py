@@ -332,6 +332,37 @@ def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mki
     check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"bf16 inputs {name}", mask=mask)
 
 
+@pytest.mark.parametrize("inputs16", [False, True], ids=["f32_inputs", "bf16_inputs"])
+@pytest.mark.parametrize("name,s,mkind,seed", BF16_IN, ids=[c[0] for c in BF16_IN])
+def test_bf16_o_equals_f32_o_of_the_same_values(torch_dev, name, s, mkind, seed, inputs16):
+    # FAB_BF16_O: fab_forward_lse writes O as bf16 -- the f32 O rounded to nearest even,
+    # bit for bit -- and fab_backward reading that bf16 O gives bit for bit the result of
+    # the f32 O holding the same values; the result matches the oracle
+    torch, dev = torch_dev
+    fab = fabmod()
+    print(f"[parity] bf16 O {name} inputs16={inputs16} {s}", flush=True)
+    q, k, v, d = make_qkvd(s, seed)
+    mask = small_mask(mkind, s, seed)
+    tm = to_dev(torch, dev, mask)
+    scale = float(np.float32(1.0 / math.sqrt(s.DK)))
+    t = [to_dev(torch, dev, x) for x in (q, k, v, d)]
+    if inputs16:
+        t = [x.to(torch.bfloat16) for x in t]
+    O32, lse32 = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode="bf16")
+    O16, lse16 = fab.forward_lse(t[0], t[1], t[2], scale, mask=tm, mode="bf16", o_bf16=True)
+    assert O16.dtype == torch.bfloat16
+    assert torch.equal(O16.view(torch.int16), O32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(lse16.view(torch.int32), lse32.view(torch.int32))
+    b16 = fab.backward(*t, scale, mask=tm, mode="bf16", O=O16, lse=lse16)
+    b32 = fab.backward(*t, scale, mask=tm, mode="bf16", O=O16.float(), lse=lse16)
+    torch.cuda.synchronize()
+    assert torch.equal(b16.view(torch.int32), b32.view(torch.int32))
+    qr, kr, vr, dr = (x.float().cpu().numpy() for x in t)
+    ref = oracle_full(s, qr, kr, vr, dr, mask, scale)
+    total = fab.blob_layout(fab.Shape(*s.astuple()))[3]
+    check_blob(s, b16[:total].cpu().numpy(), ref, "bf16", tag=f"bf16 O {name}", mask=mask)
+
+
 @pytest.mark.parametrize("supplied", [False, True], ids=["own_forward", "o_lse_supplied"])
 @pytest.mark.parametrize("name,s,mkind,seed", [
     ("causal_d64", Shape(1, 4, 2, 333, 333, 64, 64), "causal", 61),
