@@ -250,11 +250,13 @@ __device__ __forceinline__ void add_mask_column(f32x16 &s, rsrc_t rmask, int key
 }
 
 // Work-groups that meet on a shared result exchange partial results through
-// global memory with device-coherent accesses (write-through stores, loads that
-// bypass the non-coherent caches), so no cache-wide writeback or invalidate is
-// needed: a work-group's stores have completed (s_waitcnt vmcnt(0)) before it
-// takes the result's ticket, and the one that finds the others done reads them
-// after.
+// global memory with device-coherent accesses (agent-scope atomic stores and
+// loads, which bypass the non-coherent caches).  Every wave waits for its own
+// stores (s_waitcnt vmcnt(0)) before the work-group barrier; one lane then takes
+// the result's ticket with an agent-scope acquire-release add, which orders the
+// work-group's partial stores (made visible to it by the barrier) before the
+// ticket, and the ticket before the loads of the other work-group's partial that
+// follow the next barrier.
 __device__ __forceinline__ void coherent_store(float *p, float x)
 {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -265,7 +267,7 @@ __device__ __forceinline__ float coherent_load(const float *p)
 }
 __device__ __forceinline__ int ticket_take(int *t)
 {
-    return __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- work order

@@ -61,13 +61,17 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char *p)
 // One 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane i
 // writes LDS bytes [la + 16 i, la + 16 i + 16); la must be wave-uniform.  Issued
 // as inline assembly so that the compiler does not make every later LDS read wait
-// for it; the caller orders it with explicit vmcnt waits and barriers.  m0 is not
-// used by the compiler in these kernels (the buffer copy is their only m0 user);
-// the copy reads m0 one wait state after it is written.
+// for it; the caller orders it with explicit vmcnt waits and barriers.  The copy
+// takes its LDS address from m0: the asm saves m0, sets it (the copy reads it one
+// wait state later, at issue) and restores it, so whatever the compiler keeps in
+// m0 is unchanged across the statement and m0 is not a clobber.  The asm writes no
+// VGPR (the data goes to LDS), so no register is left pending on the load.
 __device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t la, uint32_t voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(la), "v"(voff), "s"(r) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(la), "v"(voff), "s"(r) : "memory");
 }
 
 // Waits until at most k * PER of this wave's vector-memory operations are in flight.

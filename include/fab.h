@@ -35,10 +35,15 @@
  * written; the pads are zero.
  *
  * Ownership and threading: the caller allocates and owns every buffer (inputs,
- * outputs, workspace).  The library never allocates, frees or synchronises
- * device memory; it only enqueues kernels on the caller's stream and keeps no
- * per-call state, so calls on different streams with separate workspaces may
- * run concurrently.
+ * outputs, workspace).  The compute entry points never allocate, free or
+ * synchronise device memory; they only enqueue kernels on the caller's stream
+ * and keep no state between calls, so calls on different streams with separate
+ * workspaces may run concurrently.  Two exceptions hold process-wide state:
+ * fab_backward_noalloc works in one static device array per GPU (calls that
+ * overlap on one GPU race, see its declaration), and the measurement hooks
+ * below create HIP events on first use, keep them until the process ends, and
+ * while enabled record them on the caller's stream around every launch (the
+ * hooks are meant for one thread at a time).
  *
  * Errors: every entry point validates all arguments before touching the
  * device.  On any error nothing is enqueued and no output byte is written; the
