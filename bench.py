@@ -24,7 +24,10 @@ causal workloads with the causal rule passed as a flag instead of the mask tenso
 (`causal_flag_instead_of_mask`); bf16 mode with q, k, v, d stored as bf16
 (`bf16_inputs`) and with O stored as bf16 as well (`bf16_storage`); and `configs`: every other (workload, mode) pair of the five
 workloads, each with its backward alone (and kernel split), whole path and
-fraction of its mode's peak.  `cpu_baseline` times the f64 CPU oracle on a
+fraction of its mode's peak.  `mfma_loop_ceiling` (bf16 mode) is the rate of a
+loop of dense bf16 products on every SIMD, with the shader clock it runs at: the
+practical ceiling of the matrix cores, beside the published peak that `roofline`
+and `frac_of_peak` use.  `cpu_baseline` times the f64 CPU oracle on a
 bounded sample of the headline workload on this host's cores.
 
 Prints exactly one JSON line.
@@ -412,6 +415,14 @@ def main():
         "forward_only": {"ms": round(ms_fwd, 4), "tflops": round(F_f / (ms_fwd * 1e-3) / 1e12, 3),
                          "frac_of_peak": round(F_f / (ms_fwd * 1e-3) / 1e12 / peak, 4)},
     }
+    # ---- the practical ceiling of the matrix cores: a loop of dense bf16 products on
+    # every SIMD (the chip lowers its clock under this load); context for `roofline`
+    if mode == "bf16":
+        tf_loop, ghz_loop = fab.measure_mfma_loop(iters=20000)
+        out["mfma_loop_ceiling"] = {"tflops": round(tf_loop, 1), "clock_ghz": round(ghz_loop, 3),
+                                    "frac_of_published_peak": round(tf_loop / peak, 4),
+                                    "dominant_kernel_frac_of_ceiling": round(roof["achieved"] / tf_loop, 4)
+                                    if roof["unit"] == "TFLOP/s" else None}
     tq, tk, tv, td = c.t
     # ---- the causal rule given as a flag instead of the mask tensor (identical
     # result; no block map, no mask reads), backward alone and whole path

@@ -37,7 +37,7 @@ FAB_E_HIP = -5
 # every symbol include/fab.h declares
 EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
            "fab_forward_lse_alibi", "fab_backward_alibi", "fab_backward_noalloc", "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
-           "fab_strerror", "fab_last_error", "fab_version")
+           "fab_probe_scratch_bytes", "fab_measure_mfma_loop", "fab_strerror", "fab_last_error", "fab_version")
 KERNELS = ("block_map", "forward", "prep", "pack", "backward", "dq", "gqa_reduce")
 
 
@@ -92,6 +92,10 @@ def lib():
         L.fab_profile_read.restype = I
         L.fab_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(I64)]
+        L.fab_probe_scratch_bytes.restype = SZ
+        L.fab_probe_scratch_bytes.argtypes = []
+        L.fab_measure_mfma_loop.restype = I
+        L.fab_measure_mfma_loop.argtypes = [P, SZ, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), P]
         _lib = L
     return _lib
 
@@ -379,3 +383,18 @@ def profile_read():
         _check(lib().fab_profile_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
         out[name] = (ms.value, n.value)
     return out
+
+
+def measure_mfma_loop(iters=20000, device=None):
+    """(TFLOP/s, shader GHz) of a loop of dense bf16 32x32x16 products on every SIMD:
+    the practical ceiling of the matrix cores on this GPU (measurement only)."""
+    import torch
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    n = lib().fab_probe_scratch_bytes()
+    scratch = torch.empty(n, dtype=torch.uint8, device=dev)
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(lib().fab_measure_mfma_loop(ctypes.c_void_p(scratch.data_ptr()), n, int(iters), ctypes.byref(tf),
+                                           ctypes.byref(ghz), ctypes.c_void_p(stream)))
+    return tf.value, ghz.value

@@ -24,6 +24,7 @@ SOURCES = {
     "fab_qouter.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fab_api.cpp": [],
     "fab_noalloc.hip": [],
+    "fab_probe.hip": [],
 }
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

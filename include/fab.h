@@ -219,6 +219,21 @@ int fab_profile_enable(int on);
 int fab_profile_reset(void);
 int fab_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
+/* Measurement hook (computes nothing of the attention): the sustained rate of the
+ * bf16 matrix cores on this GPU.  A fully resident grid in which every wave
+ * runs `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 products
+ * (32x32x16x2 flops each) is timed with two HIP events on `stream` (after a
+ * short warm-up launch); *tflops receives the rate and *clock_ghz the shader
+ * clock over the run (s_memtime cycles per 100 MHz s_memrealtime tick, averaged
+ * over 64 work-groups).  The chip lowers its clock under this load, so the rate
+ * is the practical ceiling of dense bf16 products, below the published peak.
+ * scratch: device memory of at least fab_probe_scratch_bytes() bytes, owned by
+ * the caller, overwritten.  Synchronises `stream`; creates and destroys two
+ * events.  iters in [1, 2^24].  Returns FAB_OK, FAB_E_INVAL or FAB_E_HIP. */
+size_t fab_probe_scratch_bytes(void);
+int fab_measure_mfma_loop(void *scratch, size_t scratch_bytes, int iters, double *tflops, double *clock_ghz,
+                          void *stream);
+
 /* Static text for a status code. */
 const char *fab_strerror(int status);
 /* Detail of the last error raised on the calling thread ("" if none). */

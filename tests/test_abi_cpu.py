@@ -186,3 +186,15 @@ def test_alibi_entry_points_reject_a_misaligned_slope_array():
     rc = L.fab_forward_lse_alibi(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE + 1), 0.5, 0, P(FAKE),
                                  P(FAKE), P(FAKE), 1 << 40, None)
     assert rc == fab.FAB_E_ALIGN
+
+
+def test_mfma_probe_rejects_bad_arguments_before_device_work():
+    L = fab.lib()
+    P = ctypes.c_void_p
+    n = L.fab_probe_scratch_bytes()
+    assert n >= 2048 * 512 * 4
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    assert L.fab_measure_mfma_loop(None, n, 10, ctypes.byref(tf), ctypes.byref(ghz), None) == fab.FAB_E_INVAL
+    assert L.fab_measure_mfma_loop(P(FAKE), n - 1, 10, ctypes.byref(tf), ctypes.byref(ghz), None) == fab.FAB_E_INVAL
+    assert "scratch" in L.fab_last_error().decode()
+    assert L.fab_measure_mfma_loop(P(FAKE), n, 0, ctypes.byref(tf), ctypes.byref(ghz), None) == fab.FAB_E_INVAL
