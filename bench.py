@@ -22,7 +22,8 @@ Beside it: `whole_path`, the op's own semantics (O = lse = NULL: the forward run
 inside fab_backward, counted as forward plus backward flops); `forward_only`;
 causal workloads with the causal rule passed as a flag instead of the mask tensor
 (`causal_flag_instead_of_mask`); bf16 mode with q, k, v, d stored as bf16
-(`bf16_inputs`) and with O stored as bf16 as well (`bf16_storage`); and `configs`: every other (workload, mode) pair of the five
+(`bf16_inputs`) and with O stored as bf16 as well (`bf16_storage`), or stored as f16
+(`f16_inputs`); and `configs`: every other (workload, mode) pair of the five
 workloads, each with its backward alone (and kernel split), whole path and
 fraction of its mode's peak.  `mfma_loop_ceiling` (bf16 mode) is the rate of a
 loop of dense bf16 products on every SIMD, with the shader clock it runs at: the
@@ -458,6 +459,15 @@ def main():
                                "backward_only": {"ms": round(ms_o, 4), "tflops": round(F_b / (ms_o * 1e-3) / 1e12, 3),
                                                  "frac_of_peak": round(F_b / (ms_o * 1e-3) / 1e12 / peak, 4)}}
         del tb, O16, lse16
+        # ... and q, k, v, d stored as f16 instead (FAB_F16_INPUTS: widened exactly, then
+        # rounded to bf16 like f32 inputs)
+        th = [x.to(torch.float16) for x in (tq, tk, tv, td)]
+        ms_h = time_loop(torch, lambda: fab.backward(*th, c.scale, mask=c.tm, mode=mode, O=c.O, lse=c.lse,
+                                                     blob=c.blob, ws=c.ws_bwd),
+                         args.steps, args.warmup, stream, args.min_warm_s)
+        out["f16_inputs"] = {"backward_only": {"ms": round(ms_h, 4), "tflops": round(F_b / (ms_h * 1e-3) / 1e12, 3),
+                                               "frac_of_peak": round(F_b / (ms_h * 1e-3) / 1e12 / peak, 4)}}
+        del th
 
     # ---- every other (workload, mode) pair, same protocol
     pairs = []

@@ -23,6 +23,7 @@ FAB_MODE_F32 = 0
 FAB_MODE_BF16 = 1
 FAB_CAUSAL = 0x100   # flag: the causal rule (key m seen by query n iff m <= n) without a mask
 FAB_BF16_INPUTS = 0x200   # flag: q, k, v, d are bf16 (bf16 mode only)
+FAB_F16_INPUTS = 0x800    # flag: q, k, v, d are f16 (bf16 mode only)
 FAB_BF16_O = 0x400        # flag: O is bf16 (bf16 mode only)
 MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
          FAB_MODE_BF16: FAB_MODE_BF16}
@@ -133,9 +134,12 @@ def blob_layout(shape: Shape):
     return tuple(x.value for x in o)
 
 
-def _mode(mode, causal, bf16_inputs=False, bf16_o=False):
-    return (MODES[mode] | (FAB_CAUSAL if causal else 0) | (FAB_BF16_INPUTS if bf16_inputs else 0)
-            | (FAB_BF16_O if bf16_o else 0))
+def _mode(mode, causal, inputs=None, bf16_o=False):
+    """The mode argument: mode | causal flag | input storage flag (inputs: the torch dtype
+    of q, k, v, d; float32 needs no flag) | bf16 O flag."""
+    import torch
+    flag = {torch.bfloat16: FAB_BF16_INPUTS, torch.float16: FAB_F16_INPUTS}.get(inputs, 0) if inputs is not None else 0
+    return MODES[mode] | (FAB_CAUSAL if causal else 0) | flag | (FAB_BF16_O if bf16_o else 0)
 
 
 def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False, causal=False) -> int:
@@ -167,11 +171,11 @@ def _mask_arg(mask):
 
 
 def _input_dtype(*ts):
-    """float32 or bfloat16, the same for every input tensor."""
+    """float32, bfloat16 or float16, the same for every input tensor."""
     import torch
     dt = ts[0].dtype
-    if dt not in (torch.float32, torch.bfloat16) or any(t.dtype != dt for t in ts):
-        raise TypeError("q, k, v (and d) must all be float32 or all bfloat16, got "
+    if dt not in (torch.float32, torch.bfloat16, torch.float16) or any(t.dtype != dt for t in ts):
+        raise TypeError("q, k, v (and d) must all be float32, all bfloat16 or all float16, got "
                         + ", ".join(str(t.dtype) for t in ts))
     return dt
 
@@ -243,13 +247,13 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
                 alibi=None, o_bf16=False):
     """O (B,N,H,DV) and the natural-log row LSE (B,H,N) of softmax(scale*q.k + mask) v.
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v
-    are float32, or bfloat16 (all three; mode "bf16").  alibi: float32 (H,) per-head
+    are float32, or bfloat16 or float16 (all three; mode "bf16").  alibi: float32 (H,) per-head
     slopes, adding alibi[h] * (m - n) to the score of query n at key m, or None.  O is
     float32, or bfloat16 (mode "bf16": a given bfloat16 O, or o_bf16=True)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
-    bf16_in = _input_dtype(q, k, v) == torch.bfloat16
+    in_dt = _input_dtype(q, k, v)
     _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
     _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
     _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
@@ -271,7 +275,7 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, True, dev, causal)
         _check(lib().fab_forward_lse_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
-                                           float(scale), _mode(mode, causal, bf16_in, o_bf16), _ptr(O), _ptr(lse),
+                                           float(scale), _mode(mode, causal, in_dt, o_bf16), _ptr(O), _ptr(lse),
                                            _ptr(ws), nbytes, _stream_handle(stream)))
     return O, lse
 
@@ -280,14 +284,14 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
              stream=None, causal=False, alibi=None):
     """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
-    are float32, or bfloat16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
+    are float32, or bfloat16 or float16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
     (float32, or bfloat16 as forward_lse wrote it) are both given (from forward_lse,
     with the same alibi) or both None.
     alibi: float32 (H,) per-head ALiBi slopes or None (see forward_lse)."""
     import torch
     s = shape_of(q, k, v)
     dev = q.device
-    bf16_in = _input_dtype(q, k, v, d) == torch.bfloat16
+    in_dt = _input_dtype(q, k, v, d)
     _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
     _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
     _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
@@ -315,7 +319,7 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
         _check(lib().fab_backward_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
-                                        _ptr(d), float(scale), _mode(mode, causal, bf16_in, o_bf16), _ptr(O),
+                                        _ptr(d), float(scale), _mode(mode, causal, in_dt, o_bf16), _ptr(O),
                                         _ptr(lse), _ptr(blob), _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 
@@ -332,7 +336,7 @@ def backward_noalloc(q, k, v, d, scale, blob, mask=None, mode="f32", O=None, lse
     import torch
     s = shape_of(q, k, v)
     dev = q.device
-    bf16_in = _input_dtype(q, k, v, d) == torch.bfloat16
+    in_dt = _input_dtype(q, k, v, d)
     _check_tensor(q, "q", (s.B, s.H, s.N, s.DK), (q.dtype,))
     _check_tensor(k, "k", (s.B, s.Hkv, s.M, s.DK), (q.dtype,))
     _check_tensor(v, "v", (s.B, s.Hkv, s.M, s.DV), (q.dtype,))
@@ -349,7 +353,7 @@ def backward_noalloc(q, k, v, d, scale, blob, mask=None, mode="f32", O=None, lse
         raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
     _check_devices(dev, k=k, v=v, d=d, mask=mask, O=O, lse=lse, blob=blob)
     _check(lib().fab_backward_noalloc(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                                      float(scale), _mode(mode, causal, bf16_in), _ptr(O), _ptr(lse), _ptr(blob),
+                                      float(scale), _mode(mode, causal, in_dt), _ptr(O), _ptr(lse), _ptr(blob),
                                       _stream_handle(stream)))
     return blob
 

@@ -175,19 +175,22 @@ int check_mode(int mode)
     return FAB_OK;
 }
 
-// Splits the FAB_CAUSAL, FAB_BF16_INPUTS and FAB_BF16_O flags off the mode argument
-// and checks the rest.
-int take_mode(int *mode, bool *causal, bool *in_bf16, bool *o_bf16 = nullptr)
+// Splits the FAB_CAUSAL, FAB_BF16_INPUTS, FAB_F16_INPUTS and FAB_BF16_O flags off the
+// mode argument and checks the rest; *in_fmt receives the storage of q, k, v and d.
+int take_mode(int *mode, bool *causal, int *in_fmt, bool *o_bf16 = nullptr)
 {
     *causal = (*mode & FAB_CAUSAL) != 0;
-    *in_bf16 = (*mode & FAB_BF16_INPUTS) != 0;
+    const bool ib = (*mode & FAB_BF16_INPUTS) != 0, ih = (*mode & FAB_F16_INPUTS) != 0;
     const bool ob = (*mode & FAB_BF16_O) != 0;
     if (o_bf16) *o_bf16 = ob;
-    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS | FAB_BF16_O);
+    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS | FAB_F16_INPUTS | FAB_BF16_O);
     const int rc = check_mode(*mode);
     if (rc != FAB_OK) return rc;
-    if (*in_bf16 && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS needs FAB_MODE_BF16");
+    if (ib && ih) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS and FAB_F16_INPUTS are exclusive");
+    if (ib && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS needs FAB_MODE_BF16");
+    if (ih && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_F16_INPUTS needs FAB_MODE_BF16");
     if (ob && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_O needs FAB_MODE_BF16");
+    *in_fmt = ib ? fab::kBF16 : (ih ? fab::kF16 : fab::kF32);
     return FAB_OK;
 }
 
@@ -406,8 +409,9 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal, in_bf16;
-    FAB_TRY(take_mode(&mode, &causal, &in_bf16));
+    bool causal;
+    int in_fmt;
+    FAB_TRY(take_mode(&mode, &causal, &in_fmt));
     if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
     if (causal && has_mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     plan_workspace(&pl, mode, has_mask != 0, have_o_lse != 0);
@@ -422,12 +426,13 @@ int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, 
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal, in_bf16, o_bf16;
-    FAB_TRY(take_mode(&mode, &causal, &in_bf16, &o_bf16));
+    bool causal, o_bf16;
+    int in_fmt;
+    FAB_TRY(take_mode(&mode, &causal, &in_fmt, &o_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
-    pl.d.in_bf16 = in_bf16;
+    pl.d.in_fmt = in_fmt;
     pl.d.o_bf16 = o_bf16;
     pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");
@@ -464,12 +469,13 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
-    bool causal, in_bf16, o_bf16;
-    FAB_TRY(take_mode(&mode, &causal, &in_bf16, &o_bf16));
+    bool causal, o_bf16;
+    int in_fmt;
+    FAB_TRY(take_mode(&mode, &causal, &in_fmt, &o_bf16));
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
-    pl.d.in_bf16 = in_bf16;
+    pl.d.in_fmt = in_fmt;
     pl.d.o_bf16 = o_bf16;
     pl.d.alibi = alibi;
     if (!std::isfinite(scale)) return fail(FAB_E_INVAL, "scale is not finite");

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 // One packing job: heads of M rows of D floats -> bf16 tiles [heads][Mp][DP].  Row
 // m of head hd = hh + H*bb starts at src + hh*sh + bb*sb + m*rs floats.
 struct PackJob {
-    const void *src;                  // f32 rows, or bf16 rows when src_bf16
-    int src_bf16;
+    const void *src;                  // rows of f32, bf16 or f16 elements (src_fmt: kF32, kBF16, kF16)
+    int src_fmt;
     __bf16 *dst;
     int64_t sh, sb, rs;
     int H, M, Mp, D, vec;
@@ -194,8 +194,8 @@ __device__ __forceinline__ void pack_tile(const PackJob &j, int bt, const PrepEx
         const int r = idx / C4, col = 4 * (idx - r * C4);
         const int m = t * 64 + r;
         const bool ok = idx < 64 * C4 && m < j.M;
-        xv[i] = ok ? load_row4_any(j.src, head_off + m * j.rs, col, j.D, j.vec, j.src_bf16) : z;
-        yv[i] = (ok && obase) ? load_row4_any(obase, head_off + m * j.rs, col, j.D, j.vec, x->O_bf16) : z;
+        xv[i] = ok ? load_row4_any(j.src, head_off + m * j.rs, col, j.D, j.vec, j.src_fmt) : z;
+        yv[i] = (ok && obase) ? load_row4_any(obase, head_off + m * j.rs, col, j.D, j.vec, x->O_bf16 ? kBF16 : kF32) : z;
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -289,10 +289,10 @@ __global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, int npack, P
 }
 
 namespace {
-PackJob rows_job(const void *src, int src_bf16, __bf16 *dst, int64_t heads, int M, int Mp, int D)
+PackJob rows_job(const void *src, int src_fmt, __bf16 *dst, int64_t heads, int M, int Mp, int D)
 {
     PackJob j = {};
-    j.src = src; j.src_bf16 = src_bf16; j.dst = dst;
+    j.src = src; j.src_fmt = src_fmt; j.dst = dst;
     j.H = 1; j.sh = 0; j.sb = (int64_t)M * D; j.rs = D;   // heads are consecutive blocks of M rows
     j.M = M; j.Mp = Mp; j.D = D; j.vec = (D % 4 == 0);
     j.tiles = (int)(heads * (Mp / 64));
@@ -315,9 +315,9 @@ PackJobs pack_jobs(const void *q, const void *k, const void *v, __bf16 *q16, __b
 {
     PackJobs a = {};
     const int64_t qh = q ? (int64_t)d.H * d.B : 0, kh = (int64_t)d.Hkv * d.B;
-    a.j[0] = rows_job(q, d.in_bf16, q16, qh, d.N, Np, d.DK);
-    a.j[1] = rows_job(k, d.in_bf16, k16, kh, d.M, Mp, d.DK);
-    a.j[2] = rows_job(v, d.in_bf16, v16, kh, d.M, Mp, d.DV);
+    a.j[0] = rows_job(q, d.in_fmt, q16, qh, d.N, Np, d.DK);
+    a.j[1] = rows_job(k, d.in_fmt, k16, kh, d.M, Mp, d.DK);
+    a.j[2] = rows_job(v, d.in_fmt, v16, kh, d.M, Mp, d.DV);
     if (map) {
         a.mask = mask; a.map = map; a.N = d.N; a.M = d.M;
         a.nqb = (d.N + kMapTile - 1) / kMapTile; a.nkb = (d.M + kMapTile - 1) / kMapTile;
@@ -331,7 +331,7 @@ void prep_job(const void *dO, const void *O, const float *lse, __bf16 *dO16, flo
               const Dims &d, PackJob *pj, PrepExtra *px)
 {
     PackJob j = {};
-    j.src = dO; j.src_bf16 = d.in_bf16; j.dst = dO16;
+    j.src = dO; j.src_fmt = d.in_fmt; j.dst = dO16;
     // d, O [DV,H,N,B]: row n of head (h, b) at DV*(h + H*(n + N*b))
     j.H = d.H; j.sh = d.DV; j.sb = (int64_t)d.DV * d.H * d.N; j.rs = (int64_t)d.DV * d.H;
     j.M = d.N; j.Mp = Np; j.D = d.DV; j.vec = (d.DV % 4 == 0);

@@ -213,11 +213,30 @@ __device__ __forceinline__ f32x4 load_row4(const __bf16 *row, int c, int D, bool
     return r;
 }
 
-// Row m of a tensor of f32 (bf16 == 0) or bf16 (bf16 != 0) elements, elem_off
-// elements past base: four entries from column c.
-__device__ __forceinline__ f32x4 load_row4_any(const void *base, int64_t elem_off, int c, int D, bool vec, int bf16)
+// The same from a row of IEEE binary16 values (widened to f32, exactly).
+__device__ __forceinline__ f32x4 load_row4(const _Float16 *row, int c, int D, bool vec)
 {
-    if (bf16) return load_row4(static_cast<const __bf16 *>(base) + elem_off, c, D, vec);
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    if (c >= D) return r;
+    if (vec) {
+        const f16x4 x = *reinterpret_cast<const f16x4 *>(row + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = (float)x[i];
+        return r;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (c + i < D) r[i] = (float)row[c + i];
+    return r;
+}
+
+// Row m of a tensor of f32, bf16 or f16 elements (fmt), elem_off elements past base:
+// four entries from column c, as f32 (the 16-bit forms widened exactly).
+__device__ __forceinline__ f32x4 load_row4_any(const void *base, int64_t elem_off, int c, int D, bool vec, int fmt)
+{
+    if (fmt == kBF16) return load_row4(static_cast<const __bf16 *>(base) + elem_off, c, D, vec);
+    if (fmt == kF16) return load_row4(static_cast<const _Float16 *>(base) + elem_off, c, D, vec);
     return load_row4(static_cast<const float *>(base) + elem_off, c, D, vec);
 }
 

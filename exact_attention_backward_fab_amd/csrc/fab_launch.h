@@ -10,10 +10,13 @@
 
 namespace fab {
 
+// Storage formats of an input tensor.
+constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
+
 struct Dims {
     int B, H, Hkv, N, M, DK, DV;
     int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
-    int in_bf16 = 0;  // q, k, v and d are bf16 (bf16 mode only); otherwise f32
+    int in_fmt = 0;   // storage of q, k, v and d: kF32, kBF16 or kF16 (the 16-bit forms in bf16 mode only)
     int o_bf16 = 0;   // O is bf16 (bf16 mode only): written so by the forward, read so by the prep
     const float *alibi = nullptr;   // per-query-head ALiBi slopes [H] (device) or NULL: score += slope_h (m - n)
 };

@@ -138,17 +138,17 @@ __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const cha
     }
 }
 
-// Per-lane query operands: B operands of S^T = K Q^T (Q rows, f32 -> bf16) for
-// query row `row` (all zero when !ok).
+// Per-lane query operands: B operands of S^T = K Q^T (Q rows of f32, bf16 or f16
+// elements, fmt, -> bf16) for query row `row` (all zero when !ok).
 template <int DKP>
 __device__ __forceinline__ void load_q_operand(bf16x8 *qf, const void *q, int64_t row_off, bool ok, int DK, int vecK,
-                                               int half, int in_bf16)
+                                               int half, int fmt)
 {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DKP / 16; ++t) {
-        const f32x4 lo = ok ? load_row4_any(q, row_off, 16 * t + 8 * half, DK, vecK, in_bf16) : z;
-        const f32x4 hi = ok ? load_row4_any(q, row_off, 16 * t + 8 * half + 4, DK, vecK, in_bf16) : z;
+        const f32x4 lo = ok ? load_row4_any(q, row_off, 16 * t + 8 * half, DK, vecK, fmt) : z;
+        const f32x4 hi = ok ? load_row4_any(q, row_off, 16 * t + 8 * half + 4, DK, vecK, fmt) : z;
         qf[t] = __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
@@ -267,8 +267,8 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
 
 // ============================================================== forward
 struct FwdArgs16 {
-    const void *q;                  // f32, or bf16 when in_bf16 (as dO)
-    int in_bf16;
+    const void *q;                  // f32, bf16 or f16 elements (in_fmt: kF32, kBF16, kF16; as dO)
+    int in_fmt;
     const __bf16 *k16, *v16;        // bf16 [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP] in 64-row tiles, rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
@@ -318,7 +318,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const rsrc_t rv = make_rsrc(p.v16 + kvrow * DVP, (uint32_t)(p.Mp * DVP) * 2u);
 
     bf16x8 qf[DKP / 16];
-    load_q_operand<DKP>(qf, p.q, (int64_t)(hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half, p.in_bf16);
+    load_q_operand<DKP>(qf, p.q, (int64_t)(hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half, p.in_fmt);
     const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // PREP: first tile row of this head
     if constexpr (PREP) {
         if (myq < p.Np) {
@@ -423,7 +423,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int c0 = dt * 32 + 8 * r4 + 4 * half;
-                const f32x4 dv = qok ? load_row4_any(p.dO, drow, c0, p.DV, p.vecV, p.in_bf16) : z;
+                const f32x4 dv = qok ? load_row4_any(p.dO, drow, c0, p.DV, p.vecV, p.in_fmt) : z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dsum += dv[i] * (oacc[dt][4 * r4 + i] * inv);
                 *reinterpret_cast<bf16x4 *>(ot16 + tile_elem(myq, c0, DVP)) = to_bf16x4(dv);
@@ -864,7 +864,7 @@ hipError_t launch_forward_bf16(const void *q, const __bf16 *k16, const __bf16 *v
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map; a.O = O; a.o_bf16 = d.o_bf16; a.lse = lse;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
-    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
+    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_fmt = d.in_fmt;
     a.scale = scale;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
 }
@@ -881,7 +881,7 @@ hipError_t launch_forward_prep_bf16(const void *q, const __bf16 *k16, const __bf
     a.q = q; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
-    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_bf16 = d.in_bf16;
+    a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_fmt = d.in_fmt;
     a.scale = scale;
     a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
     a.pad_lo[0] = nq; a.pad_hi[0] = off_k;

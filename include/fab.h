@@ -98,8 +98,17 @@ typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
  * [DV,H,N,B]) instead of f32 -- written so by fab_forward_lse (the f32 output
  * rounded to nearest even) and read so by fab_backward (D = rowsum(dO o O) from
  * those values, widened exactly).  FAB_MODE_BF16 only (FAB_E_INVAL otherwise);
- * it combines with FAB_BF16_INPUTS.  lse and the blob stay f32. */
+ * it combines with FAB_BF16_INPUTS or FAB_F16_INPUTS.  lse and the blob stay f32. */
 #define FAB_BF16_O 0x400
+
+/* Flag OR-ed into the mode argument: q, k, v and d are IEEE binary16 (f16, the
+ * 16-bit storage of the ggmlR reference manual's tensors; same layouts) instead
+ * of f32.  Each value is widened exactly to f32 and then handled as an f32 input
+ * (rounded to bf16 for the matrix cores; D = rowsum(dO o O) from the widened dO),
+ * so the results equal those for the f32 inputs holding the same values.
+ * FAB_MODE_BF16 only, and not together with FAB_BF16_INPUTS (FAB_E_INVAL
+ * otherwise); O (unless FAB_BF16_O), lse and the blob stay f32. */
+#define FAB_F16_INPUTS 0x800
 
 typedef enum fab_status {
     FAB_OK = 0,
@@ -127,11 +136,12 @@ int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have
 
 /* Forward with row log-sum-exp (labml "Flash Attention": "Forward pass" and the
  * running max/sum of "Flash Attention Optimization").
- *   q, k, v   device, f32 (bf16 with FAB_BF16_INPUTS), layouts above (read only)
+ *   q, k, v   device, f32 (bf16 with FAB_BF16_INPUTS, f16 with FAB_F16_INPUTS), layouts
+ *             above (read only)
  *   mask      device f16 bits [M,N] or NULL for no mask (read only)
  *   scale     finite f32 softmax scale
  *   mode      fab_mode, optionally | FAB_CAUSAL (then mask must be NULL)
- *             | FAB_BF16_INPUTS, FAB_BF16_O (FAB_MODE_BF16 only)
+ *             | FAB_BF16_INPUTS or FAB_F16_INPUTS, FAB_BF16_O (FAB_MODE_BF16 only)
  *   O         device f32 (bf16 with FAB_BF16_O) [DV,H,N,B] (written):
  *             softmax(scale*q.k + mask) v
  *   lse       device f32 [N,H,B] (written): natural-log log-sum-exp of the row's
@@ -145,7 +155,7 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
 /* The attention backward ("Function ggml_flash_attn_back"; ggmlR
  * `fab_grads`): gradients of sum(d * attn(q,k,v)) packed into blob.
  *   q, k, v, mask, scale, mode  as for fab_forward_lse
- *   d         device f32 (bf16 with FAB_BF16_INPUTS) [DV,H,N,B]: upstream gradient
+ *   d         device f32 (bf16 / f16 with FAB_BF16_INPUTS / FAB_F16_INPUTS) [DV,H,N,B]: upstream gradient
  *             of the attention output
  *   O, lse    either both NULL (the forward is recomputed internally, the
  *             pages' semantics) or both given: the output and row LSE of the

@@ -125,7 +125,9 @@ GOOD = (1, 4, 2, 8, 8, 16, 16)
     (GOOD, {"ws": None}, fab.FAB_E_WORKSPACE),
     (GOOD, {"ws_bytes": 16}, fab.FAB_E_WORKSPACE),
     (GOOD, {"mode": fab.FAB_CAUSAL, "mask": FAKE}, fab.FAB_E_INVAL),         # mask and causal flag
-    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x800}, fab.FAB_E_INVAL),           # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x1000}, fab.FAB_E_INVAL),          # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_F16_INPUTS}, fab.FAB_E_INVAL),   # f16 inputs need bf16 mode
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | fab.FAB_F16_INPUTS | fab.FAB_BF16_INPUTS}, fab.FAB_E_INVAL),  # one input storage
     (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_BF16_O, "O": FAKE, "lse": FAKE}, fab.FAB_E_INVAL),  # bf16 O needs bf16 mode
     (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_BF16_INPUTS}, fab.FAB_E_INVAL),  # bf16 inputs need bf16 mode
 ])

@@ -72,7 +72,20 @@ def test_inputs_of_mixed_dtype_or_shape_are_refused():
     q, k, v, d = inputs()
     with pytest.raises(TypeError):
         fab.backward(q, k.double(), v, d, 0.25)
+    with pytest.raises(TypeError):
+        fab.backward(q.half(), k.half(), v.bfloat16(), d.half(), 0.25, mode="bf16")
     with pytest.raises(ValueError, match="d has shape"):
         fab.backward(q, k, v, d.transpose(1, 2).contiguous(), 0.25)
     with pytest.raises(ValueError, match="contiguous"):
         fab.backward(q.transpose(2, 3).contiguous().transpose(2, 3), k, v, d, 0.25)
+
+
+def test_float16_inputs_pass_the_checks_and_set_the_flag():
+    """float16 q, k, v, d are accepted (bf16 mode); the mode argument carries
+    FAB_F16_INPUTS, bfloat16 inputs FAB_BF16_INPUTS; the call then stops at the device check."""
+    q, k, v, d = (x.half() for x in inputs())
+    with pytest.raises(ValueError, match="GPU"):
+        fab.backward(q, k, v, d, 0.25, mode="bf16")
+    assert fab._mode("bf16", False, torch.float16) == fab.FAB_MODE_BF16 | fab.FAB_F16_INPUTS
+    assert fab._mode("bf16", True, torch.bfloat16) == fab.FAB_MODE_BF16 | fab.FAB_CAUSAL | fab.FAB_BF16_INPUTS
+    assert fab._mode("f32", False, torch.float32) == fab.FAB_MODE_F32

@@ -300,20 +300,23 @@ BF16_IN = [
 ]
 
 
+@pytest.mark.parametrize("store", ["bf16", "f16"])
 @pytest.mark.parametrize("supplied", [False, True], ids=["own_forward", "o_lse_supplied"])
 @pytest.mark.parametrize("name,s,mkind,seed", BF16_IN, ids=[c[0] for c in BF16_IN])
-def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mkind, seed, supplied):
-    # FAB_BF16_INPUTS: q, k, v, d stored as bf16 give bit for bit the result of the
-    # f32 inputs holding the same (bf16) values -- the values bf16 mode rounds to
-    # anyway -- and that result matches the oracle on those values
+def test_16bit_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mkind, seed, supplied, store):
+    # FAB_BF16_INPUTS / FAB_F16_INPUTS: q, k, v, d stored as bf16 (the values bf16 mode
+    # rounds to anyway) or as f16 (widened exactly, then rounded like f32 inputs) give
+    # bit for bit the result of the f32 inputs holding the same values, and that
+    # result matches the oracle on those values
     torch, dev = torch_dev
     fab = fabmod()
-    print(f"[parity] bf16 inputs {name} supplied={supplied} {s}", flush=True)
+    print(f"[parity] {store} inputs {name} supplied={supplied} {s}", flush=True)
     q, k, v, d = make_qkvd(s, seed)
     mask = small_mask(mkind, s, seed)
     tm = to_dev(torch, dev, mask)
     scale = float(np.float32(1.0 / math.sqrt(s.DK)))
-    t16 = [to_dev(torch, dev, x).to(torch.bfloat16) for x in (q, k, v, d)]
+    dt16 = torch.bfloat16 if store == "bf16" else torch.float16
+    t16 = [to_dev(torch, dev, x).to(dt16) for x in (q, k, v, d)]
     t32 = [x.float() for x in t16]
     outs = []
     for t in (t16, t32):
@@ -329,7 +332,7 @@ def test_bf16_inputs_equal_f32_inputs_of_the_same_values(torch_dev, name, s, mki
     qr, kr, vr, dr = (x.cpu().numpy() for x in t32)
     ref = oracle_full(s, qr, kr, vr, dr, mask, scale)
     total = fab.blob_layout(fab.Shape(*s.astuple()))[3]
-    check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"bf16 inputs {name}", mask=mask)
+    check_blob(s, outs[0][:total].cpu().numpy(), ref, "bf16", tag=f"{store} inputs {name}", mask=mask)
 
 
 @pytest.mark.parametrize("inputs16", [False, True], ids=["f32_inputs", "bf16_inputs"])
