@@ -69,6 +69,8 @@ struct KvArgs {
     // of a pair sit side by side, so the dQ product reads one contiguous stream.
     // Pairs the block map skips are not written.
     __bf16 *ds;
+    uint32_t ds_bytes;              // extent of ds (below 4 GiB)
+    int ds_cached;                  // dS^T stores through the caches (small totals, read back from them)
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
     int hpw;                        // query heads of one group per work-group (1 or 2), summed in registers
     int part_heads, nqb, nkb, nkb128;
@@ -137,6 +139,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float kbias = mykey < p.M ? 0.f : -INFINITY;  // keys past M never get weight
     const float sl2 = p.scale * kLog2e;
     const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
+    const rsrc_t rds = make_rsrc(p.ds, p.ds_bytes);   // the dS^T tiles (p.ds: dq_from_ds shapes only)
 
     // ---- the block's K and V rows (B operands of S = Q K^T and dP = dO V^T, one key
     // per lane) into LDS: 2 tiles of each, copied by chunk columns
@@ -295,12 +298,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     // the dS^T operands of this step, for dQ = scale dS K: stored before the
                     // products so that the stores complete behind them (the next step's
                     // vmcnt wait counts them too); streaming stores, which leave the L2 to
-                    // the Q and dO tiles this kernel re-reads
-                    __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
-                                        (kw >> 1) * 2 + (it & 1)) * 4096 +
-                                (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8;
-                    __builtin_nontemporal_store(da[0], reinterpret_cast<bf16x8 *>(t));
-                    __builtin_nontemporal_store(da[1], reinterpret_cast<bf16x8 *>(t + 1024));
+                    // the Q and dO tiles this kernel re-reads, unless the tiles are few
+                    // enough to be read back from the caches by the dQ launch
+                    const uint32_t t = 2u * (uint32_t)(((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
+                                                         (kw >> 1) * 2 + (it & 1)) * 4096 +
+                                                        (4 * qq + half) * 512 + (32 * (kw & 1) + l32) * 8);
+                    buf_store16(rds, t, da[0], p.ds_cached);
+                    buf_store16(rds, t + 2048u, da[1], p.ds_cached);
                 }
                 {
                     // the transposed operands of both halves' dV and dK products in one
@@ -440,6 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float sl2 = p.scale * kLog2e;
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
+    const rsrc_t rds = make_rsrc(p.ds, p.ds_bytes);   // the dS^T tiles (p.ds: dq_from_ds shapes only)
 
     // ---- this lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[DKP / 16], vf[DVP / 16];
@@ -595,11 +600,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     da4[2 * qq + u] = da;
                     if (p.ds) {
                         // the dS^T operands of this step for dQ = scale dS K, in the tile
-                        // layout bwd_bf16_kernel stores (streaming stores)
-                        __bf16 *t = p.ds + ((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
-                                            (w >> 1) * 2 + (it & 1)) * 4096 +
-                                    (4 * qq + half) * 512 + u * 1024 + (32 * (w & 1) + l32) * 8;
-                        __builtin_nontemporal_store(da, reinterpret_cast<bf16x8 *>(t));
+                        // layout and with the stores bwd_bf16_kernel uses
+                        const uint32_t t = 2u * (uint32_t)(((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
+                                                             (w >> 1) * 2 + (it & 1)) * 4096 +
+                                                            (4 * qq + half) * 512 + u * 1024 + (32 * (w & 1) + l32) * 8);
+                        buf_store16(rds, t, da, p.ds_cached);
                     }
                 }
             {
@@ -1020,6 +1025,10 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     KvArgs a;
     a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
     a.dk = dk; a.dv = dv; a.ds = ds; a.nkb128 = ceil_div(d.M, 128);
+    // dS^T totals up to 64 MiB stay in the caches between the two launches (the dQ
+    // launch reads them back from there); larger ones are streamed past the L2
+    a.ds_bytes = ds ? (uint32_t)ds_bytes(d, Np) : 0u;
+    a.ds_cached = ds && ds_bytes(d, Np) <= ((int64_t)64 << 20);
     a.hpw = bwd_heads_per_wg(d, hd.dk, hd.dv);
     // partials only while a head unit is smaller than its group
     if (part_heads != (d.H / d.Hkv / a.hpw > 1 ? 1 : 0)) return hipErrorInvalidValue;

@@ -129,6 +129,16 @@ __device__ __forceinline__ void buf_atomic_add_f32(rsrc_t r, uint32_t byte_off, 
 {
     __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
 }
+// A 16-byte store either through the caches (cached) or streamed past the L2
+// (the nontemporal cache policy, immediate 2).  The two are separate intrinsic calls
+// with different immediates, so the compiler cannot merge them into one store with
+// the policy dropped (as it does with a nontemporal and a plain store of one value).
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t byte_off, const bf16x8 &v, bool cached)
+{
+    const u32x4 x = __builtin_bit_cast(u32x4, v);
+    if (cached) __builtin_amdgcn_raw_buffer_store_b128(x, r, byte_off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b128(x, r, byte_off, 0, 2);
+}
 
 // ---------------------------------------------------------------- LDS tile layouts
 // Row-major bf16 tiles of D columns, stored without padding; the 16-byte chunks
