@@ -46,7 +46,7 @@ struct Plan {
     int mp;        // key rows per head of the bf16 K / V copies
     bool gqa;
     bool ds;       // bf16 mode: dQ from the stored dS^T tiles (else the recompute kernel)
-    int hpw;       // query heads per work-group of the dK/dV kernel (its partials per head unit)
+    int upg;       // dK/dV partials per key/value head (1: none, the kernels write the result)
     bool part;     // dK/dV go through per-unit partials and the grouped-query reduction
 };
 
@@ -147,8 +147,8 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         off = align_up(off + sizeof(float) * qrows / 64 * 128);
     }
     pl->ds = mode == FAB_MODE_BF16 && fab::dq_from_ds(d, pl->np, pl->dkp, pl->dvp);
-    pl->hpw = mode == FAB_MODE_BF16 ? fab::bwd_heads_per_wg(d, pl->dkp, pl->dvp) : 1;
-    pl->part = d.H / d.Hkv / pl->hpw > 1;
+    pl->upg = mode == FAB_MODE_BF16 ? fab::bwd_units_per_group(d, pl->dkp, pl->dvp) : d.H / d.Hkv;
+    pl->part = pl->upg > 1;
     pl->ws_dqp = off;
     pl->ws_tick = off;
     pl->ws_ds = off;
@@ -161,10 +161,10 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
     }
     pl->ws_pk = off;
     pl->ws_pv = off;
-    if (pl->part) {   // one partial per head unit of hpw query heads
-        off = align_up(off + sizeof(float) * (size_t)d.DK * d.M * (d.H / pl->hpw) * d.B);
+    if (pl->part) {   // one partial per unit (head unit x query split)
+        off = align_up(off + sizeof(float) * (size_t)d.DK * d.M * ((size_t)d.Hkv * pl->upg) * d.B);
         pl->ws_pv = off;
-        off = align_up(off + sizeof(float) * (size_t)d.DV * d.M * (d.H / pl->hpw) * d.B);
+        off = align_up(off + sizeof(float) * (size_t)d.DV * d.M * ((size_t)d.Hkv * pl->upg) * d.B);
     }
     pl->ws_bytes = off;
 }
@@ -559,7 +559,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
                    "backward launch");
         if (pl.ds)   // with the grouped-query reduction of dK and dV in the same launch
             FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.part ? dk : nullptr,
-                                                   blob + pl.off_k, pl.part ? dv : nullptr, blob + pl.off_v, pl.hpw,
+                                                   blob + pl.off_k, pl.part ? dv : nullptr, blob + pl.off_v, pl.upg,
                                                    pl.d, s),
                        "dQ launch");
         else
@@ -574,7 +574,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
                    "backward launch");
     }
     if (pl.part && !pl.ds) {
-        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, pl.hpw, s),
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, pl.upg, s),
                    "dK/dV reduce launch");
     }
     return FAB_OK;

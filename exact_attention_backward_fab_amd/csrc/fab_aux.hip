@@ -389,7 +389,7 @@ hipError_t launch_pack_prep_bf16(const void *q, const void *k, const void *v, __
 
 // ============================================================== GQA reduce
 // dK and dV in one launch: work items [0, n0) reduce job 0, the rest job 1; each
-// sums the rk2 per-query-head partials of a group in head order.
+// sums the rk2 partials of a group in unit order.
 __global__ __launch_bounds__(256) void gqa_reduce_kernel(ReduceJob j0, ReduceJob j1, int rk2)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -434,11 +434,11 @@ hipError_t launch_prep(const float *dO, const float *O, float *delta, float *blo
     return hipGetLastError();
 }
 
-hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int upg,
                              hipStream_t s)
 {
     ReduceJob j[2];
-    const int rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, hpw, j);
+    const int rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, upg, j);
     const int64_t work = j[0].items + j[1].items;
     if (work == 0) return hipSuccess;
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);

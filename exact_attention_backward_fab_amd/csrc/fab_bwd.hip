@@ -73,6 +73,7 @@ struct KvArgs {
     int ds_cached;                  // dS^T stores through the caches (small totals, read back from them)
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
     int hpw;                        // query heads of one group per work-group (1 or 2), summed in registers
+    int qsplit;                     // work-groups per (key block, head unit) on interleaved query steps (8-wave kernel)
     int part_heads, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
@@ -120,19 +121,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t qo_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sQO;
 
-    // ---- work-group -> (key block, head unit of hpw query heads of one group): first
-    // key blocks first (under a causal mask they see the most queries); units dealt to
-    // the XCDs in contiguous ranges
-    const int hpu = p.H / p.hpw, HU = hpu * p.B;
-    int kb, hu;
+    // ---- work-group -> (key block, head unit of hpw query heads of one group, query
+    // split): first key blocks first (under a causal mask they see the most queries);
+    // units dealt to the XCDs in contiguous ranges, the splits of a unit side by side
+    const int qs = p.qsplit;
+    const int hpu = p.H / p.hpw, HU = hpu * p.B * qs;
+    int kb, hus;
     if (HU % 8 == 0) {
         const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HU / 8;
         kb = jj / per;
-        hu = xcd * per + jj % per;
+        hus = xcd * per + jj % per;
     } else {
         kb = blockIdx.x / HU;
-        hu = blockIdx.x % HU;
+        hus = blockIdx.x % HU;
     }
+    const int split = hus % qs, hu = hus / qs;   // this work-group takes live steps split, split + qs, ...
     const int hp = hu % hpu, b = hu / hpu, g = hp * p.hpw / (p.H / p.Hkv);
     const int key0 = kb * kKBC;
     const int mykey = key0 + 32 * kw + l32;  // this lane's key in the C layout of S and dP
@@ -208,15 +211,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 return tile_class<kKBR / kMapTile, kKBC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, it * (kKBR / kMapTile),
                                   key0 / kMapTile);
             });
-            if (count == 0) continue;
+            // this work-group's share of the live steps: list entries split + qs li
+            const int mine = count > split ? (count - split + qs - 1) / qs : 0;
+            if (mine == 0) continue;
     #pragma unroll
             for (int i = 0; i < NS - 1; ++i)
-                if (i < count) issue(sList[i] >> 2, i);
-            for (int li = 0; li < count; ++li) {
-                wait_vm_steps<PER>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
-                __syncthreads();                                    // ... for every wave; stage li-1 is free
-                if (li + NS - 1 < count) issue(sList[li + NS - 1] >> 2, (li + NS - 1) % NS);
-                const int e = sList[li];
+                if (i < mine) issue(sList[split + qs * i] >> 2, i);
+            for (int li = 0; li < mine; ++li) {
+                wait_vm_steps<PER>(min(mine - 1 - li, NS - 2));   // step li has landed (this wave)
+                __syncthreads();                                   // ... for every wave; stage li-1 is free
+                if (li + NS - 1 < mine) issue(sList[split + qs * (li + NS - 1)] >> 2, (li + NS - 1) % NS);
+                const int e = sList[split + qs * li];
                 const int it = e >> 2, cls = e & 3;
                 const int q0 = it * kKBR;
                 const char *Qb = sQO + (li % NS) * ST::kBytes;
@@ -364,9 +369,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int r = 0; r < 16; ++r) dvacc[dt][r] += xch[(16 * dt + r) * 64 + lane];
     }
 
-    // ---- store dK (scaled) and dV of this key block: per head unit (partials) or,
-    // when a unit covers the whole group, into the result
-    const int hdd = p.part_heads ? hp : g, Hd = p.part_heads ? hpu : p.Hkv;
+    // ---- store dK (scaled) and dV of this key block: per unit (head unit x query
+    // split; partials) or, when a unit covers the whole group, into the result
+    const int hdd = p.part_heads ? hp * qs + split : g, Hd = p.part_heads ? hpu * qs : p.Hkv;
     float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
     float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
 #pragma unroll
@@ -980,7 +985,7 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
     if constexpr (!BF16) {
         return hipErrorInvalidValue;
     } else if constexpr (DKP + DVP <= 256) {
-        const dim3 grid(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B);
+        const dim3 grid(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B * a.qsplit);
         if (a.alibi)
             hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, true>), grid, dim3(kKNT), 0, s, a);
         else
@@ -1030,8 +1035,9 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     a.ds_bytes = ds ? (uint32_t)ds_bytes(d, Np) : 0u;
     a.ds_cached = ds && ds_bytes(d, Np) <= ((int64_t)64 << 20);
     a.hpw = bwd_heads_per_wg(d, hd.dk, hd.dv);
-    // partials only while a head unit is smaller than its group
-    if (part_heads != (d.H / d.Hkv / a.hpw > 1 ? 1 : 0)) return hipErrorInvalidValue;
+    a.qsplit = bwd_query_splits(d, hd.dk, hd.dv);
+    // partials only while a unit (head unit x query split) is smaller than its group
+    if (part_heads != (bwd_units_per_group(d, hd.dk, hd.dv) > 1 ? 1 : 0)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;

@@ -164,11 +164,32 @@ inline int bwd_heads_per_wg(const Dims &d, int dkp, int dvp)
     return (dkp + dvp <= 256 && rk2 % 2 == 0 && (int64_t)((d.M + 127) / 128) * d.H * d.B >= 1024) ? 2 : 1;
 }
 
+// Query splits of the 8-wave dK/dV kernel (bf16 mode): on a grid smaller than one
+// work-group per CU, each (key block, head unit) is run by qs work-groups that take
+// interleaved live query steps, each writing its own dK/dV partial (summed with the
+// grouped-query reduction).  The 4-wave kernel of the 192-wide heads does not split.
+inline int bwd_query_splits(const Dims &d, int dkp, int dvp)
+{
+    if (dkp + dvp > 256) return 1;
+    const int64_t wgs = (int64_t)((d.M + 127) / 128) * (d.H / bwd_heads_per_wg(d, dkp, dvp)) * d.B;
+    int qs = 1;
+    while (qs < 4 && wgs * qs < 256) qs *= 2;
+    return qs;
+}
+
+// dK/dV partials per key/value head of the bf16 dK/dV kernels: head units (of
+// bwd_heads_per_wg query heads) times query splits; 1 = no partials (the kernel
+// writes the result).
+inline int bwd_units_per_group(const Dims &d, int dkp, int dvp)
+{
+    return d.H / d.Hkv / bwd_heads_per_wg(d, dkp, dvp) * bwd_query_splits(d, dkp, dvp);
+}
+
 // Key-block-outer backward, bf16 mode: dV, dK from the bf16 tiles of Q, dO
 // (launch_pack_prep_bf16 or the forward of launch_forward_prep_bf16, Np rows per head), K, V (Mp rows per head)
-// and the LSE/D blocks.  With part_heads, per head unit of hpw = bwd_heads_per_wg
-// query heads into dk/dv [D,M,H/hpw,B] partials; else (a unit covers its group)
-// into dk/dv [D,M,Hkv,B].  With ds (dq_from_ds shapes only) it also stores the
+// and the LSE/D blocks.  With part_heads (bwd_units_per_group > 1), one partial per
+// unit into dk/dv [D,M,Hkv*upg,B] (unit = head unit of bwd_heads_per_wg query heads
+// times query split); else (a unit covers its group) into dk/dv [D,M,Hkv,B].  With ds (dq_from_ds shapes only) it also stores the
 // dS^T tiles of every pair it visits.
 hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const float *stats, const __bf16 *k16,
                                 const __bf16 *v16, const uint16_t *mask, const uint8_t *map, float scale, float *dk,
@@ -179,7 +200,7 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
 // also runs the grouped-query reduction of launch_gqa_reduce (extra work-groups
 // that take the CU slots the short query blocks free).
 hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
-                             int Mp, const float *pk, float *dk, const float *pv, float *dv, int hpw, const Dims &d,
+                             int Mp, const float *pk, float *dk, const float *pv, float *dv, int upg, const Dims &d,
                              hipStream_t s);
 
 // dQ work split.  Query blocks have kDqBlock rows.  A grid of at most
@@ -211,9 +232,8 @@ struct ReduceJob {
     int vec;         // chunk % 4 == 0: float4 items
     int64_t items;   // work items (float4 or float) over all groups
 };
-// Fills the two jobs for partials of hpw query heads each; returns the partials
-// per group, H / Hkv / hpw.
-inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+// Fills the two jobs for upg partials per group; returns upg.
+inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int upg,
                            ReduceJob j[2])
 {
     const int64_t groups = (int64_t)d.Hkv * d.B;
@@ -227,11 +247,11 @@ inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *d
         j[t].vec = (j[t].chunk % 4 == 0);
         j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;
     }
-    return d.H / d.Hkv / hpw;
+    return upg;
 }
 
 // The reduction above, one launch.
-hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int hpw,
+hipError_t launch_gqa_reduce(const float *pk, float *dk, const float *pv, float *dv, const Dims &d, int upg,
                              hipStream_t s);
 
 // Records the detail of an error for fab_last_error (thread-local) and returns code.

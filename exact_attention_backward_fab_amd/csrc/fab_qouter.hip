@@ -909,7 +909,7 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
 }
 
 hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t *map, float scale, float *dq, int Np,
-                             int Mp, const float *pk, float *dk, const float *pv, float *dv, int hpw, const Dims &d,
+                             int Mp, const float *pk, float *dk, const float *pv, float *dv, int upg, const Dims &d,
                              hipStream_t s)
 {
     HeadDims hd;
@@ -921,7 +921,7 @@ hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t 
     a.causal = d.causal;
     a.scale = scale;
     if (pk) {
-        a.rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, hpw, a.red);
+        a.rk2 = gqa_reduce_jobs(pk, dk, pv, dv, d, upg, a.red);
     } else {
         a.rk2 = 1;
         a.red[0] = a.red[1] = ReduceJob{nullptr, nullptr, 0, 0, 0};

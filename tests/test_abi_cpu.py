@@ -85,8 +85,14 @@ def test_workspace_grows_with_what_must_be_recomputed():
     # f32: the internal O and LSE need room
     assert fab.workspace_bytes(s, "bf16", False, False) == base
     assert fab.workspace_bytes(s, "f32", False, False) > fab.workspace_bytes(s, "f32", False, True)
-    mha = fab.Shape(1, 8, 8, 300, 400, 64, 64)
-    assert fab.workspace_bytes(mha, "bf16", False, True) < base  # no grouped-query partials
+    # with a grid of at least one dK/dV work-group per CU: partials only for grouped-query
+    # heads; on smaller grids the query splits of the dK/dV kernel have partials too
+    big = fab.Shape(1, 8, 2, 300, 4096, 64, 64)
+    big_mha = fab.Shape(1, 8, 8, 300, 4096, 64, 64)
+    assert fab.workspace_bytes(big_mha, "bf16", False, True) < fab.workspace_bytes(big, "bf16", False, True)
+    small_mha = fab.Shape(1, 8, 8, 300, 400, 64, 64)
+    partials = 2 * 4 * 64 * 400 * 8 * 4   # dK and dV, f32, 4 query splits of 8 heads
+    assert fab.workspace_bytes(small_mha, "bf16", False, True) >= partials
 
 
 FAKE = 1 << 20   # a 256-byte aligned address that is never dereferenced: every call below fails validation
