@@ -256,20 +256,21 @@ __global__ __launch_bounds__(256) void pack_qkv_kernel(PackJobs a)
 }
 
 // The pack (Q, K, V, block map) and the prep of a supplied O and LSE (dO tiles,
-// LSE/D blocks, blob pads, counters) in one launch: work-groups [0, npack) pack,
-// the rest prep.
+// LSE/D blocks, blob pads, counters) in one launch: the prep tiles (two input rows
+// each, the heavier work-groups) first, then the pack.
 template <int DKP, int DVP>
-__global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, int npack, PackJob j, PrepExtra x)
+__global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, PackJob j, PrepExtra x)
 {
     for (int i = blockIdx.x * 256 + threadIdx.x; i < x.nzero; i += gridDim.x * 256) x.zero[i] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 4)
         for (int k = 0; k < 3; ++k)
             if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) x.blob[x.pad_lo[k] + threadIdx.x] = 0.f;
     int bt = blockIdx.x;
-    if (bt >= npack) {
-        pack_tile<DVP>(j, bt - npack, &x);
+    if (bt < j.tiles) {
+        pack_tile<DVP>(j, bt, &x);
         return;
     }
+    bt -= j.tiles;
     if (bt < a.map_groups) {
         block_map_strip(a.mask, a.map, a.N, a.M, a.nqb, a.nkb, bt);
         return;
@@ -358,7 +359,7 @@ hipError_t run_pack_prep(const PackPrep &p, hipStream_t s)
 {
     const int64_t grid = (int64_t)p.npack + p.j.tiles;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((pack_prep_kernel<DKP, DVP>), dim3((unsigned)grid), dim3(256), 0, s, p.a, p.npack, p.j, p.x);
+    hipLaunchKernelGGL((pack_prep_kernel<DKP, DVP>), dim3((unsigned)grid), dim3(256), 0, s, p.a, p.j, p.x);
     return hipGetLastError();
 }
 }  // namespace
