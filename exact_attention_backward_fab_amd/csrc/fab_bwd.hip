@@ -403,24 +403,30 @@ constexpr int kKW4 = 4, kKNT4 = 64 * kKW4;
 
 
 // LDS stages of the 4-wave kernel: the Q tile, the dO tile and the LSE/D block of
-// one step each.
-template <int DKP, int DVP>
+// one step each, and with MS the step's mask rows (64 queries x the block's 128
+// keys, f16, 256-byte rows).
+template <int DKP, int DVP, bool MS = false>
 struct KStages4 {
     static constexpr int kQ = DKP / 8 * kChunkL, kO = DVP / 8 * kChunkL, kS = kStatsTile * 4;
-    static constexpr int kBytes = kQ + kO + kS;
+    static constexpr int kM = MS ? kTR * kKBC * 2 : 0;
+    static constexpr int kBytes = kQ + kO + kS + kM;
     static constexpr int kFit = (160 * 1024 - 4 * kKList - 256) / kBytes;
     static constexpr int N = kFit > 4 ? 4 : kFit;
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-template <int DKP, int DVP, bool AB>
+// MS: the mask rows of every step are copied into the LDS stage with the Q and dO
+// tiles (mask given, M % 8 == 0), so a MIXED step reads its mask from LDS instead of
+// waiting on 32 global loads with nothing else in flight (one wave per SIMD).
+template <int DKP, int DVP, bool AB, bool MS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_w4_kernel(KvArgs p)
 {
-    using ST = KStages4<DKP, DVP>;
+    using ST = KStages4<DKP, DVP, MS>;
     constexpr int NS = ST::N;
     constexpr int QCH = DKP / 8 / kKW4, OCH = DVP / 8 / kKW4;   // chunk columns copied per wave
     static_assert(QCH * 8 * kKW4 == DKP && OCH * 8 * kKW4 == DVP, "tile copy split");
-    constexpr int PER = QCH + OCH + 1;                         // copies per wave and step
+    constexpr int MCH = MS ? kTR * kKBC * 2 / 1024 / kKW4 : 0;   // 1 KiB mask copies per wave (4 rows each)
+    constexpr int PER = QCH + OCH + 1 + MCH;                     // copies per wave and step
     __shared__ __attribute__((aligned(16))) char sQO[NS * ST::kBytes];
     __shared__ int sList[kKList];
     __shared__ int sCount[kKW4 + 1];
@@ -493,6 +499,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (lane < 8)
             lds_copy16(rs, stg + ST::kQ + ST::kO + w * 128,
                        (uint32_t)(it * kStatsTile * 4 + w * 128) + (uint32_t)lane * 16u);
+        if constexpr (MS) {
+            // mask rows it*64 + 4c + lane/16, bytes 16 (lane%16).. of keys key0..key0+127;
+            // rows past N read as zero (buffer bounds)
+#pragma unroll
+            for (int i = 0; i < MCH; ++i) {
+                const int c = i * kKW4 + w, row = it * kKBR + 4 * c + (lane >> 4);
+                lds_copy16(rmask, stg + ST::kQ + ST::kO + ST::kS + c * 1024,
+                           2u * ((uint32_t)row * (uint32_t)p.M + (uint32_t)key0) + (uint32_t)(lane & 15) * 16u);
+            }
+        }
     };
 
     const int nqt = p.Np / kKBR;
@@ -567,8 +583,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                 }
                 if (cls == kTileMixed) {
+                    if constexpr (MS) {
+                        // this lane's key column of the step's mask rows in LDS
+                        const _Float16 *mcol = reinterpret_cast<const _Float16 *>(Sb + 128) + 32 * w + l32;
 #pragma unroll
-                    for (int qq = 0; qq < 2; ++qq) add_mask_column(sacc[qq], rmask, mykey, q0 + 32 * qq, half, p.N, p.M);
+                        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                sacc[qq][r] += (float)mcol[(32 * qq + crow(r, half)) * kKBC] * kLog2e;
+                    } else {
+#pragma unroll
+                        for (int qq = 0; qq < 2; ++qq)
+                            add_mask_column(sacc[qq], rmask, mykey, q0 + 32 * qq, half, p.N, p.M);
+                    }
                 }
             }
 #pragma unroll
@@ -993,10 +1020,15 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
         return hipGetLastError();
     } else {
         const dim3 grid(ceil_div(a.M, kKBC) * a.H * a.B);
-        if (a.alibi)
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true>), grid, dim3(kKNT4), 0, s, a);
+        const bool ms = a.mask && a.M % 8 == 0;   // mask rows staged in LDS (16-byte aligned rows)
+        if (a.alibi && ms)
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, true>), grid, dim3(kKNT4), 0, s, a);
+        else if (a.alibi)
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, false>), grid, dim3(kKNT4), 0, s, a);
+        else if (ms)
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, true>), grid, dim3(kKNT4), 0, s, a);
         else
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false>), grid, dim3(kKNT4), 0, s, a);
+            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, false>), grid, dim3(kKNT4), 0, s, a);
         return hipGetLastError();
     }
 }

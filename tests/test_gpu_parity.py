@@ -128,13 +128,15 @@ SMALL = [
     ("d192_128_padding", Shape(1, 2, 2, 130, 260, 192, 128), "padding", 44),
     ("d40_72_nomask", Shape(1, 3, 1, 70, 90, 40, 72), None, 45),
     ("d192_192_random", Shape(1, 2, 1, 65, 97, 192, 192), "random", 46),
+    # M % 8 == 0: the 4-wave kernel copies each step's mask rows into LDS (rows past
+    # N=100 read as zero, the last key block runs past M)
+    ("d192_128_random_staged_mask", Shape(1, 2, 2, 100, 264, 192, 128), "random", 50),
     ("one_key", Shape(1, 2, 1, 17, 1, 16, 16), None, 47),
     ("one_query", Shape(1, 2, 2, 1, 130, 64, 64), "random", 48),
     ("workload1", fi.WORKLOADS[1].shape, None, 1),
-    # head dims 192 take dQ from the recompute kernel: 16 x 33 = 528 query blocks of
-    # 128 is above its two-share split's limit (512), so it runs one work-group per
-    # block (the other 192-wide cases here are split)
-    ("dq_unsplit_528_blocks", Shape(1, 33, 3, 2000, 200, 192, 128), "causal", 49),
+    # 192-wide heads with many (batch, head, query-step) blocks: the 4-wave dK/dV
+    # kernel (mask rows staged in LDS, M % 8 == 0) and dQ from its stored dS
+    ("d192_528_query_blocks", Shape(1, 33, 3, 2000, 200, 192, 128), "causal", 49),
     # 16 key blocks x 64 (batch, head) pairs = 1024 work-groups: the bf16 dK/dV kernel
     # takes two query heads of a group per work-group; with 2 heads per group a unit is
     # the whole group (dK/dV straight into the result), with 4 two partials per group
