@@ -41,10 +41,14 @@ constexpr int kQList = 512;   // live key steps listed at a time
 // per CU: two work-groups (two waves per SIMD, so that one wave's softmax
 // arithmetic overlaps the other's matrix-core work) when two stages of each fit
 // in half of the 160 KiB, else one; then as many stages as fit, at most 4.
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool MS = false>
 struct QStages {
     static constexpr int kK = DKP / 8 * kChunkL;            // bytes of a K tile in LDS
-    static constexpr int kBytes = (DKP + DVP) / 8 * kChunkL;
+    static constexpr int kKV = (DKP + DVP) / 8 * kChunkL;   // ... and of the K and V tiles
+    // with MS the step's mask rows (128 queries x 64 keys, f16) follow, chunk-major:
+    // the 16-byte chunk c (keys 8c..8c+7) of row r at byte (c * 128 + r) * 16
+    static constexpr int kM = MS ? kQBQ * kQBK * 2 : 0;
+    static constexpr int kBytes = kKV + kM;
     static constexpr int kFixed = 4 * kQList + 256;
     static constexpr int Occ = (2 * kBytes + kFixed <= 80 * 1024) ? 2 : 1;
     static constexpr int kFit = (160 * 1024 / Occ - kFixed) / kBytes;
@@ -95,16 +99,23 @@ __device__ __forceinline__ QShare query_share(int bid, int HB, int split)
 // sKV is the stage array and kv_lds its LDS byte address.
 // With stride > 1 the work-group takes only the live steps at list positions
 // off, off + stride, ... (one share of a query block split over work-groups).
+// With ST::kM (mask rows staged) every step also copies the mask rows of the
+// work-group's queries q0.. at the step's 64 keys into the stage (mask [N][M],
+// M % 8 == 0; rows past N read as zero), and body receives their LDS address.
 template <int DKP, int DVP, int W = kQW, typename ST = QStages<DKP, DVP>, typename ClassOf, typename Body>
 __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const char *sKV, uint32_t kv_lds, int *sList,
                                                  int *sCount, int nks, int tid, int lane, int w, ClassOf class_of,
-                                                 Body body, int off = 0, int stride = 1)
+                                                 Body body, int off = 0, int stride = 1,
+                                                 const uint16_t *mask = nullptr, int N = 0, int q0 = 0, int M = 0)
 {
     constexpr int NS = ST::N;
     // chunk columns copied per wave; when a tile has fewer columns than waves, the
     // surplus copies repeat a column (same bytes to the same place) so that every
     // wave issues the same number of copies per step (its vmcnt waits count on it)
     constexpr int KCH = (DKP / 8 + W - 1) / W, VCH = (DVP / 8 + W - 1) / W;
+    constexpr int MCH = ST::kM / 1024 / W;   // 1 KiB mask copies per wave: 64 rows of one chunk each
+    static_assert(MCH * 1024 * W == ST::kM, "mask copy split");
+    const rsrc_t rm = mask_rsrc(MCH ? mask : nullptr, N, M);
     auto issue = [&](int s, int bf) {
         const uint32_t stg = kv_lds + (uint32_t)(bf * ST::kBytes);   // wave-uniform LDS byte address
 #pragma unroll
@@ -117,6 +128,13 @@ __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const cha
             const int c = (i * W + w) % (DVP / 8);
             lds_copy16(rv, stg + ST::kK + c * kChunkL, (uint32_t)(s * DVP / 8 + c) * kChunkG + (uint32_t)lane * 16u);
         }
+#pragma unroll
+        for (int i = 0; i < MCH; ++i) {
+            // copy x: chunk x / 2 of rows 64 (x % 2) + lane
+            const int x = i * W + w, c = x >> 1, r = 64 * (x & 1) + lane;
+            lds_copy16(rm, stg + ST::kKV + (uint32_t)(c * 128 + 64 * (x & 1)) * 16u,
+                       2u * ((uint32_t)(q0 + r) * (uint32_t)M + (uint32_t)(s * kQBK)) + (uint32_t)c * 16u);
+        }
     };
     for (int seg = 0; seg < nks; seg += kQList) {
         const int live = build_live_list<W>(sList, sCount, seg, min(seg + kQList, nks), tid, lane, w, class_of);
@@ -127,12 +145,12 @@ __device__ __forceinline__ void stream_key_steps(rsrc_t rk, rsrc_t rv, const cha
         for (int i = 0; i < NS - 1; ++i)
             if (i < count) issue(list[stride * i] >> 2, i);
         for (int li = 0; li < count; ++li) {
-            wait_vm_steps<KCH + VCH>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
-            __syncthreads();                                          // ... for every wave; stage li-1 is free
+            wait_vm_steps<KCH + VCH + MCH>(min(count - 1 - li, NS - 2));   // step li has landed (this wave)
+            __syncthreads();                                                // ... for every wave; stage li-1 is free
             if (li + NS - 1 < count) issue(list[stride * (li + NS - 1)] >> 2, (li + NS - 1) % NS);
             const int e = list[stride * li];
             const char *stg = sKV + (li % NS) * ST::kBytes;
-            body(e >> 2, e & 3, stg, stg + ST::kK);
+            body(e >> 2, e & 3, stg, stg + ST::kK, stg + ST::kKV);
         }
         __syncthreads();   // every wave is done with the stages before they are refilled
     }
@@ -222,9 +240,12 @@ __device__ __forceinline__ void tr_products(f32x16 *acc, const bf16x8 *a4, const
 // bias slope2 (key - myq) is added; MIXED steps add the mask row of the query.  A
 // lane's keys come in runs of 4 (slots 4j..4j+3), read as one 8-byte load when
 // vecM (M % 4 == 0).
+// With mst (mask rows staged in LDS by stream_key_steps), the mask of row mrl of the
+// stage is read from there instead of from mrow.
 template <int NT, bool AB = false>
 __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bool mixed, const uint16_t *mrow, int M,
-                                               bool vecM, float sl2, int half, float slope2 = 0.f, int myq = 0)
+                                               bool vecM, float sl2, int half, float slope2 = 0.f, int myq = 0,
+                                               const char *mst = nullptr, int mrl = 0)
 {
 #pragma unroll
     for (int kk = 0; kk < NT; ++kk)
@@ -240,7 +261,19 @@ __device__ __forceinline__ void scale_and_mask(f32x16 *st, int key0, int lim, bo
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[kk][r] += __builtin_fmaf(slope2, (float)(kk * 32 + crow(r, half)), ab);
     }
-    if (mixed) {
+    if (mixed && mst) {
+#pragma unroll
+        for (int kk = 0; kk < NT; ++kk)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                // keys kk*32 + 8 r4 + 4 half.. of the step: chunk 4 kk + r4, bytes 8 half..
+                const uint2 x = *reinterpret_cast<const uint2 *>(mst + ((4 * kk + r4) * 128 + mrl) * 16 + 8 * half);
+                const uint16_t m4[4] = {(uint16_t)(x.x & 0xFFFFu), (uint16_t)(x.x >> 16), (uint16_t)(x.y & 0xFFFFu),
+                                        (uint16_t)(x.y >> 16)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[kk][4 * r4 + i] += half_bits_to_float(m4[i]) * kLog2e;
+            }
+    } else if (mixed) {
         uint16_t m[NT][16];
 #pragma unroll
         for (int kk = 0; kk < NT; ++kk)
@@ -293,11 +326,16 @@ struct FwdArgs16 {
     int fold;                       // the whole grid is resident at once (query_block_work)
 };
 
-template <int DKP, int DVP, bool PREP, bool AB>
-__global__ __launch_bounds__(256, (QStages<DKP, DVP>::Occ))
-__attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
+// MS: the mask rows of every key step are staged in LDS with its K and V tiles
+// (a mask is given and M % 8 == 0).  Used where one work-group fills a CU (the
+// 192-wide heads): there the MIXED steps would otherwise wait on their own mask
+// loads with no other work-group's products to hide them.
+template <int DKP, int DVP, bool PREP, bool AB, bool MS = false>
+__global__ __launch_bounds__(256, (QStages<DKP, DVP, MS>::Occ))
+__attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP, MS>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
 {
-    __shared__ __attribute__((aligned(16))) char sKV[QStages<DKP, DVP>::N * QStages<DKP, DVP>::kBytes];
+    using ST = QStages<DKP, DVP, MS>;
+    __shared__ __attribute__((aligned(16))) char sKV[ST::N * ST::kBytes];
     __shared__ int sList[kQList];
     __shared__ int sCount[kQW + 1];
 
@@ -340,13 +378,13 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const uint16_t *mrow = p.mask + (size_t)p.M * min(myq, p.N - 1);
 
-    stream_key_steps<DKP, DVP>(
+    stream_key_steps<DKP, DVP, kQW, ST>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
             return tile_class<kQBQ / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
                               s * (kQBK / kMapTile));
         },
-        [&](int s, int cls, const char *Kb, const char *Vb) {
+        [&](int s, int cls, const char *Kb, const char *Vb, const char *Mb) {
             const int key0 = s * kQBK;
             f32x16 st[2];
             st_pt_pair<DKP, DVP, false>(Kb, qf, nullptr, nullptr, row_off, st, nullptr);
@@ -356,7 +394,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f && (!AB || slope2 == 0.f))) {
                 const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
                 scale_and_mask<2, AB>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half, slope2,
-                                  myq);
+                                  myq, MS ? Mb : nullptr, 32 * w + l32);
                 mul = 1.f;
             }
 
@@ -405,7 +443,8 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
                     pb4[2 * kk + u] = to_bf16x8(pv);
                 }
             tr_products<DVP / 32, true>(oacc, pb4, Vb, tr_off);
-        });
+        },
+        0, 1, p.mask, p.N, q0, p.M);
 
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
     const float l = swap_halves_sum(l_part);
@@ -550,7 +589,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
             return tile_class<kQBQ / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
                               s * (kQBK / kMapTile));
         },
-        [&](int s, int cls, const char *Kb, const char *Vb) {
+        [&](int s, int cls, const char *Kb, const char *Vb, const char *) {
             const int key0 = s * kQBK;
             // ---- S^T = K Q^T and dP^T = V dO^T for two 32-key sub-tiles (lane = query)
             f32x16 st[2], pt[2];
@@ -824,6 +863,19 @@ hipError_t run_dq(const DqArgs &a, hipStream_t s)
     }
 }
 
+// One forward variant (PREP: the backward's own forward; MS: mask rows staged in
+// LDS), ALiBi or not; the ALiBi instantiation shares the plain one's occupancy query.
+template <int DKP, int DVP, bool PREP, bool MS>
+void launch_fwd16_variant(FwdArgs16 b, int grid, hipStream_t s)
+{
+    static ResidentCache slots;
+    b.fold = grid <= slots.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, PREP, false, MS>), kQNT);
+    if (b.alibi)
+        hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, PREP, true, MS>), dim3(grid), dim3(kQNT), 0, s, b);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, PREP, false, MS>), dim3(grid), dim3(kQNT), 0, s, b);
+}
+
 template <int DKP, int DVP, bool BF16>
 hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
 {
@@ -831,23 +883,19 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         const int grid = ceil_div(a.N, kQBQ) * a.H * a.B;
-        static ResidentCache slots_prep, slots_fwd;
-        FwdArgs16 b = a;
-        // (the ALiBi instantiations share the plain ones' occupancy query)
-        if (a.dO) {
-            b.fold = grid <= slots_prep.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, true, false>),
-                                            kQNT);
-            if (a.alibi)
-                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true, true>), dim3(grid), dim3(kQNT), 0, s, b);
-            else
-                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, true, false>), dim3(grid), dim3(kQNT), 0, s, b);
+        bool ms = false;   // stage the mask rows: one work-group per CU, rows of whole 16-byte chunks
+        if constexpr (QStages<DKP, DVP>::Occ == 1) ms = a.mask && a.M % 8 == 0;
+        if (ms) {
+            if constexpr (QStages<DKP, DVP>::Occ == 1) {
+                if (a.dO)
+                    launch_fwd16_variant<DKP, DVP, true, true>(a, grid, s);
+                else
+                    launch_fwd16_variant<DKP, DVP, false, true>(a, grid, s);
+            }
+        } else if (a.dO) {
+            launch_fwd16_variant<DKP, DVP, true, false>(a, grid, s);
         } else {
-            b.fold = grid <= slots_fwd.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, false, false>),
-                                           kQNT);
-            if (a.alibi)
-                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false, true>), dim3(grid), dim3(kQNT), 0, s, b);
-            else
-                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, false, false>), dim3(grid), dim3(kQNT), 0, s, b);
+            launch_fwd16_variant<DKP, DVP, false, false>(a, grid, s);
         }
         return hipGetLastError();
     }
