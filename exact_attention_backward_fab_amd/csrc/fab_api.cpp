@@ -147,7 +147,8 @@ void plan_workspace(Plan *pl, int mode, int has_mask, int have_o_lse)
         off = align_up(off + sizeof(float) * qrows / 64 * 128);
     }
     pl->ds = mode == FAB_MODE_BF16 && fab::dq_from_ds(d, pl->np, pl->dkp, pl->dvp);
-    pl->upg = mode == FAB_MODE_BF16 ? fab::bwd_units_per_group(d, pl->dkp, pl->dvp) : d.H / d.Hkv;
+    pl->upg = mode == FAB_MODE_BF16 ? fab::bwd_units_per_group(d, pl->dkp, pl->dvp)
+                                    : fab::f32_units_per_group(d, pl->dkp, pl->dvp);
     pl->part = pl->upg > 1;
     pl->ws_dqp = off;
     pl->ws_tick = off;

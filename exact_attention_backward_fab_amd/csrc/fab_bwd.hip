@@ -40,6 +40,7 @@ struct BwdArgs {
     float *dq, *dk, *dv;
     int B, H, Hkv, N, M, DK, DV;
     int part_heads, nqb, nkb, vecK, vecV;
+    int qsplit;                     // work-groups per (key block, query head) on interleaved live query steps
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
     const float *alibi;             // per-head ALiBi slopes [H] or NULL
@@ -703,6 +704,7 @@ struct F32Cfg {
     static constexpr int W = KW * QH;
     static constexpr int NT = 64 * W;
     static constexpr int BC = 32 * KW;  // keys per work-group
+    static_assert(BC == f32_keys_per_wg(DKP, DVP), "f32 key block");
     static constexpr int BR = 32 * QH;  // queries per step
     static constexpr int LK = DKP + 4, LV = DVP + 4, LQ = DKP + 4, LO = DVP + 4, LS = BC + 4;
 };
@@ -723,8 +725,9 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
     const int kw = QH == 1 ? w : w % KW, qq = QH == 1 ? 0 : w / KW;   // key sub-block, query half
-    const int HB = p.H * p.B;
-    const int j = blockIdx.x / HB, hb = blockIdx.x % HB;
+    const int HB = p.H * p.B, qs = p.qsplit;
+    const int split = blockIdx.x % qs, jhb = blockIdx.x / qs;   // this work-group takes live steps split, split + qs, ...
+    const int j = jhb / HB, hb = jhb % HB;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int key0 = j * BC;
     const int mykey = key0 + 32 * kw + l32;
@@ -798,14 +801,20 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             pd = Dl;
         }
     };
+    // this work-group's live steps: every qs-th, from the split-th on
+    auto next_mine = [&](int from, int *c, int skip) {
+        int i = next_live(from, c);
+        for (int k = 0; k < skip && i < nqt; ++k) i = next_live(i + 1, c);
+        return i;
+    };
     int cls = kTileSkip;
-    int it = next_live(0, &cls);
+    int it = next_mine(0, &cls, split);
     if constexpr (PF)
         if (it < nqt) fetch(it);
     while (it < nqt) {
         const int q0 = it * BR;
         int ncls = kTileSkip;
-        const int nx = next_live(it + 1, &ncls);
+        const int nx = next_mine(it + 1, &ncls, qs - 1);
         __syncthreads();  // the previous step is done with sQ, sO, sS
         if constexpr (PF) {
 #pragma unroll
@@ -960,7 +969,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             for (int r = 0; r < 16; ++r) dvacc[dt][r] += xv[(dt * 16 + r) * 64 + lane];
     }
 
-    const int hd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
+    const int hd = p.part_heads ? h * qs + split : g, Hd = p.part_heads ? p.H * qs : p.Hkv;
     float *dkb = p.dk + (size_t)p.DK * p.M * (hd + Hd * b);
     float *dvb = p.dv + (size_t)p.DV * p.M * (hd + Hd * b);
 #pragma unroll
@@ -997,11 +1006,11 @@ hipError_t run_bwd_f32(const BwdArgs &a, hipStream_t s)
     } else {
         using C = F32Cfg<DKP, DVP>;
         if (a.alibi)
-            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, true>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
-                               0, s, a);
+            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, true>), dim3(ceil_div(a.M, C::BC) * a.H * a.B * a.qsplit),
+                               dim3(C::NT), 0, s, a);
         else
-            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, false>), dim3(ceil_div(a.M, C::BC) * a.H * a.B), dim3(C::NT),
-                               0, s, a);
+            hipLaunchKernelGGL((bwd_f32_kernel<DKP, DVP, false>), dim3(ceil_div(a.M, C::BC) * a.H * a.B * a.qsplit),
+                               dim3(C::NT), 0, s, a);
         return hipGetLastError();
     }
 }
@@ -1046,6 +1055,8 @@ hipError_t launch_backward_f32(const float *q, const float *k, const float *v, c
     a.lse = lse; a.delta = delta; a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.M = d.M; a.DK = d.DK; a.DV = d.DV;
     a.part_heads = part_heads;
+    a.qsplit = f32_query_splits(d, hd.dk, hd.dv);
+    if (a.qsplit > 1 && !part_heads) return hipErrorInvalidValue;   // the splits' partials need the reduction
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0);
     a.scale = scale;

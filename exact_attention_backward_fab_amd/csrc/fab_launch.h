@@ -127,9 +127,29 @@ constexpr int kPackRows = 64;
 hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *q16, __bf16 *k16, __bf16 *v16,
                            const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s);
 
-// Key-block-outer backward, f32 mode: dV, dK per key tile (stored into dk/dv with
-// per-query-head layout when part_heads != 0) and dQ by f32 atomics into dq
-// (zeroed beforehand).
+// f32-mode dK/dV kernel: keys per work-group (32 per key sub-block of waves: 4
+// sub-blocks for head-dim pairs up to 64 + 64, else 2).
+constexpr int f32_keys_per_wg(int dkp, int dvp) { return 32 * (dkp + dvp <= 128 ? 4 : 2); }
+
+// Query splits of the f32 dK/dV kernel: below one work-group per CU (256 CUs), each
+// (key block, query head) is run by 2 or 4 work-groups that take interleaved live
+// query steps, each with its own dK/dV partial.
+inline int f32_query_splits(const Dims &d, int dkp, int dvp)
+{
+    const int64_t wgs = (int64_t)((d.M + f32_keys_per_wg(dkp, dvp) - 1) / f32_keys_per_wg(dkp, dvp)) * d.H * d.B;
+    int qs = 1;
+    while (qs < 4 && wgs * qs < 256) qs *= 2;
+    return qs;
+}
+
+// dK/dV partials per key/value head of the f32 dK/dV kernel: query heads of the
+// group times query splits; 1 = no partials (the kernel writes the result).
+inline int f32_units_per_group(const Dims &d, int dkp, int dvp) { return d.H / d.Hkv * f32_query_splits(d, dkp, dvp); }
+
+// Key-block-outer backward, f32 mode: dV, dK per key tile and dQ by f32 atomics into
+// dq (zeroed beforehand).  With part_heads (f32_units_per_group > 1), one partial per
+// unit (query head x query split) into dk/dv [D,M,Hkv*upg,B]; else into dk/dv
+// [D,M,Hkv,B].
 hipError_t launch_backward_f32(const float *q, const float *k, const float *v, const float *dO,
                                const uint16_t *mask, const uint8_t *map, const float *lse, const float *delta,
                                float scale, float *dq, float *dk, float *dv, int part_heads, const Dims &d,

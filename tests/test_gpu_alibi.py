@@ -114,7 +114,12 @@ def test_alibi_causal_flag_equals_causal_mask(mode):
     a = fab.backward(*t, 0.125, mode=mode, causal=True, alibi=ta)
     b = fab.backward(*t, 0.125, mask=tm, mode=mode, alibi=ta)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if mode == "bf16":
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    else:   # the dQ atomics of f32 mode add in any order; dK and dV are summed in a fixed one
+        off_k = fab.blob_layout(fab.Shape(*s.astuple()))[1]
+        assert float((a[:off_k] - b[:off_k]).abs().max()) <= 1e-6 * float(b[:off_k].abs().max())
+        assert torch.equal(a[off_k:].view(torch.int32), b[off_k:].view(torch.int32))
 
 
 @pytest.mark.parametrize("mode", ["f32", "bf16"])

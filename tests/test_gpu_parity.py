@@ -274,6 +274,7 @@ CAUSAL_FLAG = [
 def test_causal_flag_equals_causal_mask(torch_dev, name, s, seed, mode):
     # FAB_CAUSAL (no mask tensor, no block map) against the oracle on the explicit
     # 0 / -inf causal mask, and bit for bit against the library's own masked path
+    # (f32 mode: dK and dV bit for bit, dQ up to the order of its atomics)
     torch, dev = torch_dev
     fab = fabmod()
     print(f"[parity] causal flag {name} {mode} {s}", flush=True)
@@ -288,7 +289,13 @@ def test_causal_flag_equals_causal_mask(torch_dev, name, s, seed, mode):
     flag = flag[:fab.blob_layout(fab.Shape(*s.astuple()))[3]].cpu().numpy()
     ref = oracle_full(s, q, k, v, d, mask, scale)
     check_blob(s, flag, ref, mode, tag=f"causal flag {name}/{mode}", mask=mask)
-    assert np.array_equal(flag.view(np.uint32), masked[:flag.size].cpu().numpy().view(np.uint32))
+    masked = masked[:flag.size].cpu().numpy()
+    if mode == "bf16":
+        assert np.array_equal(flag.view(np.uint32), masked.view(np.uint32))
+    else:   # f32 mode: dQ is summed by atomics in any order, dK and dV in a fixed one
+        off_k = fab.blob_layout(fab.Shape(*s.astuple()))[1]
+        assert np.abs(flag[:off_k] - masked[:off_k]).max() <= 1e-6 * np.abs(masked[:off_k]).max()
+        assert np.array_equal(flag[off_k:].view(np.uint32), masked[off_k:].view(np.uint32))
     from oracle import oracle as orc
     O_ref, _ = orc.forward(s, q, k, v, mask, scale)
     assert rel_err(O.cpu().numpy(), O_ref) <= TOL[mode]
