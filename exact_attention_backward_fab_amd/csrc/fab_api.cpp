@@ -28,7 +28,7 @@ int fail(int code, const char *fmt, ...)
 }
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
-constexpr int kMaxHeadDim = 192;
+constexpr int kMaxHeadDim = 256;
 constexpr size_t kWsAlign = 256;
 
 int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }

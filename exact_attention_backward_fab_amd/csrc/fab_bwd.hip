@@ -399,8 +399,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // 4-wave variant for the large head dims (K and V rows of the block in registers,
 // one wave per SIMD): wave w owns keys 32w.. of the block and both 32-query halves
-// of every step.
+// of every step.  For the 256-wide heads the dK/dV columns are split over two
+// work-groups per (key block, head) (kW4ColSplit): each forms the whole S and dP
+// but accumulates half of the dK and dV columns, so that the accumulators fit the
+// registers beside the K and V rows.
 constexpr int kKW4 = 4, kKNT4 = 64 * kKW4;
+template <int DKP, int DVP>
+constexpr int kW4ColSplit = DKP + DVP > 384 ? 2 : 1;
 
 
 // LDS stages of the 4-wave kernel: the Q tile, the dO tile and the LSE/D block of
@@ -437,17 +442,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t qo_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sQO;
 
-    // ---- work-group -> (key block, head): first key blocks first (under a causal
-    // mask they see the most queries); heads dealt to the XCDs in contiguous ranges
+    // ---- work-group -> (key block, head, column part): first key blocks first (under
+    // a causal mask they see the most queries); heads dealt to the XCDs in contiguous
+    // ranges
+    constexpr int CS = kW4ColSplit<DKP, DVP>;
+    constexpr int NVC = DVP / 32 / CS, NKC = DKP / 32 / CS;   // dV, dK column tiles of this work-group
+    const int cs = blockIdx.x % CS, bid = blockIdx.x / CS;
     const int HB = p.H * p.B;
     int kb, hb;
     if (HB % 8 == 0) {
-        const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8, per = HB / 8;
+        const int xcd = bid % 8, jj = bid / 8, per = HB / 8;
         kb = jj / per;
         hb = xcd * per + jj % per;
     } else {
-        kb = blockIdx.x / HB;
-        hb = blockIdx.x % HB;
+        kb = bid / HB;
+        hb = bid % HB;
     }
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
     const int key0 = kb * kKBC;
@@ -472,11 +481,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int t = 0; t < DVP / 16; ++t)
             vf[t] = in ? *reinterpret_cast<const bf16x8 *>(vh + tile_elem(mykey, 16 * t + 8 * half, DVP)) : z;
     }
-    f32x16 dkacc[DKP / 32], dvacc[DVP / 32];
+    f32x16 dkacc[NKC], dvacc[NVC];
 #pragma unroll
-    for (int i = 0; i < DKP / 32; ++i) dkacc[i] = zero16();
+    for (int i = 0; i < NKC; ++i) dkacc[i] = zero16();
 #pragma unroll
-    for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
+    for (int i = 0; i < NVC; ++i) dvacc[i] = zero16();
 
     const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // first tile row of this head
     const rsrc_t rq = make_rsrc(p.q16 + qhead * DKP, (uint32_t)(p.Np * DKP) * 2u);
@@ -631,7 +640,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const bf16x8 pa = to_bf16x8(pv), da = to_bf16x8(dv8);
                     pa4[2 * qq + u] = pa;
                     da4[2 * qq + u] = da;
-                    if (p.ds) {
+                    if (p.ds && cs == 0) {
                         // the dS^T operands of this step for dQ = scale dS K, in the tile
                         // layout and with the stores bwd_bf16_kernel uses
                         const uint32_t t = 2u * (uint32_t)(((((size_t)hb * ((nqt + 1) / 2) + (it >> 1)) * p.nkb128 + kb) * 4 +
@@ -642,8 +651,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             {
                 // the transposed operands of the four (half, u) groups' dV and dK products in
-                // one sequence, read R2 products ahead
-                constexpr int NV = DVP / 32, NK = DKP / 32, NC = NV + NK, NJ = 4 * NC, R2 = 4;
+                // one sequence (this work-group's column tiles), read R2 products ahead
+                constexpr int NV = NVC, NK = NKC, NC = NV + NK, NJ = 4 * NC, R2 = 4;
+                const char *Obc = Ob + tr_off + 4608 * NV * cs, *Qbc = Qb + tr_off + 4608 * NK * cs;
                 bf16x8 br[R2];
 #pragma unroll
                 for (int j = 0; j < NJ + R2; ++j) {
@@ -654,8 +664,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                     if (j < NJ) {
                         const int gq = j / NC, c = j % NC, qq = gq >> 1, u = gq & 1;
-                        br[j % R2] = c < NV ? lds_tr8(Ob + tr_off + 4608 * c + 512 * qq + 256 * u)
-                                            : lds_tr8(Qb + tr_off + 4608 * (c - NV) + 512 * qq + 256 * u);
+                        br[j % R2] = c < NV ? lds_tr8(Obc + 4608 * c + 512 * qq + 256 * u)
+                                            : lds_tr8(Qbc + 4608 * (c - NV) + 512 * qq + 256 * u);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -664,13 +674,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __syncthreads();   // every wave is done with the stages before they are refilled
     }
 
-    // ---- store dK (scaled) and dV of this key block
+    // ---- store dK (scaled) and dV of this key block (this work-group's columns)
     const int hdd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
     float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
     float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
 #pragma unroll
-    for (int dt = 0; dt < DKP / 32; ++dt) {
-        const int col = dt * 32 + l32;
+    for (int dt = 0; dt < NKC; ++dt) {
+        const int col = (NKC * cs + dt) * 32 + l32;
         if (col < p.DK)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -679,8 +689,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
     }
 #pragma unroll
-    for (int dt = 0; dt < DVP / 32; ++dt) {
-        const int col = dt * 32 + l32;
+    for (int dt = 0; dt < NVC; ++dt) {
+        const int col = (NVC * cs + dt) * 32 + l32;
         if (col < p.DV)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -696,10 +706,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // A work-group has KW x QH waves: KW sub-blocks of 32 keys times QH halves of
 // 32 queries of each step (the query halves of one key sub-block add their dK,
 // dV through LDS at the end).  4 x 1 for the small head dims, 2 x 2 for
-// 128 / 128 (every SIMD busy; the LDS just fits), 2 x 1 for the 192-wide ones.
+// 128 / 128 (every SIMD busy; the LDS just fits), 2 x 1 for the 192-wide ones,
+// 1 x 1 for 256 / 256 (the K, V, Q and dO rows of one sub-block fill the LDS).
 template <int DKP, int DVP>
 struct F32Cfg {
-    static constexpr int KW = (DKP + DVP <= 128) ? 4 : 2;
+    static constexpr int KW = (DKP + DVP <= 128) ? 4 : (DKP + DVP <= 384) ? 2 : 1;
     static constexpr int QH = (DKP + DVP == 256) ? 2 : 1;
     static constexpr int W = KW * QH;
     static constexpr int NT = 64 * W;
@@ -1028,14 +1039,21 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
             hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, false>), grid, dim3(kKNT), 0, s, a);
         return hipGetLastError();
     } else {
-        const dim3 grid(ceil_div(a.M, kKBC) * a.H * a.B);
-        const bool ms = a.mask && a.M % 8 == 0;   // mask rows staged in LDS (16-byte aligned rows)
-        if (a.alibi && ms)
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, true>), grid, dim3(kKNT4), 0, s, a);
-        else if (a.alibi)
+        const dim3 grid(ceil_div(a.M, kKBC) * a.H * a.B * kW4ColSplit<DKP, DVP>);
+        // mask rows staged in LDS (16-byte aligned rows), where two stages with them fit
+        constexpr bool kMsFits = 2 * (KStages4<DKP, DVP>::kBytes + kTR * kKBC * 2) + 4 * kKList + 256 <= 160 * 1024;
+        const bool ms = kMsFits && a.mask && a.M % 8 == 0;
+        if constexpr (kMsFits) {
+            if (ms) {
+                if (a.alibi)
+                    hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, true>), grid, dim3(kKNT4), 0, s, a);
+                else
+                    hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, true>), grid, dim3(kKNT4), 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        if (a.alibi)
             hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, false>), grid, dim3(kKNT4), 0, s, a);
-        else if (ms)
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, true>), grid, dim3(kKNT4), 0, s, a);
         else
             hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, false>), grid, dim3(kKNT4), 0, s, a);
         return hipGetLastError();

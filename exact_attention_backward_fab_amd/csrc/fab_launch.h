@@ -26,7 +26,7 @@ struct Dims {
 struct HeadDims {
     int dk, dv;
 };
-constexpr HeadDims kHeadDims[] = {{32, 32}, {64, 64}, {128, 128}, {192, 128}, {192, 192}};
+constexpr HeadDims kHeadDims[] = {{32, 32}, {64, 64}, {128, 128}, {192, 128}, {192, 192}, {256, 256}};
 
 // Work-groups of one kernel (no dynamic LDS, `threads` per group) that the
 // current device holds resident at once: occupancy per CU times the CU count,
@@ -76,6 +76,8 @@ inline bool pick_head_dims(int DK, int DV, HeadDims *out)
             return (BF) ? FN<192, 128, true>(ARGS, STREAM) : FN<192, 128, false>(ARGS, STREAM);   \
         if ((HD).dk == 192 && (HD).dv == 192)                                                     \
             return (BF) ? FN<192, 192, true>(ARGS, STREAM) : FN<192, 192, false>(ARGS, STREAM);   \
+        if ((HD).dk == 256 && (HD).dv == 256)                                                     \
+            return (BF) ? FN<256, 256, true>(ARGS, STREAM) : FN<256, 256, false>(ARGS, STREAM);   \
         return hipErrorInvalidValue;                                                              \
     } while (0)
 
@@ -128,8 +130,8 @@ hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *
                            const uint16_t *mask, uint8_t *map, int Np, int Mp, const Dims &d, hipStream_t s);
 
 // f32-mode dK/dV kernel: keys per work-group (32 per key sub-block of waves: 4
-// sub-blocks for head-dim pairs up to 64 + 64, else 2).
-constexpr int f32_keys_per_wg(int dkp, int dvp) { return 32 * (dkp + dvp <= 128 ? 4 : 2); }
+// sub-blocks for head-dim pairs up to 64 + 64, 2 up to 192 + 192, else 1).
+constexpr int f32_keys_per_wg(int dkp, int dvp) { return 32 * (dkp + dvp <= 128 ? 4 : dkp + dvp <= 384 ? 2 : 1); }
 
 // Query splits of the f32 dK/dV kernel: below one work-group per CU (256 CUs), each
 // (key block, query head) is run by 2 or 4 work-groups that take interleaved live

@@ -883,10 +883,14 @@ hipError_t run_fwd16(const FwdArgs16 &a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         const int grid = ceil_div(a.N, kQBQ) * a.H * a.B;
-        bool ms = false;   // stage the mask rows: one work-group per CU, rows of whole 16-byte chunks
-        if constexpr (QStages<DKP, DVP>::Occ == 1) ms = a.mask && a.M % 8 == 0;
+        // stage the mask rows: one work-group per CU, rows of whole 16-byte chunks, two
+        // stages with the mask rows fit
+        constexpr bool kMs = QStages<DKP, DVP>::Occ == 1 &&
+                             2 * (QStages<DKP, DVP>::kKV + kQBQ * kQBK * 2) + QStages<DKP, DVP>::kFixed <= 160 * 1024;
+        bool ms = false;
+        if constexpr (kMs) ms = a.mask && a.M % 8 == 0;
         if (ms) {
-            if constexpr (QStages<DKP, DVP>::Occ == 1) {
+            if constexpr (kMs) {
                 if (a.dO)
                     launch_fwd16_variant<DKP, DVP, true, true>(a, grid, s);
                 else

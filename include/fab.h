@@ -64,7 +64,7 @@ extern "C" {
 #define FAB_VERSION 100  /* 1.0.0 */
 
 /* Problem extents.  B, N, M >= 0 (zero gives an empty problem); H, Hkv, DK,
- * DV >= 1; H % Hkv == 0; DK, DV <= 192; every tensor below 2^31 elements, and
+ * DV >= 1; H % Hkv == 0; DK, DV <= 256; every tensor below 2^31 elements, and
  * one head's rows (N or M, rounded up to 64) times its padded head dim below
  * 2^30 (FAB_E_UNSUPPORTED otherwise). */
 typedef struct fab_shape {
@@ -113,7 +113,7 @@ typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
 typedef enum fab_status {
     FAB_OK = 0,
     FAB_E_INVAL = -1,        /* bad shape, NULL pointer, bad scale or mode */
-    FAB_E_UNSUPPORTED = -2,  /* valid but outside what the kernels handle (DK/DV > 192, size) */
+    FAB_E_UNSUPPORTED = -2,  /* valid but outside what the kernels handle (DK/DV > 256, size) */
     FAB_E_WORKSPACE = -3,    /* workspace missing or smaller than fab_workspace_bytes() */
     FAB_E_ALIGN = -4,        /* a pointer is not 16-byte aligned (workspace: 256-byte) */
     FAB_E_HIP = -5           /* a HIP launch or runtime call failed */

@@ -114,7 +114,8 @@ GOOD = (1, 4, 2, 8, 8, 16, 16)
     ((1, 4, 2, -1, 8, 16, 16), {}, fab.FAB_E_INVAL),         # negative N
     ((1, 0, 1, 8, 8, 16, 16), {}, fab.FAB_E_INVAL),          # no heads
     ((1, 4, 2, 8, 8, 0, 16), {}, fab.FAB_E_INVAL),           # DK = 0
-    ((1, 4, 2, 8, 8, 256, 16), {}, fab.FAB_E_UNSUPPORTED),   # head dim above the kernels' range
+    ((1, 4, 2, 8, 8, 257, 16), {}, fab.FAB_E_UNSUPPORTED),   # head dim above the kernels' range (256)
+    ((1, 4, 2, 8, 8, 16, 257), {}, fab.FAB_E_UNSUPPORTED),
     ((1 << 20, 64, 64, 1024, 1024, 128, 128), {}, fab.FAB_E_UNSUPPORTED),  # beyond 2^31 elements
     ((1, 1, 1, 8, 5_700_000, 192, 32), {}, fab.FAB_E_UNSUPPORTED),  # one head's tiles beyond 2 GiB
     (GOOD, {"mode": 7}, fab.FAB_E_INVAL),

@@ -131,6 +131,12 @@ SMALL = [
     # M % 8 == 0: the 4-wave kernel copies each step's mask rows into LDS (rows past
     # N=100 read as zero, the last key block runs past M)
     ("d192_128_random_staged_mask", Shape(1, 2, 2, 100, 264, 192, 128), "random", 50),
+    # 256-wide heads (the pair 256 / 256): the 4-wave dK/dV kernel splits the dK/dV
+    # columns over two work-groups, each forming the whole S and dP; the f32 kernel
+    # runs one 32-key sub-block per work-group
+    ("d256_random_gqa", Shape(1, 4, 2, 100, 264, 256, 256), "random", 55),
+    ("d200_256_causal_batch", Shape(2, 2, 1, 130, 130, 200, 256), "causal", 56),
+    ("d64_256_padding", Shape(1, 2, 2, 70, 300, 64, 256), "padding", 57),
     ("one_key", Shape(1, 2, 1, 17, 1, 16, 16), None, 47),
     ("one_query", Shape(1, 2, 2, 1, 130, 64, 64), "random", 48),
     ("workload1", fi.WORKLOADS[1].shape, None, 1),
