@@ -14,8 +14,8 @@
 //
 // dQ = scale dS K: in bf16 mode this kernel stores the bf16 dS^T operands of
 // its dK product, and a query-outer kernel (fab_qouter.hip) forms dQ from them
-// as a plain product, writing each dQ row once (for the 192-wide heads and for
-// shapes whose dS would pass 4 GiB that kernel recomputes S and dP instead); in
+// as a plain product, writing each dQ row once (for shapes whose dS would pass
+// 4 GiB a query-outer kernel recomputes S and dP instead); in
 // f32 mode this kernel adds every key block's share with f32 atomics into the
 // result blob.
 //

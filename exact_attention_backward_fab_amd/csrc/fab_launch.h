@@ -189,7 +189,7 @@ inline int bwd_heads_per_wg(const Dims &d, int dkp, int dvp)
 // Query splits of the 8-wave dK/dV kernel (bf16 mode): on a grid smaller than one
 // work-group per CU, each (key block, head unit) is run by qs work-groups that take
 // interleaved live query steps, each writing its own dK/dV partial (summed with the
-// grouped-query reduction).  The 4-wave kernel of the 192-wide heads does not split.
+// grouped-query reduction).  The 4-wave kernel of the 192- and 256-wide heads does not split.
 inline int bwd_query_splits(const Dims &d, int dkp, int dvp)
 {
     if (dkp + dvp > 256) return 1;

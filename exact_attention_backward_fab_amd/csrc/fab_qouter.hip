@@ -13,7 +13,7 @@
 //                          query steps, each dQ element written once; the same
 //                          launch runs the grouped-query reduction of dK and dV
 //   dq_bf16_kernel         dQ = scale dS K by query blocks without stored dS (the
-//                          192-wide heads, and shapes whose dS would pass 4 GiB):
+//                          shapes whose dS would pass 4 GiB):
 //                          a work-group owns 128 queries of one (batch, head) and
 //                          streams the key blocks that see them (block map),
 //                          recomputing S^T = K Q^T and dP^T = V dO^T on the
@@ -327,9 +327,10 @@ struct FwdArgs16 {
 };
 
 // MS: the mask rows of every key step are staged in LDS with its K and V tiles
-// (a mask is given and M % 8 == 0).  Used where one work-group fills a CU (the
-// 192-wide heads): there the MIXED steps would otherwise wait on their own mask
-// loads with no other work-group's products to hide them.
+// (a mask is given and M % 8 == 0).  Used where one work-group fills a CU and two
+// stages with the mask rows fit (the 192-wide heads): there the MIXED steps would
+// otherwise wait on their own mask loads with no other work-group's products to
+// hide them.
 template <int DKP, int DVP, bool PREP, bool AB, bool MS = false>
 __global__ __launch_bounds__(256, (QStages<DKP, DVP, MS>::Occ))
 __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP, MS>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
