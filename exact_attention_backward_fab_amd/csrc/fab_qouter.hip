@@ -695,16 +695,21 @@ constexpr int kDsW = 8, kDsNT = 64 * kDsW;
 constexpr int kDsList = 512;       // live key blocks listed at a time
 
 // LDS stages: the two dS^T key tiles and the K tile of 64 keys.  Two stages and
-// two work-groups per CU (16 waves): measured on the N=2048 and N=8192 causal
-// workloads, a second resident work-group hides the copy latency better than
-// deeper staging in one (4 stages, one work-group: 70 / 381 us instead of 53 / 256).
+// two work-groups per CU (16 waves) where they fit: measured on the N=2048 and
+// N=8192 causal workloads, a second resident work-group hides the copy latency
+// better than deeper staging in one (4 stages, one work-group: 70 / 381 us instead
+// of 53 / 256).  Where only one work-group fits (the wide heads), as many stages as
+// the LDS holds, at most 4.
 template <int DKP>
 struct DsStages {
     static constexpr int kCols = 16 + DKP / 8;   // chunk columns: dS^T of step 0, of step 1, K
     static constexpr int kS = 8 * kChunkL;
     static constexpr int kBytes = kCols * kChunkL;
-    static constexpr int N = 2;
-    static constexpr int Occ = (2 * (N * kBytes + 4 * kDsList + 256) <= 160 * 1024) ? 2 : 1;
+    static constexpr int kFixed = 4 * kDsList + 256;
+    static constexpr int Occ = (2 * (2 * kBytes + kFixed) <= 160 * 1024) ? 2 : 1;
+    static constexpr int kFit = (160 * 1024 - kFixed) / kBytes;
+    static constexpr int N = Occ == 2 ? 2 : (kFit > 4 ? 4 : kFit);
+    static_assert(N >= 2, "two LDS stages must fit");
 };
 
 template <int DKP>
