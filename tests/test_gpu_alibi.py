@@ -48,6 +48,8 @@ CASES = [
     ("random_mask_d64", Shape(2, 4, 2, 200, 300, 64, 64), "random", 502),
     ("d192_128_padding", Shape(1, 3, 3, 130, 260, 192, 128), "padding", 503),
     ("odd_dims_nomask", Shape(1, 3, 1, 70, 90, 40, 72), None, 504),
+    # 256-wide heads: the 4-wave dK/dV kernel with its columns split over two work-groups
+    ("d256_random_gqa", Shape(1, 4, 2, 90, 200, 256, 256), "random", 506),
     ("two_heads_per_wg", Shape(2, 32, 8, 70, 2048, 128, 128), None, 505),
 ]
 
