@@ -22,8 +22,8 @@ Beside it: `whole_path`, the op's own semantics (O = lse = NULL: the forward run
 inside fab_backward, counted as forward plus backward flops); `forward_only`;
 causal workloads with the causal rule passed as a flag instead of the mask tensor
 (`causal_flag_instead_of_mask`); bf16 mode with q, k, v, d stored as bf16
-(`bf16_inputs`) and with O stored as bf16 as well (`bf16_storage`), or stored as f16
-(`f16_inputs`); and `configs`: every other (workload, mode) pair of the five
+(`bf16_inputs`), with O stored as bf16 as well (`bf16_storage`) and with the result
+blob as bf16 too (`bf16_storage_and_blob`), or stored as f16 (`f16_inputs`); and `configs`: every other (workload, mode) pair of the five
 workloads, each with its backward alone (and kernel split), whole path and
 fraction of its mode's peak.  `mfma_loop_ceiling` (bf16 mode) is the rate of a
 loop of dense bf16 products on every SIMD, with the shader clock it runs at: the
@@ -458,7 +458,17 @@ def main():
         out["bf16_storage"] = {"what": "q, k, v, d and O stored as bf16",
                                "backward_only": {"ms": round(ms_o, 4), "tflops": round(F_b / (ms_o * 1e-3) / 1e12, 3),
                                                  "frac_of_peak": round(F_b / (ms_o * 1e-3) / 1e12 / peak, 4)}}
-        del tb, O16, lse16
+        # ... and the result blob as bf16 too (FAB_BF16_BLOB: the f32 gradients rounded
+        # once at the store): every tensor the backward reads or writes is 16-bit
+        blob16 = torch.empty(fab.blob_layout(c.fs, torch.bfloat16)[3], dtype=torch.bfloat16, device=dev)
+        ms_ob = time_loop(torch, lambda: fab.backward(*tb, c.scale, mask=c.tm, mode=mode, O=O16, lse=lse16,
+                                                      blob=blob16, ws=c.ws_bwd),
+                          args.steps, args.warmup, stream, args.min_warm_s)
+        out["bf16_storage_and_blob"] = {
+            "what": "q, k, v, d, O and the result blob stored as bf16",
+            "backward_only": {"ms": round(ms_ob, 4), "tflops": round(F_b / (ms_ob * 1e-3) / 1e12, 3),
+                              "frac_of_peak": round(F_b / (ms_ob * 1e-3) / 1e12 / peak, 4)}}
+        del tb, O16, lse16, blob16
         # ... and q, k, v, d stored as f16 instead (FAB_F16_INPUTS: widened exactly, then
         # rounded to bf16 like f32 inputs)
         th = [x.to(torch.float16) for x in (tq, tk, tv, td)]

@@ -25,6 +25,8 @@ FAB_CAUSAL = 0x100   # flag: the causal rule (key m seen by query n iff m <= n) 
 FAB_BF16_INPUTS = 0x200   # flag: q, k, v, d are bf16 (bf16 mode only)
 FAB_F16_INPUTS = 0x800    # flag: q, k, v, d are f16 (bf16 mode only)
 FAB_BF16_O = 0x400        # flag: O is bf16 (bf16 mode only)
+FAB_BF16_BLOB = 0x1000    # flag: the result blob is bf16 (bf16 mode, backward only)
+FAB_F16_BLOB = 0x2000     # flag: the result blob is f16 (bf16 mode, backward only)
 MODES = {"f32": FAB_MODE_F32, "bf16": FAB_MODE_BF16, FAB_MODE_F32: FAB_MODE_F32,
          FAB_MODE_BF16: FAB_MODE_BF16}
 
@@ -36,7 +38,7 @@ FAB_E_ALIGN = -4
 FAB_E_HIP = -5
 
 # every symbol include/fab.h declares
-EXPORTS = ("fab_blob_layout", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
+EXPORTS = ("fab_blob_layout", "fab_blob_layout16", "fab_workspace_bytes", "fab_forward_lse", "fab_backward",
            "fab_forward_lse_alibi", "fab_backward_alibi", "fab_backward_noalloc", "fab_profile_enable", "fab_profile_reset", "fab_profile_read",
            "fab_probe_scratch_bytes", "fab_measure_mfma_loop", "fab_strerror", "fab_last_error", "fab_version")
 KERNELS = ("block_map", "forward", "prep", "pack", "backward", "dq", "gqa_reduce")
@@ -68,6 +70,9 @@ def lib():
         L.fab_blob_layout.restype = I
         L.fab_blob_layout.argtypes = [SP, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                       ctypes.POINTER(I64), ctypes.POINTER(I64)]
+        L.fab_blob_layout16.restype = I
+        L.fab_blob_layout16.argtypes = [SP, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                        ctypes.POINTER(I64), ctypes.POINTER(I64)]
         L.fab_workspace_bytes.restype = I
         L.fab_workspace_bytes.argtypes = [SP, I, I, I, ctypes.POINTER(SZ)]
         L.fab_forward_lse.restype = I
@@ -127,19 +132,31 @@ def shape_of(q, k, v):
     return Shape(B, H, Hkv, N, M, DK, DV)
 
 
-def blob_layout(shape: Shape):
-    """(off_q, off_k, off_v, total_floats) of the packed [dQ | dK | dV] blob."""
+def _blob_dtypes():
+    import torch
+    return (torch.float32, torch.bfloat16, torch.float16)
+
+
+def blob_layout(shape: Shape, dtype=None):
+    """(off_q, off_k, off_v, total) of the packed [dQ | dK | dV] blob, in elements of
+    dtype: float32 (None; fab_blob_layout) or bfloat16 / float16 (fab_blob_layout16)."""
+    if dtype is not None and dtype not in _blob_dtypes():
+        raise TypeError(f"blob dtype must be float32, bfloat16 or float16, got {dtype}")
+    f32 = dtype is None or dtype == _blob_dtypes()[0]
+    fn = lib().fab_blob_layout if f32 else lib().fab_blob_layout16
     o = [ctypes.c_int64() for _ in range(4)]
-    _check(lib().fab_blob_layout(ctypes.byref(shape.c()), *[ctypes.byref(x) for x in o]))
+    _check(fn(ctypes.byref(shape.c()), *[ctypes.byref(x) for x in o]))
     return tuple(x.value for x in o)
 
 
-def _mode(mode, causal, inputs=None, bf16_o=False):
+def _mode(mode, causal, inputs=None, bf16_o=False, blob=None):
     """The mode argument: mode | causal flag | input storage flag (inputs: the torch dtype
-    of q, k, v, d; float32 needs no flag) | bf16 O flag."""
+    of q, k, v, d; float32 needs no flag) | bf16 O flag | blob flag (blob: the torch
+    dtype of the result blob; float32 needs no flag)."""
     import torch
     flag = {torch.bfloat16: FAB_BF16_INPUTS, torch.float16: FAB_F16_INPUTS}.get(inputs, 0) if inputs is not None else 0
-    return MODES[mode] | (FAB_CAUSAL if causal else 0) | flag | (FAB_BF16_O if bf16_o else 0)
+    bflag = {torch.bfloat16: FAB_BF16_BLOB, torch.float16: FAB_F16_BLOB}.get(blob, 0) if blob is not None else 0
+    return MODES[mode] | (FAB_CAUSAL if causal else 0) | flag | (FAB_BF16_O if bf16_o else 0) | bflag
 
 
 def workspace_bytes(shape: Shape, mode="f32", has_mask=False, have_o_lse=False, causal=False) -> int:
@@ -281,8 +298,10 @@ def forward_lse(q, k, v, scale, mask=None, mode="f32", O=None, lse=None, ws=None
 
 
 def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=None, ws=None,
-             stream=None, causal=False, alibi=None):
-    """The packed f32 blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v).
+             stream=None, causal=False, alibi=None, blob_dtype=None):
+    """The packed blob [dQ | pad | dK | pad | dV | pad] of d sum(d * attn) / d(q, k, v):
+    float32, or (mode "bf16") bfloat16 / float16 elements rounded from the f32 result --
+    the dtype of a given blob, else blob_dtype (default float32).
     causal=True applies the causal rule without a mask (mask must be None).  q, k, v, d
     are float32, or bfloat16 or float16 (all four; mode "bf16").  O (B,N,H,DV) and lse (B,H,N),
     (float32, or bfloat16 as forward_lse wrote it) are both given (from forward_lse,
@@ -305,21 +324,22 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
         _check_tensor(O, "O", (s.B, s.N, s.H, s.DV), (torch.float32, torch.bfloat16))
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
         o_bf16 = O.dtype == torch.bfloat16
-    total = blob_layout(s)[3]
+    bdt = blob.dtype if blob is not None else (blob_dtype or torch.float32)
+    total = blob_layout(s, bdt)[3]
     if blob is not None:
-        _check_tensor(blob, "blob", None)
+        _check_tensor(blob, "blob", None, _blob_dtypes())
         if blob.numel() < total:
-            raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
+            raise ValueError(f"blob has {blob.numel()} elements, {total} needed")
     if ws is not None:
         nbytes = _check_ws(ws, workspace_bytes(s, mode, mask is not None, O is not None, causal))
     _check_devices(dev, k=k, v=v, d=d, mask=mask, alibi=alibi, O=O, lse=lse, blob=blob, ws=ws)
     with _on_stream(stream):
         if blob is None:
-            blob = torch.empty(max(total, 4), dtype=torch.float32, device=dev)
+            blob = torch.empty(max(total, 8), dtype=bdt, device=dev)
         if ws is None:
             ws, nbytes = alloc_workspace(s, mode, mask is not None, O is not None, dev, causal)
         _check(lib().fab_backward_alibi(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(alibi),
-                                        _ptr(d), float(scale), _mode(mode, causal, in_dt, o_bf16), _ptr(O),
+                                        _ptr(d), float(scale), _mode(mode, causal, in_dt, o_bf16, bdt), _ptr(O),
                                         _ptr(lse), _ptr(blob), _ptr(ws), nbytes, _stream_handle(stream)))
     return blob
 
@@ -330,8 +350,9 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # FAB_NOALLOC_SCRATCH_BYTES of include/fab.h
 def backward_noalloc(q, k, v, d, scale, blob, mask=None, mode="f32", O=None, lse=None, stream=None,
                      causal=False):
     """backward() through fab_backward_noalloc: the library's fixed scratch array serves
-    as the workspace, so the call allocates nothing; the caller passes the blob (f32,
-    at least blob_layout()[3] floats).  Shapes needing more than NOALLOC_SCRATCH_BYTES
+    as the workspace, so the call allocates nothing; the caller passes the blob (float32,
+    or in mode "bf16" bfloat16 / float16, at least blob_layout(shape, blob.dtype)[3]
+    elements).  Shapes needing more than NOALLOC_SCRATCH_BYTES
     of workspace raise FabError (FAB_E_UNSUPPORTED)."""
     import torch
     s = shape_of(q, k, v)
@@ -347,21 +368,22 @@ def backward_noalloc(q, k, v, d, scale, blob, mask=None, mode="f32", O=None, lse
     if O is not None:
         _check_tensor(O, "O", (s.B, s.N, s.H, s.DV))
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
-    _check_tensor(blob, "blob", None)
-    total = blob_layout(s)[3]
+    _check_tensor(blob, "blob", None, _blob_dtypes())
+    total = blob_layout(s, blob.dtype)[3]
     if blob.numel() < total:
-        raise ValueError(f"blob has {blob.numel()} floats, {total} needed")
+        raise ValueError(f"blob has {blob.numel()} elements, {total} needed")
     _check_devices(dev, k=k, v=v, d=d, mask=mask, O=O, lse=lse, blob=blob)
     _check(lib().fab_backward_noalloc(ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(d),
-                                      float(scale), _mode(mode, causal, in_dt), _ptr(O), _ptr(lse), _ptr(blob),
+                                      float(scale), _mode(mode, causal, in_dt, blob=blob.dtype), _ptr(O), _ptr(lse), _ptr(blob),
                                       _stream_handle(stream)))
     return blob
 
 
 def unpack(blob, shape: Shape):
-    """Views dq (B,H,N,DK), dk (B,Hkv,M,DK), dv (B,Hkv,M,DV) into the blob at the padded offsets."""
+    """Views dq (B,H,N,DK), dk (B,Hkv,M,DK), dv (B,Hkv,M,DV) into the blob at the padded
+    offsets of its dtype."""
     s = shape
-    _, off_k, off_v, _ = blob_layout(s)
+    _, off_k, off_v, _ = blob_layout(s, blob.dtype)
     nq, nk, nv = s.DK * s.N * s.H * s.B, s.DK * s.M * s.Hkv * s.B, s.DV * s.M * s.Hkv * s.B
     dq = blob[0:nq].view(s.B, s.H, s.N, s.DK)
     dk = blob[off_k:off_k + nk].view(s.B, s.Hkv, s.M, s.DK)

@@ -32,12 +32,14 @@ constexpr int kMaxHeadDim = 256;
 constexpr size_t kWsAlign = 256;
 
 int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
+int64_t pad8(int64_t n) { return (n + 7) / 8 * 8; }
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Plan {
     fab::Dims d;
-    int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;
+    int64_t nq, nk, nv, nrow, nO, off_k, off_v, total;   // blob offsets and length in its elements
+    int esize;                                            // bytes of one blob element (4, or 2 for 16-bit)
     // workspace offsets (bytes) and total
     size_t ws_map, ws_k16, ws_v16, ws_fwd, ws_lse, ws_O, ws_delta, ws_q16, ws_o16, ws_stats, ws_dqp, ws_tick, ws_ds,
         ws_pk, ws_pv, ws_bytes;
@@ -49,6 +51,19 @@ struct Plan {
     int upg;       // dK/dV partials per key/value head (1: none, the kernels write the result)
     bool part;     // dK/dV go through per-unit partials and the grouped-query reduction
 };
+
+// Blob layout [dQ | pad | dK | pad | dV | pad] for elements of fmt: every slice
+// starts on a 16-byte boundary (4 f32 or 8 16-bit elements).
+void set_blob_layout(Plan *pl, int fmt)
+{
+    const bool h = fmt != fab::kF32;
+    auto pad = h ? pad8 : pad4;
+    pl->esize = h ? 2 : 4;
+    pl->d.out_fmt = fmt;
+    pl->off_k = pad(pl->nq);
+    pl->off_v = pl->off_k + pad(pl->nk);
+    pl->total = pl->off_v + pad(pl->nv);
+}
 
 // Shape checks: the asserts of "Function ggml_flash_attn_back" restated for the
 // ggmlR layouts (q [DK,N,H,B], k [DK,M,Hkv,B], v [DV,M,Hkv,B], d [DV,H,N,B]),
@@ -81,9 +96,7 @@ int check_shape(const fab_shape *s, Plan *pl)
     pl->nv = s->DV * s->M * s->Hkv * s->B;
     pl->nO = s->DV * s->H * s->N * s->B;
     pl->nrow = s->N * s->H * s->B;
-    pl->off_k = pad4(pl->nq);
-    pl->off_v = pl->off_k + pad4(pl->nk);
-    pl->total = pl->off_v + pad4(pl->nv);
+    set_blob_layout(pl, fab::kF32);
     if ((double)pl->total > kMaxElems) return fail(FAB_E_UNSUPPORTED, "result blob exceeds 2^31-1 floats");
     pl->gqa = s->H > s->Hkv;
     fab::HeadDims hd;
@@ -176,22 +189,29 @@ int check_mode(int mode)
     return FAB_OK;
 }
 
-// Splits the FAB_CAUSAL, FAB_BF16_INPUTS, FAB_F16_INPUTS and FAB_BF16_O flags off the
-// mode argument and checks the rest; *in_fmt receives the storage of q, k, v and d.
-int take_mode(int *mode, bool *causal, int *in_fmt, bool *o_bf16 = nullptr)
+// Splits the FAB_CAUSAL, FAB_BF16_INPUTS, FAB_F16_INPUTS, FAB_BF16_O, FAB_BF16_BLOB and
+// FAB_F16_BLOB flags off the mode argument and checks the rest; *in_fmt receives the
+// storage of q, k, v and d, *out_fmt (when given) the blob's element type.  Without
+// out_fmt (the forward, which writes no blob) the blob flags are FAB_E_INVAL.
+int take_mode(int *mode, bool *causal, int *in_fmt, bool *o_bf16 = nullptr, int *out_fmt = nullptr)
 {
     *causal = (*mode & FAB_CAUSAL) != 0;
     const bool ib = (*mode & FAB_BF16_INPUTS) != 0, ih = (*mode & FAB_F16_INPUTS) != 0;
     const bool ob = (*mode & FAB_BF16_O) != 0;
+    const bool bb = (*mode & FAB_BF16_BLOB) != 0, hb = (*mode & FAB_F16_BLOB) != 0;
     if (o_bf16) *o_bf16 = ob;
-    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS | FAB_F16_INPUTS | FAB_BF16_O);
+    *mode &= ~(FAB_CAUSAL | FAB_BF16_INPUTS | FAB_F16_INPUTS | FAB_BF16_O | FAB_BF16_BLOB | FAB_F16_BLOB);
     const int rc = check_mode(*mode);
     if (rc != FAB_OK) return rc;
     if (ib && ih) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS and FAB_F16_INPUTS are exclusive");
     if (ib && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_INPUTS needs FAB_MODE_BF16");
     if (ih && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_F16_INPUTS needs FAB_MODE_BF16");
     if (ob && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_O needs FAB_MODE_BF16");
+    if ((bb || hb) && !out_fmt) return fail(FAB_E_INVAL, "FAB_BF16_BLOB / FAB_F16_BLOB apply to the backward only");
+    if (bb && hb) return fail(FAB_E_INVAL, "FAB_BF16_BLOB and FAB_F16_BLOB are exclusive");
+    if ((bb || hb) && *mode != FAB_MODE_BF16) return fail(FAB_E_INVAL, "FAB_BF16_BLOB / FAB_F16_BLOB need FAB_MODE_BF16");
     *in_fmt = ib ? fab::kBF16 : (ih ? fab::kF16 : fab::kF32);
+    if (out_fmt) *out_fmt = bb ? fab::kBF16 : (hb ? fab::kF16 : fab::kF32);
     return FAB_OK;
 }
 
@@ -405,14 +425,28 @@ int fab_blob_layout(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int6
     return FAB_OK;
 }
 
+int fab_blob_layout16(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int64_t *off_v,
+                      int64_t *total_elems)
+{
+    g_err[0] = 0;
+    Plan pl;
+    FAB_TRY(check_shape(shape, &pl));
+    set_blob_layout(&pl, fab::kBF16);
+    if (off_q) *off_q = 0;
+    if (off_k) *off_k = pl.off_k;
+    if (off_v) *off_v = pl.off_v;
+    if (total_elems) *total_elems = pl.total;
+    return FAB_OK;
+}
+
 int fab_workspace_bytes(const fab_shape *shape, int mode, int has_mask, int have_o_lse, size_t *bytes)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
     bool causal;
-    int in_fmt;
-    FAB_TRY(take_mode(&mode, &causal, &in_fmt));
+    int in_fmt, out_fmt;
+    FAB_TRY(take_mode(&mode, &causal, &in_fmt, nullptr, &out_fmt));   // the blob's type changes no workspace
     if (!bytes) return fail(FAB_E_INVAL, "bytes is NULL");
     if (causal && has_mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     plan_workspace(&pl, mode, has_mask != 0, have_o_lse != 0);
@@ -465,14 +499,15 @@ int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, 
 
 int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
                        const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
-                       const void *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+                       const void *O, const float *lse, void *blob, void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     Plan pl;
     FAB_TRY(check_shape(shape, &pl));
     bool causal, o_bf16;
-    int in_fmt;
-    FAB_TRY(take_mode(&mode, &causal, &in_fmt, &o_bf16));
+    int in_fmt, out_fmt;
+    FAB_TRY(take_mode(&mode, &causal, &in_fmt, &o_bf16, &out_fmt));
+    set_blob_layout(&pl, out_fmt);
     if (causal && mask) return fail(FAB_E_INVAL, "a mask and FAB_CAUSAL exclude each other");
     FAB_TRY(check_alibi(alibi));
     pl.d.causal = causal;
@@ -502,10 +537,14 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (empty) {
         // no queries (dK = dV = 0) or no keys (every row all-masked: dQ = 0)
-        FAB_HIP(fab::launch_zero(blob, pl.total, s), "zero blob");
+        FAB_HIP(fab::launch_zero(static_cast<float *>(blob), pl.total * pl.esize / 4, s), "zero blob");
         return FAB_OK;
     }
     char *wsb = static_cast<char *>(ws);
+    // the blob's slices as the kernels take them: element offsets of the blob's type
+    float *const bq = static_cast<float *>(blob);
+    float *const bk = reinterpret_cast<float *>(static_cast<char *>(blob) + pl.off_k * pl.esize);
+    float *const bv = reinterpret_cast<float *>(static_cast<char *>(blob) + pl.off_v * pl.esize);
     uint8_t *map = use_mask ? reinterpret_cast<uint8_t *>(wsb + pl.ws_map) : nullptr;
     const uint16_t *mk = use_mask ? mask : nullptr;
     const int bf16 = mode == FAB_MODE_BF16;
@@ -526,7 +565,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
         // directly (no O, no separate prep pass); dQ is written once by the
         // query-block-outer kernel (only its pad is zeroed)
         FAB_TRY(launch_pack(pl, q, k, v, nullptr, k16, v16, mk, map, s));
-        FAB_LAUNCH(kFwd, fab::launch_forward_prep_bf16(q, k16, v16, mk, map, scale, d, q16, o16, stats, blob, pl.nq,
+        FAB_LAUNCH(kFwd, fab::launch_forward_prep_bf16(q, k16, v16, mk, map, scale, d, q16, o16, stats, bq, pl.nq,
                                                        pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, tick, ntick, pl.np,
                                                        pl.mp, pl.d, s),
                    "forward launch");
@@ -534,7 +573,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
         // the bf16 tiles of Q, K, V (and the block map) with the dO tiles and LSE/D
         // blocks of the supplied O and LSE: one launch
         FAB_LAUNCH(kPack,
-                   fab::launch_pack_prep_bf16(q, k, v, q16, k16, v16, mk, map, d, O, lse, o16, stats, blob, pl.nq,
+                   fab::launch_pack_prep_bf16(q, k, v, q16, k16, v16, mk, map, d, O, lse, o16, stats, bq, pl.nq,
                                               pl.off_k, pl.nk, pl.off_v, pl.nv, pl.total, tick, ntick, pl.np, pl.mp,
                                               pl.d, s),
                    "pack and prep launch");
@@ -548,34 +587,34 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
             Ou = Ow;
             lseu = lw;
         }
-        FAB_LAUNCH(kPrep, fab::launch_prep(static_cast<const float *>(d), Ou, delta, blob, pl.off_k, pl.nk, pl.off_v,
+        FAB_LAUNCH(kPrep, fab::launch_prep(static_cast<const float *>(d), Ou, delta, bq, pl.off_k, pl.nk, pl.off_v,
                                            pl.nv, pl.total, pl.d, s),
                    "prep launch");
     }
-    float *dk = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pk) : blob + pl.off_k;
-    float *dv = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pv) : blob + pl.off_v;
+    float *dk = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pk) : bk;
+    float *dv = pl.part ? reinterpret_cast<float *>(wsb + pl.ws_pv) : bv;
     if (bf16) {
         FAB_LAUNCH(kBwd, fab::launch_backward_bf16(q16, o16, stats, k16, v16, mk, map, scale, dk, dv, dst,
                                                    pl.part ? 1 : 0, pl.np, pl.mp, pl.d, s),
                    "backward launch");
         if (pl.ds)   // with the grouped-query reduction of dK and dV in the same launch
-            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, blob, pl.np, pl.mp, pl.part ? dk : nullptr,
-                                                   blob + pl.off_k, pl.part ? dv : nullptr, blob + pl.off_v, pl.upg,
+            FAB_LAUNCH(kDq, fab::launch_dq_from_ds(dst, k16, map, scale, bq, pl.np, pl.mp, pl.part ? dk : nullptr,
+                                                   bk, pl.part ? dv : nullptr, bv, pl.upg,
                                                    pl.d, s),
                        "dQ launch");
         else
-            FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, blob, dqp, tick, pl.np, pl.mp,
+            FAB_LAUNCH(kDq, fab::launch_dq(q16, o16, stats, k16, v16, mk, map, scale, bq, dqp, tick, pl.np, pl.mp,
                                            pl.d, s),
                        "dQ launch");
     } else {
         FAB_LAUNCH(kBwd, fab::launch_backward_f32(static_cast<const float *>(q), static_cast<const float *>(k),
                                                   static_cast<const float *>(v), static_cast<const float *>(d), mk,
-                                                  map, lseu, delta, scale, blob, dk, dv,
+                                                  map, lseu, delta, scale, bq, dk, dv,
                                                   pl.part ? 1 : 0, pl.d, s),
                    "backward launch");
     }
     if (pl.part && !pl.ds) {
-        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, blob + pl.off_k, dv, blob + pl.off_v, pl.d, pl.upg, s),
+        FAB_LAUNCH(kRed, fab::launch_gqa_reduce(dk, bk, dv, bv, pl.d, pl.upg, s),
                    "dK/dV reduce launch");
     }
     return FAB_OK;
@@ -590,7 +629,7 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
 
 int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
                  const uint16_t *mask, const void *d, float scale, int mode, const void *O,
-                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream)
+                 const float *lse, void *blob, void *ws, size_t ws_bytes, void *stream)
 {
     return fab_backward_alibi(shape, q, k, v, mask, nullptr, d, scale, mode, O, lse, blob, ws, ws_bytes, stream);
 }

@@ -164,7 +164,7 @@ struct PrepExtra {
     const float *lse;                 // row LSE [N,H,B] (natural log)
     float *stats;                     // LSE/D blocks [heads][Mp/64][128]
     float *blob;                      // result blob whose pads are zeroed (work-group 0)
-    int64_t pad_lo[3], pad_hi[3];
+    int64_t pad_lo[3], pad_hi[3];     // the pads, in 16-bit units (zero in every element type)
     int *zero;                        // nzero ints set to 0 (the dQ split counters)
     int nzero;
 };
@@ -262,9 +262,9 @@ template <int DKP, int DVP>
 __global__ __launch_bounds__(256) void pack_prep_kernel(PackJobs a, PackJob j, PrepExtra x)
 {
     for (int i = blockIdx.x * 256 + threadIdx.x; i < x.nzero; i += gridDim.x * 256) x.zero[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x < 4)
+    if (blockIdx.x == 0 && threadIdx.x < 8)   // pads below 16 bytes: at most 7 16-bit units
         for (int k = 0; k < 3; ++k)
-            if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) x.blob[x.pad_lo[k] + threadIdx.x] = 0.f;
+            if (x.pad_lo[k] + threadIdx.x < x.pad_hi[k]) reinterpret_cast<uint16_t *>(x.blob)[x.pad_lo[k] + threadIdx.x] = 0;
     int bt = blockIdx.x;
     if (bt < j.tiles) {
         pack_tile<DVP>(j, bt, &x);
@@ -339,9 +339,10 @@ void prep_job(const void *dO, const void *O, const float *lse, __bf16 *dO16, flo
     j.tiles = d.H * d.B * (Np / 64);
     PrepExtra x = {};
     x.O = O; x.O_bf16 = d.o_bf16; x.lse = lse; x.stats = stats; x.blob = blob;
-    x.pad_lo[0] = nq; x.pad_hi[0] = off_k;
-    x.pad_lo[1] = off_k + nk; x.pad_hi[1] = off_v;
-    x.pad_lo[2] = off_v + nv; x.pad_hi[2] = total;
+    const int u = d.out_fmt == kF32 ? 2 : 1;   // 16-bit units per blob element
+    x.pad_lo[0] = u * nq; x.pad_hi[0] = u * off_k;
+    x.pad_lo[1] = u * (off_k + nk); x.pad_hi[1] = u * off_v;
+    x.pad_lo[2] = u * (off_v + nv); x.pad_hi[2] = u * total;
     x.zero = zero; x.nzero = nzero;
     *pj = j;
     *px = x;

@@ -75,6 +75,7 @@ struct KvArgs {
     int B, H, Hkv, N, Np, M, Mp, DK, DV;
     int hpw;                        // query heads of one group per work-group (1 or 2), summed in registers
     int qsplit;                     // work-groups per (key block, head unit) on interleaved query steps (8-wave kernel)
+    int out_fmt;                    // element type of the result blob (dk, dv when not partials)
     int part_heads, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     float scale;
@@ -100,7 +101,7 @@ struct KStages {
     static_assert(N >= 2, "two LDS stages must fit");
 };
 
-template <int DKP, int DVP, bool AB>
+template <int DKP, int DVP, bool AB, bool O16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(KvArgs p)
 {
     using ST = KStages<DKP, DVP>;
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- store dK (scaled) and dV of this key block: per unit (head unit x query
     // split; partials) or, when a unit covers the whole group, into the result
     const int hdd = p.part_heads ? hp * qs + split : g, Hd = p.part_heads ? hpu * qs : p.Hkv;
-    float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
-    float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
+    // O16: the result slices hold 16-bit elements (p.out_fmt); partials are always f32
+    const size_t dk0 = (size_t)p.DK * p.M * (hdd + Hd * b), dv0 = (size_t)p.DV * p.M * (hdd + Hd * b);
 #pragma unroll
     for (int dt = 0; dt < DKP / 32; ++dt) {
         const int col = dt * 32 + l32;
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 32 * kw + crow(r, half);
-                if (key < p.M) dkb[col + (size_t)p.DK * key] = dkacc[dt][r] * p.scale;
+                if (key < p.M) store_as<O16>(p.dk, dk0 + col + (size_t)p.DK * key, dkacc[dt][r] * p.scale, p.out_fmt);
             }
     }
 #pragma unroll
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 32 * kw + crow(r, half);
-                if (key < p.M) dvb[col + (size_t)p.DV * key] = dvacc[dt][r];
+                if (key < p.M) store_as<O16>(p.dv, dv0 + col + (size_t)p.DV * key, dvacc[dt][r], p.out_fmt);
             }
     }
 }
@@ -424,7 +425,7 @@ struct KStages4 {
 // MS: the mask rows of every step are copied into the LDS stage with the Q and dO
 // tiles (mask given, M % 8 == 0), so a MIXED step reads its mask from LDS instead of
 // waiting on 32 global loads with nothing else in flight (one wave per SIMD).
-template <int DKP, int DVP, bool AB, bool MS>
+template <int DKP, int DVP, bool AB, bool MS, bool O16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_bf16_w4_kernel(KvArgs p)
 {
     using ST = KStages4<DKP, DVP, MS>;
@@ -676,8 +677,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- store dK (scaled) and dV of this key block (this work-group's columns)
     const int hdd = p.part_heads ? h : g, Hd = p.part_heads ? p.H : p.Hkv;
-    float *dkb = p.dk + (size_t)p.DK * p.M * (hdd + Hd * b);
-    float *dvb = p.dv + (size_t)p.DV * p.M * (hdd + Hd * b);
+    // O16: the result slices hold 16-bit elements (p.out_fmt); partials are always f32
+    const size_t dk0 = (size_t)p.DK * p.M * (hdd + Hd * b), dv0 = (size_t)p.DV * p.M * (hdd + Hd * b);
 #pragma unroll
     for (int dt = 0; dt < NKC; ++dt) {
         const int col = (NKC * cs + dt) * 32 + l32;
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 32 * w + crow(r, half);
-                if (key < p.M) dkb[col + (size_t)p.DK * key] = dkacc[dt][r] * p.scale;
+                if (key < p.M) store_as<O16>(p.dk, dk0 + col + (size_t)p.DK * key, dkacc[dt][r] * p.scale, p.out_fmt);
             }
     }
 #pragma unroll
@@ -695,7 +696,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 32 * w + crow(r, half);
-                if (key < p.M) dvb[col + (size_t)p.DV * key] = dvacc[dt][r];
+                if (key < p.M) store_as<O16>(p.dv, dv0 + col + (size_t)p.DV * key, dvacc[dt][r], p.out_fmt);
             }
     }
 }
@@ -1026,6 +1027,13 @@ hipError_t run_bwd_f32(const BwdArgs &a, hipStream_t s)
     }
 }
 
+// The kernel instance for the result's element width: 16-bit only when the kernel
+// itself writes a 16-bit result (partials stay f32).
+inline void launch_o16(const KvArgs &a, void (*k32)(KvArgs), void (*k16)(KvArgs), dim3 grid, int nt, hipStream_t s)
+{
+    hipLaunchKernelGGL((!a.part_heads && a.out_fmt != kF32) ? k16 : k32, grid, dim3(nt), 0, s, a);
+}
+
 template <int DKP, int DVP, bool BF16>
 hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
 {
@@ -1034,9 +1042,9 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
     } else if constexpr (DKP + DVP <= 256) {
         const dim3 grid(ceil_div(a.M, kKBC) * (a.H / a.hpw) * a.B * a.qsplit);
         if (a.alibi)
-            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, true>), grid, dim3(kKNT), 0, s, a);
+            launch_o16(a, bwd_bf16_kernel<DKP, DVP, true, false>, bwd_bf16_kernel<DKP, DVP, true, true>, grid, kKNT, s);
         else
-            hipLaunchKernelGGL((bwd_bf16_kernel<DKP, DVP, false>), grid, dim3(kKNT), 0, s, a);
+            launch_o16(a, bwd_bf16_kernel<DKP, DVP, false, false>, bwd_bf16_kernel<DKP, DVP, false, true>, grid, kKNT, s);
         return hipGetLastError();
     } else {
         const dim3 grid(ceil_div(a.M, kKBC) * a.H * a.B * kW4ColSplit<DKP, DVP>);
@@ -1046,16 +1054,20 @@ hipError_t run_bwd_bf16(const KvArgs &a, hipStream_t s)
         if constexpr (kMsFits) {
             if (ms) {
                 if (a.alibi)
-                    hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, true>), grid, dim3(kKNT4), 0, s, a);
+                    launch_o16(a, bwd_bf16_w4_kernel<DKP, DVP, true, true, false>, bwd_bf16_w4_kernel<DKP, DVP, true, true, true>, grid,
+                               kKNT4, s);
                 else
-                    hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, true>), grid, dim3(kKNT4), 0, s, a);
+                    launch_o16(a, bwd_bf16_w4_kernel<DKP, DVP, false, true, false>, bwd_bf16_w4_kernel<DKP, DVP, false, true, true>, grid,
+                               kKNT4, s);
                 return hipGetLastError();
             }
         }
         if (a.alibi)
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, true, false>), grid, dim3(kKNT4), 0, s, a);
+            launch_o16(a, bwd_bf16_w4_kernel<DKP, DVP, true, false, false>, bwd_bf16_w4_kernel<DKP, DVP, true, false, true>, grid,
+                               kKNT4, s);
         else
-            hipLaunchKernelGGL((bwd_bf16_w4_kernel<DKP, DVP, false, false>), grid, dim3(kKNT4), 0, s, a);
+            launch_o16(a, bwd_bf16_w4_kernel<DKP, DVP, false, false, false>, bwd_bf16_w4_kernel<DKP, DVP, false, false, true>, grid,
+                               kKNT4, s);
         return hipGetLastError();
     }
 }
@@ -1094,6 +1106,7 @@ hipError_t launch_backward_bf16(const __bf16 *q16, const __bf16 *o16, const floa
     // dS^T totals up to 64 MiB stay in the caches between the two launches (the dQ
     // launch reads them back from there); larger ones are streamed past the L2
     a.ds_bytes = ds ? (uint32_t)ds_bytes(d, Np) : 0u;
+    a.out_fmt = d.out_fmt;
     a.ds_cached = ds && ds_bytes(d, Np) <= ((int64_t)64 << 20);
     a.hpw = bwd_heads_per_wg(d, hd.dk, hd.dv);
     a.qsplit = bwd_query_splits(d, hd.dk, hd.dv);

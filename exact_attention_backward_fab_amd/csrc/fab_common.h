@@ -324,6 +324,63 @@ __device__ __forceinline__ void query_block_work(int bid, int nqt, int HB, int f
     *qt = (!fold || sl < hn) ? nqt - 1 - sl : sl - hn;
 }
 
+// ---------------------------------------------------------------- result stores
+// A result slice holds f32 elements, or 16-bit ones (kBF16 / kF16) rounded to
+// nearest even from the f32 value.  The 16-bit bits of x in format fmt:
+__device__ __forceinline__ uint16_t result_bits16(float x, int fmt)
+{
+    // x as an f32 value in a register: without this the compiler may fuse the
+    // product or sum that made x into one mixed-precision operation that rounds
+    // the exact result to 16 bits once (no longer the f32 value rounded)
+    asm("" : "+v"(x));
+    const __bf16 b = (__bf16)x;
+    const _Float16 h = (_Float16)x;
+    return fmt == kF16 ? __builtin_bit_cast(uint16_t, h) : __builtin_bit_cast(uint16_t, b);
+}
+// Element i of a result slice at base.  W16 (compile time): 16-bit elements of
+// format fmt (the choice between the two is a select, not a branch); else f32.
+template <bool W16>
+__device__ __forceinline__ void store_as(float *base, size_t i, float x, int fmt)
+{
+    if constexpr (W16)
+        reinterpret_cast<uint16_t *>(base)[i] = result_bits16(x, fmt);
+    else
+        base[i] = x;
+}
+// fn(std::bool_constant<W16>) with W16 = (fmt is a 16-bit format): a store loop
+// inside fn is compiled once per element width and carries no per-element branch.
+template <class Fn>
+__device__ __forceinline__ void with_result_width(int fmt, Fn &&fn)
+{
+    if (fmt == kF32)
+        fn(std::bool_constant<false>{});
+    else
+        fn(std::bool_constant<true>{});
+}
+// The same with the width chosen at run time (single stores off the hot loops).
+__device__ __forceinline__ void store_result(float *base, size_t i, float x, int fmt)
+{
+    if (fmt == kF32)
+        base[i] = x;
+    else
+        reinterpret_cast<uint16_t *>(base)[i] = result_bits16(x, fmt);
+}
+// Elements 4 q .. 4 q + 3 (16-byte aligned for f32, 8-byte for 16-bit elements).
+__device__ __forceinline__ void store_result4(float *base, size_t q, f32x4 x, int fmt)
+{
+    if (fmt == kF32) {
+        reinterpret_cast<f32x4 *>(base)[q] = x;
+        return;
+    }
+    asm("" : "+v"(x));   // the f32 sums themselves are rounded (see result_bits16)
+    if (fmt == kBF16) {
+        reinterpret_cast<bf16x4 *>(base)[q] = to_bf16x4(x);
+    } else {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        reinterpret_cast<f16x4 *>(base)[q] = f16x4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    }
+}
+
 // ---------------------------------------------------------------- grouped-query reduction
 // Item i of a ReduceJob (fab_launch.h): the sum of the rk2 partials of a group
 // (one per head unit) of one float4 (or float) of a key/value head's dK or dV
@@ -335,13 +392,13 @@ __device__ __forceinline__ void reduce_item(const ReduceJob &r, int rk2, int64_t
         const f32x4 *src = reinterpret_cast<const f32x4 *>(r.part) + gb * rk2 * c4 + off;
         f32x4 s = src[0];
         for (int k = 1; k < rk2; ++k) s += src[k * c4];
-        reinterpret_cast<f32x4 *>(r.dst)[i] = s;
+        store_result4(r.dst, (size_t)i, s, r.out_fmt);
     } else {
         const int64_t gb = i / r.chunk, off = i - gb * r.chunk;
         const float *src = r.part + gb * rk2 * r.chunk + off;
         float s = src[0];
         for (int k = 1; k < rk2; ++k) s += src[k * r.chunk];
-        r.dst[i] = s;
+        store_result(r.dst, (size_t)i, s, r.out_fmt);
     }
 }
 

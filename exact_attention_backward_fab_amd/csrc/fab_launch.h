@@ -18,6 +18,7 @@ struct Dims {
     int causal = 0;   // the mask is the causal rule (key m seen by query n iff m <= n), given as a flag
     int in_fmt = 0;   // storage of q, k, v and d: kF32, kBF16 or kF16 (the 16-bit forms in bf16 mode only)
     int o_bf16 = 0;   // O is bf16 (bf16 mode only): written so by the forward, read so by the prep
+    int out_fmt = 0;  // element type of the result blob: kF32, or kBF16 / kF16 (bf16 mode only)
     const float *alibi = nullptr;   // per-query-head ALiBi slopes [H] (device) or NULL: score += slope_h (m - n)
 };
 
@@ -249,7 +250,8 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
 // are float4 (chunk % 4 == 0) or single floats, numbered over all groups.
 struct ReduceJob {
     const float *part;
-    float *dst;
+    float *dst;      // elements of out_fmt (the result blob) or f32
+    int out_fmt;
     int64_t chunk;   // floats of one head's slice (D * M)
     int vec;         // chunk % 4 == 0: float4 items
     int64_t items;   // work items (float4 or float) over all groups
@@ -265,6 +267,7 @@ inline int gqa_reduce_jobs(const float *pk, float *dk, const float *pv, float *d
     for (int t = 0; t < 2; ++t) {
         j[t].part = part[t];
         j[t].dst = dst[t];
+        j[t].out_fmt = d.out_fmt;
         j[t].chunk = (int64_t)D[t] * d.M;
         j[t].vec = (j[t].chunk % 4 == 0);
         j[t].items = (j[t].vec ? j[t].chunk / 4 : j[t].chunk) * groups;

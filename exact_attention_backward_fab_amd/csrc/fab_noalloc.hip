@@ -51,7 +51,7 @@ extern "C" {
 
 int fab_backward_noalloc(const fab_shape *shape, const void *q, const void *k, const void *v,
                          const uint16_t *mask, const void *d, float scale, int mode, const void *O,
-                         const float *lse, float *blob, void *stream)
+                         const float *lse, void *blob, void *stream)
 {
     // shape and mode first (host only): the workspace this call needs
     size_t need = 0;

@@ -320,7 +320,7 @@ struct FwdArgs16 {
     __bf16 *q16, *o16;              // tiles [B,H,Np,DKP] / [B,H,Np,DVP]
     float *stats;                   // [B,H,Np/64][128]
     float *blob;
-    int64_t pad_lo[3], pad_hi[3];
+    int64_t pad_lo[3], pad_hi[3];   // the blob's pads, in 16-bit units (zero in every element type)
     int *zero;
     int nzero, Np;
     int fold;                       // the whole grid is resident at once (query_block_work)
@@ -367,9 +367,9 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
                 *reinterpret_cast<bf16x8 *>(qt16 + tile_elem(myq, 16 * t + 8 * half, DKP)) = qf[t];
         }
         for (int i = blockIdx.x * kQNT + tid; i < p.nzero; i += gridDim.x * kQNT) p.zero[i] = 0;
-        if (blockIdx.x == 0 && tid < 4)
+        if (blockIdx.x == 0 && tid < 8)   // pads below 16 bytes: at most 7 16-bit units
             for (int k = 0; k < 3; ++k)
-                if (p.pad_lo[k] + tid < p.pad_hi[k]) p.blob[p.pad_lo[k] + tid] = 0.f;
+                if (p.pad_lo[k] + tid < p.pad_hi[k]) reinterpret_cast<uint16_t *>(p.blob)[p.pad_lo[k] + tid] = 0;
     }
     f32x16 oacc[DVP / 32];
 #pragma unroll
@@ -517,7 +517,8 @@ struct DqArgs {
     const __bf16 *k16, *v16;        // bf16 tiles [B,Hkv,Mp,DKP] / [B,Hkv,Mp,DVP], rows >= M zero
     const uint16_t *mask;
     const uint8_t *map;
-    float *dq;                      // [DK,N,H,B] slice of the result blob
+    float *dq;                      // [DK,N,H,B] slice of the result blob (out_fmt elements)
+    int out_fmt;
     float *part;                    // split == 2: per-share dQ partials [blocks][2][4 waves][DKP/2 * 64]
     int *ticket;                    // split == 2: one zeroed counter per query block
     int B, H, Hkv, N, Np, M, Mp, DK, DV, nqb, nkb;
@@ -654,17 +655,20 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP>::Occ, QStages<DKP, DVP>::Oc
     }
 
     // ---- store dQ (scaled): lane = head-dim column, rows = this wave's queries
-    float *dqh = p.dq + hrow * p.DK;
+    const size_t dq0 = hrow * p.DK;   // this head's dQ rows in the result slice (out_fmt elements)
+    with_result_width(p.out_fmt, [&](auto w16) {
+        constexpr bool W16 = decltype(w16)::value;
 #pragma unroll
-    for (int dt = 0; dt < DKP / 32; ++dt) {
-        const int col = dt * 32 + l32;
-        if (col < p.DK)
+        for (int dt = 0; dt < DKP / 32; ++dt) {
+            const int col = dt * 32 + l32;
+            if (col < p.DK)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = q0 + 32 * w + crow(r, half);
-                if (n < p.N) dqh[(size_t)n * p.DK + col] = dqacc[dt][r] * p.scale;
-            }
-    }
+                for (int r = 0; r < 16; ++r) {
+                    const int n = q0 + 32 * w + crow(r, half);
+                    if (n < p.N) store_as<W16>(p.dq, dq0 + (size_t)n * p.DK + col, dqacc[dt][r] * p.scale, p.out_fmt);
+                }
+        }
+    });
 }
 
 // ============================================================== dQ from the stored dS
@@ -681,7 +685,8 @@ struct DqsArgs {
     const __bf16 *ds;               // dS^T tiles [B,H,ceil(Np/128),nkb128][2 key tiles][2 query steps][64 x 64]
     const __bf16 *k16;              // bf16 tiles [B,Hkv,Mp,DKP], rows >= M zero
     const uint8_t *map;
-    float *dq;                      // [DK,N,H,B] slice of the result blob
+    float *dq;                      // [DK,N,H,B] slice of the result blob (out_fmt elements)
+    int out_fmt;
     int B, H, Hkv, N, Np, M, Mp, DK, nqb, nkb, nkb128;
     int causal;                     // causal rule as a flag (no mask, no map)
     int fold;                       // the whole grid is resident at once (query_block_work)
@@ -819,17 +824,20 @@ void dq_ds_kernel(DqsArgs p)
 
     // ---- store dQ (scaled): lane = head-dim column, slot r = query column
     // crow(r, half) of this wave's 32, in the dS^T column order (ds_query)
-    float *dqh = p.dq + (size_t)p.N * p.DK * hb;
+    const size_t dq0 = (size_t)p.N * p.DK * hb;   // this head's dQ rows in the result slice (out_fmt elements)
+    with_result_width(p.out_fmt, [&](auto w16) {
+        constexpr bool W16 = decltype(w16)::value;
 #pragma unroll
-    for (int j = 0; j < DT; ++j) {
-        const int col = (2 * j + dh) * 32 + l32;
-        if (2 * j + dh < NDT && col < p.DK)
+        for (int j = 0; j < DT; ++j) {
+            const int col = (2 * j + dh) * 32 + l32;
+            if (2 * j + dh < NDT && col < p.DK)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = (it0 + sw) * kTR + ds_query(32 * qh + crow(r, half));
-                if (n < p.N) dqh[(size_t)n * p.DK + col] = acc[j][r] * p.scale;
-            }
-    }
+                for (int r = 0; r < 16; ++r) {
+                    const int n = (it0 + sw) * kTR + ds_query(32 * qh + crow(r, half));
+                    if (n < p.N) store_as<W16>(p.dq, dq0 + (size_t)n * p.DK + col, acc[j][r] * p.scale, p.out_fmt);
+                }
+        }
+    });
 }
 
 namespace {
@@ -942,9 +950,10 @@ hipError_t launch_forward_prep_bf16(const void *q, const __bf16 *k16, const __bf
     a.vecK = (d.DK % 4 == 0); a.vecV = (d.DV % 4 == 0); a.in_fmt = d.in_fmt;
     a.scale = scale;
     a.dO = dO; a.q16 = q16; a.o16 = o16; a.stats = stats; a.blob = blob;
-    a.pad_lo[0] = nq; a.pad_hi[0] = off_k;
-    a.pad_lo[1] = off_k + nk; a.pad_hi[1] = off_v;
-    a.pad_lo[2] = off_v + nv; a.pad_hi[2] = total;
+    const int u = d.out_fmt == kF32 ? 2 : 1;   // 16-bit units per blob element
+    a.pad_lo[0] = u * nq; a.pad_hi[0] = u * off_k;
+    a.pad_lo[1] = u * (off_k + nk); a.pad_hi[1] = u * off_v;
+    a.pad_lo[2] = u * (off_v + nv); a.pad_hi[2] = u * total;
     a.zero = zero; a.nzero = nzero; a.Np = Np;
     FAB_DISPATCH_HEAD_DIMS(run_fwd16, a, s, hd, true);
 }
@@ -958,7 +967,7 @@ hipError_t launch_dq(const __bf16 *q16, const __bf16 *o16, const float *stats, c
     if (!pick_head_dims(d.DK, d.DV, &hd)) return hipErrorInvalidValue;
     DqArgs a;
     a.q16 = q16; a.o16 = o16; a.stats = stats; a.k16 = k16; a.v16 = v16; a.mask = mask; a.map = map;
-    a.dq = dq; a.part = part; a.ticket = ticket; a.split = dq_split(d);
+    a.dq = dq; a.out_fmt = d.out_fmt; a.part = part; a.ticket = ticket; a.split = dq_split(d);
     if (a.split == 2 && (!part || !ticket)) return hipErrorInvalidValue;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK; a.DV = d.DV;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.causal = d.causal; a.alibi = d.alibi;
@@ -973,7 +982,7 @@ hipError_t launch_dq_from_ds(const __bf16 *ds, const __bf16 *k16, const uint8_t 
     HeadDims hd;
     if (!pick_head_dims(d.DK, d.DV, &hd) || !ds || !dq_from_ds(d, Np, hd.dk, hd.dv)) return hipErrorInvalidValue;
     DqsArgs a;
-    a.ds = ds; a.k16 = k16; a.map = map; a.dq = dq;
+    a.ds = ds; a.k16 = k16; a.map = map; a.dq = dq; a.out_fmt = d.out_fmt;
     a.B = d.B; a.H = d.H; a.Hkv = d.Hkv; a.N = d.N; a.Np = Np; a.M = d.M; a.Mp = Mp; a.DK = d.DK;
     a.nqb = ceil_div(d.N, kMapTile); a.nkb = ceil_div(d.M, kMapTile); a.nkb128 = ceil_div(d.M, 128);
     a.causal = d.causal;

@@ -32,7 +32,8 @@
  *     off_q = 0, off_k = pad4(nq), off_v = off_k + pad4(nk), total = off_v + pad4(nv)
  * in floats, where nq, nk, nv are the element counts of q, k, v and
  * pad4(x) = ceil(x/4)*4 (16-byte alignment).  Every float of the blob is
- * written; the pads are zero.
+ * written; the pads are zero.  A 16-bit blob (FAB_BF16_BLOB, FAB_F16_BLOB) has
+ * the same order with pad8 in 16-bit elements (fab_blob_layout16).
  *
  * Ownership and threading: the caller allocates and owns every buffer (inputs,
  * outputs, workspace).  The compute entry points never allocate, free or
@@ -110,6 +111,21 @@ typedef enum fab_mode { FAB_MODE_F32 = 0, FAB_MODE_BF16 = 1 } fab_mode;
  * otherwise); O (unless FAB_BF16_O), lse and the blob stay f32. */
 #define FAB_F16_INPUTS 0x800
 
+/* Flags OR-ed into the mode argument of fab_backward (and its ALiBi and
+ * allocation-free forms) and fab_workspace_bytes: the result blob holds bf16
+ * (FAB_BF16_BLOB) or IEEE f16 (FAB_F16_BLOB) elements instead of f32 -- each the
+ * f32 gradient the kernels accumulate, rounded to nearest even once at the
+ * store (half-precision storage of gradients, as the ggmlR package description on
+ * its ggml_flash_attn_back page names half precision among the package's features).
+ * The blob then follows fab_blob_layout16: the same [dQ | pad | dK | pad | dV |
+ * pad] order with each slice padded to 16 bytes (8 elements), pads zero.  Every
+ * accumulation, including the grouped-query sums of dK and dV, stays f32, so the
+ * 16-bit blob is element for element the rounding of the f32 blob.  The
+ * workspace is unchanged.  FAB_MODE_BF16 only, exclusive of each other, and
+ * FAB_E_INVAL in fab_forward_lse (which writes no blob). */
+#define FAB_BF16_BLOB 0x1000
+#define FAB_F16_BLOB 0x2000
+
 typedef enum fab_status {
     FAB_OK = 0,
     FAB_E_INVAL = -1,        /* bad shape, NULL pointer, bad scale or mode */
@@ -123,6 +139,12 @@ typedef enum fab_status {
  * Returns FAB_OK or FAB_E_INVAL. */
 int fab_blob_layout(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int64_t *off_v,
                     int64_t *total_floats);
+
+/* Host only.  The same for a 16-bit blob (FAB_BF16_BLOB, FAB_F16_BLOB):
+ * offsets and total length in 16-bit elements, each slice padded to a multiple
+ * of 8 elements.  Returns FAB_OK or FAB_E_INVAL. */
+int fab_blob_layout16(const fab_shape *shape, int64_t *off_q, int64_t *off_k, int64_t *off_v,
+                      int64_t *total_elems);
 
 /* Host only.  Workspace bytes that fab_forward_lse (have_o_lse ignored) or
  * fab_backward need for this shape, mode and mask presence.  have_o_lse != 0
@@ -161,12 +183,14 @@ int fab_forward_lse(const fab_shape *shape, const void *q, const void *k, const 
  *             pages' semantics) or both given: the output and row LSE of the
  *             same forward (as written by fab_forward_lse; O f32, or bf16 with
  *             FAB_BF16_O); exactly one NULL is FAB_E_INVAL
- *   blob      device f32, total_floats of fab_blob_layout (written in full)
+ *   blob      device f32, total_floats of fab_blob_layout (written in full); with
+ *             FAB_BF16_BLOB / FAB_F16_BLOB 16-bit elements, total_elems of
+ *             fab_blob_layout16
  *   ws        device workspace, ws_bytes >= fab_workspace_bytes(.., have_o_lse)
  *   stream    hipStream_t of the caller */
 int fab_backward(const fab_shape *shape, const void *q, const void *k, const void *v,
                  const uint16_t *mask, const void *d, float scale, int mode, const void *O,
-                 const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
+                 const float *lse, void *blob, void *ws, size_t ws_bytes, void *stream);
 
 /* ALiBi: fab_forward_lse and fab_backward with a linear per-head bias on the
  * scores.  The ggmlR test file names ALiBi only through `max_bias`, in its block
@@ -187,7 +211,7 @@ int fab_forward_lse_alibi(const fab_shape *shape, const void *q, const void *k, 
                           void *ws, size_t ws_bytes, void *stream);
 int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, const void *v,
                        const uint16_t *mask, const float *alibi, const void *d, float scale, int mode,
-                       const void *O, const float *lse, float *blob, void *ws, size_t ws_bytes, void *stream);
+                       const void *O, const float *lse, void *blob, void *ws, size_t ws_bytes, void *stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: fab_backward
@@ -209,7 +233,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
 #define FAB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int fab_backward_noalloc(const fab_shape *shape, const void *q, const void *k, const void *v,
                          const uint16_t *mask, const void *d, float scale, int mode, const void *O,
-                         const float *lse, float *blob, void *stream);
+                         const float *lse, void *blob, void *stream);
 
 /* Measurement hooks (they compute nothing).  While enabled, every kernel
  * launch made by fab_forward_lse and fab_backward is bracketed by a pair of

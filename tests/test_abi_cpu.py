@@ -9,6 +9,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import exact_attention_backward_fab_amd as fab
 
@@ -77,6 +78,49 @@ def test_blob_layout_matches_the_pages_padding(shape):
     assert fab.blob_layout(s) == (0, pad(nq), pad(nq) + pad(nk), pad(nq) + pad(nk) + pad(nv))
 
 
+@pytest.mark.parametrize("shape", [
+    fab.Shape(2, 4, 2, 2, 4, 3, 5), fab.Shape(1, 2, 1, 3, 5, 3, 5), fab.Shape(1, 1, 1, 1, 1, 1, 1),
+    fab.Shape(1, 32, 8, 2048, 2048, 128, 128), fab.Shape(1, 3, 3, 7, 9, 5, 3),
+    fab.Shape(0, 2, 1, 3, 5, 3, 5), fab.Shape(1, 2, 1, 0, 5, 3, 5)])
+def test_blob_layout16_pads_each_slice_to_16_bytes(shape):
+    """A 16-bit blob keeps the [dQ | pad | dK | pad | dV | pad] order with each slice
+    padded to 16 bytes = 8 elements."""
+    s = shape
+    nq, nk, nv = s.DK * s.N * s.H * s.B, s.DK * s.M * s.Hkv * s.B, s.DV * s.M * s.Hkv * s.B
+    pad8 = lambda n: -(-n // 8) * 8
+    want = (0, pad8(nq), pad8(nq) + pad8(nk), pad8(nq) + pad8(nk) + pad8(nv))
+    assert fab.blob_layout(s, torch.bfloat16) == want
+    assert fab.blob_layout(s, torch.float16) == want
+    assert fab.blob_layout(s, torch.float32) == fab.blob_layout(s)
+    o = [ctypes.c_int64() for _ in range(4)]
+    assert fab.lib().fab_blob_layout16(ctypes.byref(s.c()), *[ctypes.byref(x) for x in o]) == fab.FAB_OK
+    assert tuple(x.value for x in o) == want
+    with pytest.raises(TypeError):
+        fab.blob_layout(s, torch.int32)
+
+
+def test_blob_flags_change_no_workspace_and_stay_out_of_the_forward():
+    s = fab.Shape(1, 8, 2, 300, 400, 64, 64)
+    L = fab.lib()
+    for has_mask in (0, 1):
+        for have in (0, 1):
+            base = fab.workspace_bytes(s, "bf16", has_mask, have)
+            for flag in (fab.FAB_BF16_BLOB, fab.FAB_F16_BLOB):
+                n = ctypes.c_size_t()
+                assert L.fab_workspace_bytes(ctypes.byref(s.c()), fab.FAB_MODE_BF16 | flag, has_mask, have,
+                                             ctypes.byref(n)) == fab.FAB_OK
+                assert n.value == base
+    n = ctypes.c_size_t()
+    assert L.fab_workspace_bytes(ctypes.byref(s.c()), fab.FAB_MODE_F32 | fab.FAB_BF16_BLOB, 0, 0,
+                                 ctypes.byref(n)) == fab.FAB_E_INVAL
+    P = ctypes.c_void_p
+    sh = fab.FabShape(*GOOD)
+    for flag in (fab.FAB_BF16_BLOB, fab.FAB_F16_BLOB):
+        rc = L.fab_forward_lse(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), None, 0.5, fab.FAB_MODE_BF16 | flag,
+                               P(FAKE), P(FAKE), P(FAKE), 1 << 40, None)
+        assert rc == fab.FAB_E_INVAL and "backward" in L.fab_last_error().decode()
+
+
 def test_workspace_grows_with_what_must_be_recomputed():
     s = fab.Shape(1, 8, 2, 300, 400, 64, 64)
     base = fab.workspace_bytes(s, "bf16", False, True)
@@ -132,7 +176,11 @@ GOOD = (1, 4, 2, 8, 8, 16, 16)
     (GOOD, {"ws": None}, fab.FAB_E_WORKSPACE),
     (GOOD, {"ws_bytes": 16}, fab.FAB_E_WORKSPACE),
     (GOOD, {"mode": fab.FAB_CAUSAL, "mask": FAKE}, fab.FAB_E_INVAL),         # mask and causal flag
-    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x1000}, fab.FAB_E_INVAL),          # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | 0x4000}, fab.FAB_E_INVAL),          # unknown flag bit
+    (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_BF16_BLOB}, fab.FAB_E_INVAL),   # 16-bit blob needs bf16 mode
+    (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_F16_BLOB}, fab.FAB_E_INVAL),
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | fab.FAB_BF16_BLOB | fab.FAB_F16_BLOB}, fab.FAB_E_INVAL),  # one blob type
+    (GOOD, {"mode": fab.FAB_MODE_BF16 | fab.FAB_F16_BLOB, "blob": FAKE + 8}, fab.FAB_E_ALIGN),  # 16-byte aligned
     (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_F16_INPUTS}, fab.FAB_E_INVAL),   # f16 inputs need bf16 mode
     (GOOD, {"mode": fab.FAB_MODE_BF16 | fab.FAB_F16_INPUTS | fab.FAB_BF16_INPUTS}, fab.FAB_E_INVAL),  # one input storage
     (GOOD, {"mode": fab.FAB_MODE_F32 | fab.FAB_BF16_O, "O": FAKE, "lse": FAKE}, fab.FAB_E_INVAL),  # bf16 O needs bf16 mode
