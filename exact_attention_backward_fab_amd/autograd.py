@@ -9,9 +9,16 @@ arithmetic runs in the library's kernels.
 
     O = attention(q, k, v, mask=None, scale=None, mode="f32", causal=False, alibi=None)
 
-q (B,H,N,DK), k (B,Hkv,M,DK), v (B,Hkv,M,DV) float32 CUDA tensors, mask (N,M)
-f16 bit patterns or None, alibi (H,) float32 per-head slopes or None, O (B,N,H,DV).
+q (B,H,N,DK), k (B,Hkv,M,DK), v (B,Hkv,M,DV) CUDA tensors, mask (N,M) f16 bit
+patterns or None, alibi (H,) float32 per-head slopes or None, O (B,N,H,DV).
 No gradient flows to the mask or the slopes.
+
+float32 inputs give a float32 O and float32 gradients (any mode).  bfloat16 inputs
+(mode "bf16") stay bfloat16 end to end: O is stored as bf16 (FAB_BF16_O, the f32
+output rounded to nearest even), so the upstream gradient arrives as bf16 and is
+read as such (FAB_BF16_INPUTS), and the gradients are bf16 views of one bf16 blob
+(FAB_BF16_BLOB: the f32 gradients rounded once).  float16 inputs are refused: the
+library stores O as f32 or bf16 only, so their upstream gradient would not be f16.
 """
 from __future__ import annotations
 
@@ -28,7 +35,11 @@ class FabAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, mask, scale, mode, causal, alibi):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        O, lse = _forward_lse(q, k, v, scale, mask=mask, mode=mode, causal=causal, alibi=alibi)
+        if q.dtype == torch.float16:
+            raise TypeError("attention(): float16 inputs are not supported (O is stored as f32 or bf16, so the "
+                            "upstream gradient would not be f16); call fab.backward with f16 q, k, v, d directly")
+        O, lse = _forward_lse(q, k, v, scale, mask=mask, mode=mode, causal=causal, alibi=alibi,
+                              o_bf16=q.dtype == torch.bfloat16)
         ctx.save_for_backward(q, k, v, O, lse)
         ctx.mask, ctx.scale, ctx.mode, ctx.causal, ctx.alibi = mask, scale, mode, causal, alibi
         return O
@@ -36,8 +47,9 @@ class FabAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dO):
         q, k, v, O, lse = ctx.saved_tensors
-        blob = _backward(q, k, v, dO.contiguous(), ctx.scale, mask=ctx.mask, mode=ctx.mode, O=O, lse=lse,
-                         causal=ctx.causal, alibi=ctx.alibi)
+        # bf16 inputs: dO (the gradient of a bf16 O) is bf16 too, and so is the blob
+        blob = _backward(q, k, v, dO.to(q.dtype).contiguous(), ctx.scale, mask=ctx.mask, mode=ctx.mode, O=O,
+                         lse=lse, causal=ctx.causal, alibi=ctx.alibi, blob_dtype=q.dtype)
         dq, dk, dv = unpack(blob, shape_of(q, k, v))
         return dq, dk, dv, None, None, None, None, None
 

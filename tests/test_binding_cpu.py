@@ -91,3 +91,10 @@ def test_float16_inputs_pass_the_checks_and_set_the_flag():
     assert fab._mode("bf16", False, torch.float16) == fab.FAB_MODE_BF16 | fab.FAB_F16_INPUTS
     assert fab._mode("bf16", True, torch.bfloat16) == fab.FAB_MODE_BF16 | fab.FAB_CAUSAL | fab.FAB_BF16_INPUTS
     assert fab._mode("f32", False, torch.float32) == fab.FAB_MODE_F32
+
+
+def test_autograd_refuses_float16_inputs():
+    from exact_attention_backward_fab_amd.autograd import attention
+    q, k, v, _ = inputs(torch.float16)
+    with pytest.raises(TypeError, match="float16"):
+        attention(q, k, v, mode="bf16")

@@ -235,3 +235,32 @@ def test_16bit_blob_unpacks_and_passes_through_noalloc(torch_dev):
     for x16, x32 in zip(fab.unpack(a, fs), fab.unpack(f, fs)):
         assert x16.dtype == torch.float16 and x16.shape == x32.shape
         assert torch.equal(x16.view(torch.int16), x32.to(torch.float16).view(torch.int16))
+
+
+def test_bf16_autograd_stays_bf16_end_to_end(torch_dev):
+    """attention() on bfloat16 inputs: O is the bf16-stored forward output, and the
+    gradients are bf16 views of one bf16 blob at its 16-bit offsets, bit for bit the
+    direct calls (forward with FAB_BF16_O, backward with bf16 d and FAB_BF16_BLOB)."""
+    torch, dev = torch_dev
+    fab = fabmod()
+    from exact_attention_backward_fab_amd.autograd import attention
+    s = Shape(2, 4, 2, 150, 170, 64, 48)
+    fs = fab.Shape(*s.astuple())
+    q, k, v, d = make_qkvd(s, 102)
+    mask = random_mask(s.N, s.M, 102, p_inf=0.3, full_rows=1, full_cols=1)
+    tm = to_dev(torch, dev, mask)
+    t = [to_dev(torch, dev, x).to(torch.bfloat16) for x in (q, k, v, d)]
+    tq, tk, tv = [x.clone().requires_grad_(True) for x in t[:3]]
+    O = attention(tq, tk, tv, mask=tm, scale=0.125, mode="bf16")
+    assert O.dtype == torch.bfloat16
+    gq, gk, gv = torch.autograd.grad(O, (tq, tk, tv), grad_outputs=t[3])
+    O_ref, lse_ref = fab.forward_lse(t[0], t[1], t[2], 0.125, mask=tm, mode="bf16", o_bf16=True)
+    blob = fab.backward(*t, 0.125, mask=tm, mode="bf16", O=O_ref, lse=lse_ref, blob_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
+    base = gq.untyped_storage().data_ptr()
+    assert gk.untyped_storage().data_ptr() == base and gv.untyped_storage().data_ptr() == base
+    _, off_k, off_v, _ = fab.blob_layout(fs, torch.bfloat16)
+    assert (gq.storage_offset(), gk.storage_offset(), gv.storage_offset()) == (0, off_k, off_v)
+    for g, r in zip((gq, gk, gv), fab.unpack(blob, fs)):
+        assert g.dtype == torch.bfloat16 and torch.equal(g.view(torch.int16), r.view(torch.int16))
