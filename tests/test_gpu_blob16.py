@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2      # the bf16-mode bar of the oracle parity tests (max|err| / max|ref|)
 GUARD = 64           # elements after the blob that must stay untouched
-SENTINEL = 0x7E55    # a 16-bit pattern the kernels never write (a NaN in both formats)
+SENTINEL = 0x7FC1    # a 16-bit pattern the kernels never write (a NaN in both formats)
 
 
 @pytest.fixture(scope="module")
