@@ -324,6 +324,8 @@ def backward(q, k, v, d, scale, mask=None, mode="f32", O=None, lse=None, blob=No
         _check_tensor(O, "O", (s.B, s.N, s.H, s.DV), (torch.float32, torch.bfloat16))
         _check_tensor(lse, "lse", (s.B, s.H, s.N))
         o_bf16 = O.dtype == torch.bfloat16
+    if blob is not None and blob_dtype is not None and blob.dtype != blob_dtype:
+        raise TypeError(f"blob is {blob.dtype} but blob_dtype is {blob_dtype}")
     bdt = blob.dtype if blob is not None else (blob_dtype or torch.float32)
     total = blob_layout(s, bdt)[3]
     if blob is not None:

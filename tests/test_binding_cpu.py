@@ -41,6 +41,7 @@ BAD = [
     ("blob_dtype", dict(blob=torch.zeros(10_000, dtype=torch.float64)), TypeError, "blob"),
     ("blob16_short", dict(blob=torch.zeros(16, dtype=torch.bfloat16)), ValueError, "blob"),
     ("blob_dtype_arg", dict(blob_dtype=torch.int32), TypeError, "blob"),
+    ("blob_dtype_mismatch", dict(blob=torch.zeros(10_000), blob_dtype=torch.bfloat16), TypeError, "blob"),
     ("blob_strided", dict(blob=torch.zeros(20_000)[::2]), ValueError, "blob"),
     ("ws_strided", dict(ws=torch.zeros(1 << 20, dtype=torch.uint8)[::2]), ValueError, "ws"),
     ("ws_short", dict(ws=torch.zeros(16, dtype=torch.uint8)), ValueError, "ws"),
