@@ -766,8 +766,8 @@ void dq_ds_kernel(DqsArgs p)
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = (i * kDsW + w) % ST::kCols;
-            if (c < 16)
-                lds_copy16(rs, stg + c * kChunkL, (uint32_t)(ss * 16 + c) * kChunkG + (uint32_t)lane * 16u);
+            if (c < 16)   // dS^T: read once, streamed (the K tiles are reused across heads and blocks)
+                lds_copy16<true>(rs, stg + c * kChunkL, (uint32_t)(ss * 16 + c) * kChunkG + (uint32_t)lane * 16u);
             else
                 lds_copy16(rk, stg + (c - 16 + 16) * kChunkL,
                            (uint32_t)(ss * (DKP / 8) + c - 16) * kChunkG + (uint32_t)lane * 16u);

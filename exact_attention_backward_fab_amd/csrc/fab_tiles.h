@@ -66,12 +66,20 @@ __device__ __forceinline__ bf16x8 lds_tr8(const char *p)
 // wait state later, at issue) and restores it, so whatever the compiler keeps in
 // m0 is unchanged across the statement and m0 is not a clobber.  The asm writes no
 // VGPR (the data goes to LDS), so no register is left pending on the load.
+// NT: the non-temporal policy, for data read once (it streams past the L2 instead
+// of displacing lines that other reads reuse).
+template <bool NT = false>
 __device__ __forceinline__ void lds_copy16(rsrc_t r, uint32_t la, uint32_t voff)
 {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(la), "v"(voff), "s"(r) : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "s"(la), "v"(voff), "s"(r) : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "s"(la), "v"(voff), "s"(r) : "memory");
 }
 
 // Waits until at most k * PER of this wave's vector-memory operations are in flight.
