@@ -86,11 +86,37 @@ def mask_of(kind, s, seed):
 @pytest.mark.parametrize("name,s,mkind,seed,mode,inputs,supplied,o16,blob,alibi", CASES, ids=[c[0] for c in CASES])
 def test_random_configuration_against_full_oracle(torch_dev, name, s, mkind, seed, mode, inputs, supplied, o16,
                                                   blob, alibi):
+    run_case(torch_dev, name, s, mkind, seed, mode, inputs, supplied, o16, blob, alibi)
+
+
+SHARED = CASES[::4]
+
+
+@pytest.fixture(scope="module")
+def dirty_workspace(torch_dev):
+    """One workspace for every case below, large enough for each, all bytes 0xFF (NaN
+    patterns) at the start and left as each call leaves it for the next."""
+    torch, dev = torch_dev
+    import exact_attention_backward_fab_amd as fab
+    need = max(fab.workspace_bytes(fab.Shape(*c[1].astuple()), c[4], c[2] not in ("none", "causal_flag"), c[6],
+                                   c[2] == "causal_flag") for c in SHARED)
+    return torch.full((need + 256,), 255, dtype=torch.uint8, device=dev)
+
+
+@pytest.mark.parametrize("name,s,mkind,seed,mode,inputs,supplied,o16,blob,alibi", SHARED, ids=[c[0] for c in SHARED])
+def test_random_configuration_in_a_shared_dirty_workspace(torch_dev, dirty_workspace, name, s, mkind, seed, mode,
+                                                          inputs, supplied, o16, blob, alibi):
+    # every call writes each workspace byte it reads: a workspace that an earlier call of
+    # another shape (or the initial NaN fill) left behind changes nothing
+    run_case(torch_dev, name, s, mkind, seed, mode, inputs, supplied, o16, blob, alibi, ws=dirty_workspace)
+
+
+def run_case(torch_dev, name, s, mkind, seed, mode, inputs, supplied, o16, blob, alibi, ws=None):
     torch, dev = torch_dev
     import exact_attention_backward_fab_amd as fab
     from oracle import oracle as orc
     print(f"[sweep] {name} {s} mask={mkind} mode={mode} inputs={inputs} supplied={supplied} o16={o16} "
-          f"blob={blob} alibi={alibi}", flush=True)
+          f"blob={blob} alibi={alibi} shared_ws={ws is not None}", flush=True)
     q, k, v, d = make_qkvd(s, seed)
     mask = mask_of(mkind, s, seed)
     causal = mkind == "causal_flag"
@@ -110,7 +136,7 @@ def test_random_configuration_against_full_oracle(torch_dev, name, s, mkind, see
     sentinel = 0x7FC0DEAD if blob == "f32" else 0x7FC1
     raw = torch.full((total + 64,), sentinel, dtype=torch.int32 if blob == "f32" else torch.int16, device=dev)
     out = raw.view(bdt)
-    fab.backward(*t, scale, mask=tm, mode=mode, O=O, lse=lse, causal=causal, alibi=ta, blob=out)
+    fab.backward(*t, scale, mask=tm, mode=mode, O=O, lse=lse, causal=causal, alibi=ta, blob=out, ws=ws)
     torch.cuda.synchronize()
     bits = raw.cpu().numpy()
     assert np.all(bits[total:] == sentinel), f"{name}: write past the end of the blob"
