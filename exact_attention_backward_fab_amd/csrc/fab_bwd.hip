@@ -713,7 +713,13 @@ template <int DKP, int DVP>
 struct F32Cfg {
     static constexpr int KW = (DKP + DVP <= 128) ? 4 : (DKP + DVP <= 384) ? 2 : 1;
     static constexpr int QH = (DKP + DVP == 256) ? 2 : 1;
-    static constexpr int W = KW * QH;
+    // column split: where KW x QH waves would leave SIMDs of the CU idle (the wide
+    // heads, whose K, V, Q and dO rows fill the LDS for one work-group), CS waves share
+    // each (key sub-block, query half): each forms the same S and dP and owns 1/CS of
+    // the dK and dV column tiles, so all four SIMDs multiply
+    static constexpr int CS = KW * QH >= 4 ? 1 : 4 / (KW * QH);
+    static_assert((DKP / 32) % CS == 0 && (DVP / 32) % CS == 0, "column split");
+    static constexpr int W = KW * QH * CS;
     static constexpr int NT = 64 * W;
     static constexpr int BC = 32 * KW;  // keys per work-group
     static_assert(BC == f32_keys_per_wg(DKP, DVP), "f32 key block");
@@ -725,7 +731,8 @@ template <int DKP, int DVP, bool AB>
 __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdArgs p)
 {
     using C = F32Cfg<DKP, DVP>;
-    constexpr int BC = C::BC, BR = C::BR, W = C::W, NT = C::NT, KW = C::KW, QH = C::QH;
+    constexpr int BC = C::BC, BR = C::BR, W = C::W, NT = C::NT, KW = C::KW, QH = C::QH, CS = C::CS;
+    constexpr int NKT = DKP / 32 / CS, NVT = DVP / 32 / CS;   // dK, dV column tiles of a wave
     constexpr int LK = C::LK, LV = C::LV, LQ = C::LQ, LO = C::LO, LS = C::LS;
     __shared__ __attribute__((aligned(16))) float sK[BC * LK];
     __shared__ __attribute__((aligned(16))) float sV[BC * LV];
@@ -736,7 +743,8 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     __shared__ __attribute__((aligned(16))) float sD[BR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-    const int kw = QH == 1 ? w : w % KW, qq = QH == 1 ? 0 : w / KW;   // key sub-block, query half
+    const int wl = w % (KW * QH), cs = w / (KW * QH);                  // (key sub-block, query half), column part
+    const int kw = QH == 1 ? wl : wl % KW, qq = QH == 1 ? 0 : wl / KW;   // key sub-block, query half
     const int HB = p.H * p.B, qs = p.qsplit;
     const int split = blockIdx.x % qs, jhb = blockIdx.x / qs;   // this work-group takes live steps split, split + qs, ...
     const int j = jhb / HB, hb = jhb % HB;
@@ -765,11 +773,11 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             key < p.M ? load_row4(vh + (size_t)p.DV * key, col, p.DV, p.vecV) : z;
     }
 
-    f32x16 dkacc[DKP / 32], dvacc[DVP / 32];
+    f32x16 dkacc[NKT], dvacc[NVT];
 #pragma unroll
-    for (int i = 0; i < DKP / 32; ++i) dkacc[i] = zero16();
+    for (int i = 0; i < NKT; ++i) dkacc[i] = zero16();
 #pragma unroll
-    for (int i = 0; i < DVP / 32; ++i) dvacc[i] = zero16();
+    for (int i = 0; i < NVT; ++i) dvacc[i] = zero16();
     const float sl2 = p.scale * kLog2e;
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
@@ -913,20 +921,21 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
                 pacc[r] = P * (pacc[r] - del4[c]);
             }
         }
-        // ---- dV += P^T dO, dK += dS^T Q
+        // ---- dV += P^T dO, dK += dS^T Q (this wave's column tiles)
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int qr = 32 * qq + crow(u, half);
 #pragma unroll
-            for (int dt = 0; dt < DVP / 32; ++dt)
-                dvacc[dt] = mfma_f32(sacc[u], sO[qr * LO + dt * 32 + l32], dvacc[dt]);
+            for (int dt = 0; dt < NVT; ++dt)
+                dvacc[dt] = mfma_f32(sacc[u], sO[qr * LO + (NVT * cs + dt) * 32 + l32], dvacc[dt]);
 #pragma unroll
-            for (int dt = 0; dt < DKP / 32; ++dt)
-                dkacc[dt] = mfma_f32(pacc[u], sQ[qr * LQ + dt * 32 + l32], dkacc[dt]);
+            for (int dt = 0; dt < NKT; ++dt)
+                dkacc[dt] = mfma_f32(pacc[u], sQ[qr * LQ + (NKT * cs + dt) * 32 + l32], dkacc[dt]);
         }
-        // ---- dS to LDS [query][key]
+        // ---- dS to LDS [query][key] (the column parts hold the same dS: part 0 writes it)
+        if (cs == 0)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sS[(32 * qq + crow(r, half)) * LS + 32 * kw + l32] = pacc[r];
+            for (int r = 0; r < 16; ++r) sS[(32 * qq + crow(r, half)) * LS + 32 * kw + l32] = pacc[r];
         __syncthreads();
         // ---- dQ tiles (32 queries x 32 dims), round-robin over the waves
         for (int tt = w; tt < QH * (DKP / 32); tt += W) {
@@ -954,6 +963,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     // ---- the second query half hands its dK, dV to the first through the K and V
     // rows, which are no longer read (sK holds KW x dK tiles, sV KW x dV tiles)
     if constexpr (QH == 2) {
+        static_assert(CS == 1, "query halves and column parts are not combined");
         static_assert(KW * (DKP / 32) * 1024 <= BC * LK && KW * (DVP / 32) * 1024 <= BC * LV,
                       "dK/dV exchange area");
         float *xk = sK + kw * (DKP / 32) * 1024;
@@ -985,8 +995,8 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     float *dkb = p.dk + (size_t)p.DK * p.M * (hd + Hd * b);
     float *dvb = p.dv + (size_t)p.DV * p.M * (hd + Hd * b);
 #pragma unroll
-    for (int dt = 0; dt < DKP / 32; ++dt) {
-        const int col = dt * 32 + l32;
+    for (int dt = 0; dt < NKT; ++dt) {
+        const int col = (NKT * cs + dt) * 32 + l32;
         if (col < p.DK)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -995,8 +1005,8 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
             }
     }
 #pragma unroll
-    for (int dt = 0; dt < DVP / 32; ++dt) {
-        const int col = dt * 32 + l32;
+    for (int dt = 0; dt < NVT; ++dt) {
+        const int col = (NVT * cs + dt) * 32 + l32;
         if (col < p.DV)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
