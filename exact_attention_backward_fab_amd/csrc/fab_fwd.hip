@@ -80,24 +80,71 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
     const float slope2 = AB ? p.alibi[h] * kLog2e : 0.f;   // ALiBi, log2 units
     const int nkt_total = (p.M + BC - 1) / BC;
 
-    for (int kt = 0; kt < nkt_total; ++kt) {
-        const int key0 = kt * BC;
-        const int cls = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
-                                                                 qt * (BR / kMapTile), key0 / kMapTile);
-        if (cls == kTileSkip) continue;
-        __syncthreads();
-        // ---- stage K and V rows
-        for (int c = tid; c < BC * (DKP / 4); c += NT) {
-            const int r = c / (DKP / 4), c4 = c % (DKP / 4);
-            const int key = key0 + r;
-            *reinterpret_cast<f32x4 *>(&sK[r * LK + 4 * c4]) =
-                key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
+    // Live key steps only.  Where one work-group fills the CU (the wide heads), no
+    // other work-group covers the latency of a step's K and V loads: where the
+    // registers also allow it (the 192/128 pair; wider pairs would spill), the rows of
+    // the next live step are loaded into registers while the current step computes
+    // and written to LDS at the top of the next one.
+    auto next_live = [&](int from, int *c) {
+        for (int kt = from; kt < nkt_total; ++kt) {
+            *c = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
+                                                          qt * (BR / kMapTile), kt * (BC / kMapTile));
+            if (*c != kTileSkip) return kt;
         }
-        for (int c = tid; c < BC * (DVP / 4); c += NT) {
-            const int r = c / (DVP / 4), c4 = c % (DVP / 4);
-            const int key = key0 + r;
-            *reinterpret_cast<f32x4 *>(&sV[r * LV + 4 * c4]) =
-                key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV) : f32x4{0, 0, 0, 0};
+        return nkt_total;
+    };
+    constexpr bool PF = FwdF32Occ<DKP, DVP>::v == 1 && DKP + DVP <= 320;
+    constexpr int PK = BC * (DKP / 4) / NT, PV = BC * (DVP / 4) / NT;   // float4 per thread and step
+    static_assert(!PF || (PK * NT == BC * (DKP / 4) && PV * NT == BC * (DVP / 4)), "prefetch split");
+    f32x4 pk[PF ? PK : 1], pv[PF ? PV : 1];
+    auto fetch = [&](int kt) {
+        const int k0 = kt * BC;
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int c = tid + i * NT, r = c / (DKP / 4), c4 = c % (DKP / 4), key = k0 + r;
+            pk[i] = key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int c = tid + i * NT, r = c / (DVP / 4), c4 = c % (DVP / 4), key = k0 + r;
+            pv[i] = key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV) : f32x4{0, 0, 0, 0};
+        }
+    };
+    int cls = kTileSkip;
+    int kt = next_live(0, &cls);
+    if constexpr (PF)
+        if (kt < nkt_total) fetch(kt);
+    while (kt < nkt_total) {
+        const int key0 = kt * BC;
+        int ncls = kTileSkip;
+        const int nx = next_live(kt + 1, &ncls);
+        __syncthreads();   // the previous step is done with sK, sV
+        // ---- stage K and V rows
+        if constexpr (PF) {
+#pragma unroll
+            for (int i = 0; i < PK; ++i) {
+                const int c = tid + i * NT, r = c / (DKP / 4), c4 = c % (DKP / 4);
+                *reinterpret_cast<f32x4 *>(&sK[r * LK + 4 * c4]) = pk[i];
+            }
+#pragma unroll
+            for (int i = 0; i < PV; ++i) {
+                const int c = tid + i * NT, r = c / (DVP / 4), c4 = c % (DVP / 4);
+                *reinterpret_cast<f32x4 *>(&sV[r * LV + 4 * c4]) = pv[i];
+            }
+            if (nx < nkt_total) fetch(nx);
+        } else {
+            for (int c = tid; c < BC * (DKP / 4); c += NT) {
+                const int r = c / (DKP / 4), c4 = c % (DKP / 4);
+                const int key = key0 + r;
+                *reinterpret_cast<f32x4 *>(&sK[r * LK + 4 * c4]) =
+                    key < p.M ? load_row4(kbase + (size_t)p.DK * key, 4 * c4, p.DK, p.vecK) : f32x4{0, 0, 0, 0};
+            }
+            for (int c = tid; c < BC * (DVP / 4); c += NT) {
+                const int r = c / (DVP / 4), c4 = c % (DVP / 4);
+                const int key = key0 + r;
+                *reinterpret_cast<f32x4 *>(&sV[r * LV + 4 * c4]) =
+                    key < p.M ? load_row4(vbase + (size_t)p.DV * key, 4 * c4, p.DV, p.vecV) : f32x4{0, 0, 0, 0};
+            }
         }
         __syncthreads();
 
@@ -158,6 +205,8 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
                 }
             }
         }
+        kt = nx;
+        cls = ncls;
     }
 
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
