@@ -783,9 +783,10 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
     const rsrc_t rmask = mask_rsrc(p.mask, p.N, p.M);
     const int nqt = (p.N + BR - 1) / BR;
 
-    // Live query steps only.  Where the registers allow it (PF), the rows of the
-    // next live step are loaded into registers while the current step computes
-    // and written to LDS at the top of the next one.
+    // Live query steps only.  Where the registers allow it (PF: head dims up to 128,
+    // and the wide heads, whose column parts split the accumulators), the rows of the
+    // next live step are loaded into registers while the current step computes and
+    // written to LDS at the top of the next one.
     auto next_live = [&](int from, int *c) {
         for (int i = from; i < nqt; ++i) {
             *c = tile_class<BR / kMapTile, BC / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb,
@@ -795,7 +796,7 @@ __global__ __launch_bounds__((F32Cfg<DKP, DVP>::NT), 1) void bwd_f32_kernel(BwdA
         return nqt;
     };
     constexpr int PQ = BR * (DKP / 4) / NT, PO = BR * (DVP / 4) / NT;
-    constexpr bool PF = DKP + DVP <= 256 && PQ * NT == BR * (DKP / 4) && PO * NT == BR * (DVP / 4);
+    constexpr bool PF = (DKP + DVP <= 256 || CS > 1) && PQ * NT == BR * (DKP / 4) && PO * NT == BR * (DVP / 4);
     f32x4 pq[PF ? PQ : 1], po[PF ? PO : 1];
     float pl = INFINITY, pd = 0.f;
     auto fetch = [&](int step) {
