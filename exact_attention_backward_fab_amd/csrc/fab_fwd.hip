@@ -25,12 +25,15 @@ struct FwdArgs {
     const float *alibi;             // per-head ALiBi slopes [H] or NULL
 };
 
-template <int DKP, int DVP>
+// KS = 2 (grids with fewer work-groups than one resident round can hold): each
+// 32-query tile is shared by two waves that take the two 32-key halves of every
+// step, each with its own running max, sum and O, merged once at the end.
+template <int DKP, int DVP, int KS = 1>
 struct FwdCfg {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;
-    static constexpr int BR = 32 * WAVES;  // queries per work-group (32 per wave)
-    static constexpr int BC = 64;          // keys per step
+    static constexpr int BR = 32 * WAVES / KS;  // queries per work-group (32 per query tile)
+    static constexpr int BC = 64;               // keys per step
     static constexpr int LK = DKP + 4;     // sK row stride (floats)
     static constexpr int LV = DVP + 4;     // sV row stride
 };
@@ -42,22 +45,25 @@ struct FwdF32Occ {
     static constexpr int v = DKP + DVP <= 256 ? 2 : 1;
 };
 
-template <int DKP, int DVP, bool AB>
+template <int DKP, int DVP, bool AB, int KS = 1>
 __global__ __launch_bounds__(256, (FwdF32Occ<DKP, DVP>::v))
 __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::v))) void fwd_f32_kernel(FwdArgs p)
 {
-    using C = FwdCfg<DKP, DVP>;
+    using C = FwdCfg<DKP, DVP, KS>;
     constexpr int BC = C::BC, BR = C::BR, NT = C::NT, LK = C::LK, LV = C::LV;
-    constexpr int NKT = BC / 32;
+    constexpr int NKT = BC / 32, NKW = NKT / KS;   // 32-key sub-tiles of a step, of a wave
+    constexpr int QW = C::WAVES / KS;              // 32-query tiles of the work-group
     __shared__ __attribute__((aligned(16))) float sK[BC * LK];
     __shared__ __attribute__((aligned(16))) float sV[BC * LV];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+    const int qw = KS == 1 ? w : w % QW, kh = KS == 1 ? 0 : w / QW;   // query tile, key half of this wave
+    const int kk0 = KS == 1 ? 0 : kh * NKW;  // first sub-tile of each step this wave takes
     const int nqt = (p.N + BR - 1) / BR;
     int qt, hb;
     query_block_work(blockIdx.x, nqt, p.H * p.B, p.fold, &qt, &hb);
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
-    const int n = qt * BR + w * 32 + l32;  // this lane's query (C-layout column)
+    const int n = qt * BR + qw * 32 + l32;  // this lane's query (C-layout column)
     const bool nok = n < p.N;
     const float *kbase = p.k + (size_t)p.DK * p.M * (g + p.Hkv * b);
     const float *vbase = p.v + (size_t)p.DV * p.M * (g + p.Hkv * b);
@@ -148,31 +154,32 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
         }
         __syncthreads();
 
-        // ---- S^T = K Q^T for NKT 32-key sub-tiles (lane = query, rows = keys)
-        f32x16 s[NKT];
+        // ---- S^T = K Q^T for this wave's 32-key sub-tiles (lane = query, rows = keys)
+        f32x16 s[NKW];
 #pragma unroll
-        for (int kk = 0; kk < NKT; ++kk) {
-            s[kk] = zero16();
+        for (int j = 0; j < NKW; ++j) {
+            const int kk = kk0 + j;
+            s[j] = zero16();
 #pragma unroll
             for (int t = 0; t < DKP / 2; t += 4) {
                 const f32x4 a = *reinterpret_cast<const f32x4 *>(&sK[(kk * 32 + l32) * LK + half * (DKP / 2) + t]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[kk] = mfma_f32(a[i], qf[t + i], s[kk]);
+                for (int i = 0; i < 4; ++i) s[j] = mfma_f32(a[i], qf[t + i], s[j]);
             }
         }
         // ---- scale, mask, running max (log2 units)
         float mloc = -INFINITY;
 #pragma unroll
-        for (int kk = 0; kk < NKT; ++kk)
+        for (int j = 0; j < NKW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = key0 + kk * 32 + crow(r, half);
-                float x = s[kk][r] * sl2;
+                const int key = key0 + (kk0 + j) * 32 + crow(r, half);
+                float x = s[j][r] * sl2;
                 if (AB && slope2 != 0.f) x += slope2 * (float)(key - n);
                 if (cls == kTileMixed && nok && key < p.M)
                     x += half_bits_to_float(p.mask[key + (size_t)p.M * n]) * kLog2e;
                 if (key >= p.M || !nok || (cls == kTileCausal && key > n)) x = -INFINITY;
-                s[kk][r] = x;
+                s[j][r] = x;
                 mloc = fmaxf(mloc, x);
             }
         mloc = swap_halves_max(mloc);
@@ -181,11 +188,11 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
         const float alpha = fast_exp2(m_run - m_use);
         float lsum = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < NKT; ++kk)
+        for (int j = 0; j < NKW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(s[kk][r] - m_use);
-                s[kk][r] = e;
+                const float e = fast_exp2(s[j][r] - m_use);
+                s[j][r] = e;
                 lsum += e;
             }
         l_half = l_half * alpha + lsum;
@@ -197,16 +204,46 @@ __attribute__((amdgpu_waves_per_eu(FwdF32Occ<DKP, DVP>::v, FwdF32Occ<DKP, DVP>::
 #pragma unroll
         for (int dt = 0; dt < DVP / 32; ++dt) {
 #pragma unroll
-            for (int kk = 0; kk < NKT; ++kk) {
+            for (int j = 0; j < NKW; ++j) {
 #pragma unroll
                 for (int u = 0; u < 16; ++u) {
-                    const float a = sV[(kk * 32 + crow(u, half)) * LV + dt * 32 + l32];
-                    oacc[dt] = mfma_f32(a, s[kk][u], oacc[dt]);
+                    const float a = sV[((kk0 + j) * 32 + crow(u, half)) * LV + dt * 32 + l32];
+                    oacc[dt] = mfma_f32(a, s[j][u], oacc[dt]);
                 }
             }
         }
         kt = nx;
         cls = ncls;
+    }
+
+    // ---- KS = 2: the second key half hands its running max, sum and O to the first
+    // through the K rows (no longer read); the first rescales both to the larger max
+    if constexpr (KS == 2) {
+        constexpr int XO = DVP / 32 * 16;   // O values per lane
+        static_assert(QW * (XO + 2) * 64 <= BC * LK, "key-half exchange area");
+        float *xch = sK + qw * (XO + 2) * 64;
+        __syncthreads();   // every wave is done with sK
+        if (kh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = oacc[dt][r];
+            xch[XO * 64 + lane] = m_run;
+            xch[(XO + 1) * 64 + lane] = l_half;
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        const float m1 = xch[XO * 64 + lane], l1 = xch[(XO + 1) * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        // a half that saw no weight has max -inf and zero sum and O: its factor is 0
+        const float a0 = m == -INFINITY ? 0.f : fast_exp2(m_run - m);
+        const float a1 = m == -INFINITY ? 0.f : fast_exp2(m1 - m);
+        l_half = l_half * a0 + l1 * a1;
+#pragma unroll
+        for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
+        m_run = m;
     }
 
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
@@ -250,8 +287,27 @@ hipError_t run_fwd(const FwdArgs &a, hipStream_t s)
         const int grid = ceil_div(a.N, C::BR) * a.H * a.B;
         static ResidentCache slots;
         FwdArgs b = a;
-        // (both instantiations have the same resources: one occupancy query)
-        b.fold = grid <= slots.get(reinterpret_cast<const void *>(&fwd_f32_kernel<DKP, DVP, false>), C::NT);
+        // (the instantiations have the same LDS and occupancy: one occupancy query)
+        const int res = slots.get(reinterpret_cast<const void *>(&fwd_f32_kernel<DKP, DVP, false>), C::NT);
+        if constexpr (DKP + DVP <= 256) {
+            // each query tile's keys split over two waves (twice the work-groups of half
+            // the queries, each wave holding half the scores): where the plain grid
+            // leaves CUs without a work-group, where a mask or the causal rule makes the
+            // query blocks' work unequal (smaller blocks balance better), and for the
+            // 32-wide heads (twice the waves per SIMD); measured slower only on unmasked
+            // 128-wide heads with a full grid
+            const int grid2 = ceil_div(a.N, FwdCfg<DKP, DVP, 2>::BR) * a.H * a.B;
+            const bool idle = grid < res / FwdF32Occ<DKP, DVP>::v;
+            if (DKP + DVP <= 64 || idle || a.causal || a.map) {
+                b.fold = grid2 <= res;
+                if (a.alibi)
+                    hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP, true, 2>), dim3(grid2), dim3(C::NT), 0, s, b);
+                else
+                    hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP, false, 2>), dim3(grid2), dim3(C::NT), 0, s, b);
+                return hipGetLastError();
+            }
+        }
+        b.fold = grid <= res;
         if (a.alibi)
             hipLaunchKernelGGL((fwd_f32_kernel<DKP, DVP, true>), dim3(grid), dim3(C::NT), 0, s, b);
         else
