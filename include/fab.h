@@ -224,7 +224,7 @@ int fab_backward_alibi(const fab_shape *shape, const void *q, const void *k, con
  *   Limit: shapes whose fab_workspace_bytes(.., has_mask = mask != NULL,
  *   have_o_lse = O != NULL) exceeds FAB_NOALLOC_SCRATCH_BYTES return
  *   FAB_E_UNSUPPORTED (nothing enqueued); e.g. B=2, H=8, N=M=1024, D=64 in bf16
- *   mode needs about 41 MB.
+ *   mode needs about 56 MiB.
  *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
  *   last call's contents (the kernels write every workspace byte they read, so
  *   nothing needs to start at zero).  Calls that overlap on one GPU -- on two
