@@ -134,14 +134,15 @@ hipError_t launch_pack_qkv(const void *q, const void *k, const void *v, __bf16 *
 // sub-blocks for head-dim pairs up to 64 + 64, 2 up to 192 + 192, else 1).
 constexpr int f32_keys_per_wg(int dkp, int dvp) { return 32 * (dkp + dvp <= 128 ? 4 : dkp + dvp <= 384 ? 2 : 1); }
 
-// Query splits of the f32 dK/dV kernel: below one work-group per CU (256 CUs), each
+// Query splits of the f32 dK/dV kernel: below two work-groups per CU (256 CUs: two
+// rounds, in which the heaviest-first order balances the causal key blocks), each
 // (key block, query head) is run by 2 or 4 work-groups that take interleaved live
 // query steps, each with its own dK/dV partial.
 inline int f32_query_splits(const Dims &d, int dkp, int dvp)
 {
     const int64_t wgs = (int64_t)((d.M + f32_keys_per_wg(dkp, dvp) - 1) / f32_keys_per_wg(dkp, dvp)) * d.H * d.B;
     int qs = 1;
-    while (qs < 4 && wgs * qs < 256) qs *= 2;
+    while (qs < 4 && wgs * qs < 512) qs *= 2;
     return qs;
 }
 
