@@ -331,11 +331,13 @@ struct FwdArgs16 {
 // stages with the mask rows fit (the 192-wide heads): there the MIXED steps would
 // otherwise wait on their own mask loads with no other work-group's products to
 // hide them.
-template <int DKP, int DVP, bool PREP, bool AB, bool MS = false>
+template <int DKP, int DVP, bool PREP, bool AB, bool MS = false, int KS = 1>
 __global__ __launch_bounds__(256, (QStages<DKP, DVP, MS>::Occ))
 __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP, MS>::Occ))) void fwd_bf16_kernel(FwdArgs16 p)
 {
     using ST = QStages<DKP, DVP, MS>;
+    static_assert(KS == 1 || (KS == 2 && !MS), "key split without staged mask rows only");
+    constexpr int QWv = kQW / KS, BRv = 32 * QWv;   // 32-query tiles and queries of the work-group
     __shared__ __attribute__((aligned(16))) char sKV[ST::N * ST::kBytes];
     __shared__ int sList[kQList];
     __shared__ int sCount[kQW + 1];
@@ -344,12 +346,13 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int row_off = tile_row_off(lane), tr_off = tile_tr_off(lane);
     const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)sKV;
-    const int nqt = (p.N + kQBQ - 1) / kQBQ;
+    const int qw = KS == 1 ? w : w % QWv, kh = KS == 1 ? 0 : w / QWv;   // query tile, key part of this wave
+    const int nqt = (p.N + BRv - 1) / BRv;
     const QWork wk = qouter_work(blockIdx.x, nqt, p.H * p.B, p.fold);   // latest queries first (most keys if causal)
     const int qt = wk.qt, hb = wk.hb;
     const int h = hb % p.H, b = hb / p.H, g = h / (p.H / p.Hkv);
-    const int q0 = qt * kQBQ;
-    const int myq = q0 + 32 * w + l32;  // this lane's query (C-layout column of S^T and O^T)
+    const int q0 = qt * BRv;
+    const int myq = q0 + 32 * qw + l32;  // this lane's query (C-layout column of S^T and O^T)
     const bool qok = myq < p.N;
     const size_t hrow = (size_t)p.N * (h + p.H * b);
     const size_t kvrow = (size_t)p.Mp * (g + p.Hkv * b);
@@ -360,7 +363,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
     load_q_operand<DKP>(qf, p.q, (int64_t)(hrow + (qok ? myq : 0)) * p.DK, qok, p.DK, p.vecK, half, p.in_fmt);
     const size_t qhead = (size_t)(h + p.H * b) * p.Np;   // PREP: first tile row of this head
     if constexpr (PREP) {
-        if (myq < p.Np) {
+        if (kh == 0 && myq < p.Np) {
             __bf16 *qt16 = p.q16 + qhead * DKP;
 #pragma unroll
             for (int t = 0; t < DKP / 16; ++t)
@@ -382,20 +385,34 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
     stream_key_steps<DKP, DVP, kQW, ST>(
         rk, rv, sKV, kv_lds, sList, sCount, (p.M + kQBK - 1) / kQBK, tid, lane, w,
         [&](int s) {
-            return tile_class<kQBQ / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
+            return tile_class<BRv / kMapTile, kQBK / kMapTile>(p.map, p.causal, p.N, p.M, p.nqb, p.nkb, q0 / kMapTile,
                               s * (kQBK / kMapTile));
         },
         [&](int s, int cls, const char *Kb, const char *Vb, const char *Mb) {
             const int key0 = s * kQBK;
-            f32x16 st[2];
-            st_pt_pair<DKP, DVP, false>(Kb, qf, nullptr, nullptr, row_off, st, nullptr);
+            constexpr int NSUB = 2 / KS;   // 32-key sub-tiles of the step this wave takes
+            f32x16 st[NSUB];
+            if constexpr (KS == 1) {
+                st_pt_pair<DKP, DVP, false>(Kb, qf, nullptr, nullptr, row_off, st, nullptr);
+            } else {
+                // S^T of sub-tile kh only, the K rows read two products ahead
+                constexpr int TS = DKP / 16, R = 2;
+                bf16x8 kr[R];
+                st[0] = zero16();
+#pragma unroll
+                for (int j = 0; j < TS + R; ++j) {
+                    if (j >= R) st[0] = mfma_bf16(kr[(j - R) % R], qf[j - R], st[0]);
+                    if (j < TS) kr[j % R] = lds_row8(Kb + row_off + 512 * kh + 2304 * j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             // scores in log2 units = st * mul: a step with every key visible (FREE and
             // inside M) keeps the raw products and folds the scale into the exponent
             float mul = sl2;
             if (!(cls == kTileFree && key0 + kQBK <= p.M && sl2 > 0.f && (!AB || slope2 == 0.f))) {
                 const int lim = qok ? min(cls == kTileCausal ? myq : INT_MAX, p.M - 1) : -1;
-                scale_and_mask<2, AB>(st, key0, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half, slope2,
-                                  myq, MS ? Mb : nullptr, 32 * w + l32);
+                scale_and_mask<NSUB, AB>(st, key0 + 32 * kh, lim, cls == kTileMixed, mrow, p.M, (p.M & 3) == 0, sl2, half,
+                                     slope2, myq, MS ? Mb : nullptr, 32 * w + l32);
                 mul = 1.f;
             }
 
@@ -406,7 +423,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
             // most steps skip rescaling the accumulators.
             float mraw = -INFINITY;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < NSUB; ++kk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, st[kk][r]);
             const float mloc = swap_halves_max(mraw) * mul;
@@ -422,7 +439,7 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // all -inf so far: P = 0
             float lsum = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < NSUB; ++kk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float e = fast_exp2(__builtin_fmaf(st[kk][r], mul, -m_use));
@@ -433,9 +450,9 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
 
             // ---- O^T += V^T P^T: A = V^T by transposing reads (key rows 16u + 4*half
             // (+8) of the sub-tile), B = P^T (lane = query, keys in operand order)
-            bf16x8 pb4[4];   // index 2 kk + u
+            bf16x8 pb4[2 * NSUB];   // index 2 kk + u
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < NSUB; ++kk)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     float pv[8];
@@ -443,9 +460,57 @@ __attribute__((amdgpu_waves_per_eu(QStages<DKP, DVP, MS>::Occ, QStages<DKP, DVP,
                     for (int i = 0; i < 8; ++i) pv[i] = st[kk][8 * u + i];
                     pb4[2 * kk + u] = to_bf16x8(pv);
                 }
-            tr_products<DVP / 32, true>(oacc, pb4, Vb, tr_off);
+            if constexpr (KS == 1) {
+                tr_products<DVP / 32, true>(oacc, pb4, Vb, tr_off);
+            } else {
+                // the two groups (u) of sub-tile kh: V^T rows of that sub-tile by transposing reads
+                constexpr int NC = DVP / 32, NJ = 2 * NC, R = 3;
+                bf16x8 br[R];
+#pragma unroll
+                for (int j = 0; j < NJ + R; ++j) {
+                    if (j >= R) {
+                        const int i = j - R, u = i / NC, c = i % NC;
+                        oacc[c] = mfma_bf16(br[i % R], pb4[u], oacc[c]);
+                    }
+                    if (j < NJ) {
+                        const int u = j / NC, c = j % NC;
+                        br[j % R] = lds_tr8(Vb + tr_off + 4608 * c + 512 * kh + 256 * u);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         },
         0, 1, p.mask, p.N, q0, p.M);
+
+    // ---- KS = 2: the second key part hands its reference max, sum and O to the first
+    // through the stages (no longer read); the first rescales both to the larger max
+    if constexpr (KS == 2) {
+        constexpr int XO = DVP / 32 * 16;   // O values per lane
+        static_assert(QWv * (XO + 2) * 64 * 4 <= ST::N * ST::kBytes, "key-part exchange area");
+        float *xch = reinterpret_cast<float *>(sKV) + qw * (XO + 2) * 64;
+        __syncthreads();   // every wave is done with the stages
+        if (kh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = oacc[dt][r];
+            xch[XO * 64 + lane] = m_run;
+            xch[(XO + 1) * 64 + lane] = l_part;
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        const float m1 = xch[XO * 64 + lane], l1 = xch[(XO + 1) * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        // a part that saw no weight has max -inf and zero sum and O: its factor is 0
+        const float a0 = m == -INFINITY ? 0.f : fast_exp2(m_run - m);
+        const float a1 = m == -INFINITY ? 0.f : fast_exp2(m1 - m);
+        l_part = l_part * a0 + l1 * a1;
+#pragma unroll
+        for (int dt = 0; dt < DVP / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
+        m_run = m;
+    }
 
     // ---- normalise and store O [DV,H,N,B] and the natural-log LSE [N,H,B]
     const float l = swap_halves_sum(l_part);
@@ -883,7 +948,24 @@ template <int DKP, int DVP, bool PREP, bool MS>
 void launch_fwd16_variant(FwdArgs16 b, int grid, hipStream_t s)
 {
     static ResidentCache slots;
-    b.fold = grid <= slots.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, PREP, false, MS>), kQNT);
+    const int res = slots.get(reinterpret_cast<const void *>(&fwd_bf16_kernel<DKP, DVP, PREP, false, MS>), kQNT);
+    // each 32-query tile's keys split over two waves (64-query work-groups, twice as
+    // many) where the plain grid fills at most half of the resident slots: causal MHA
+    // N=1024, 64-wide heads, forward 27.7 -> 23.2 us.  Only the kernels that never
+    // stage mask rows (two work-groups per CU) split, so that a mask and the causal
+    // flag, which may differ in MS, still take the same path and give the same bits.
+    if constexpr (!MS && QStages<DKP, DVP>::Occ == 2) {
+        if (2 * grid <= res) {
+            const int grid2 = ceil_div(b.N, kQBQ / 2) * b.H * b.B;
+            b.fold = grid2 <= res;
+            if (b.alibi)
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, PREP, true, MS, 2>), dim3(grid2), dim3(kQNT), 0, s, b);
+            else
+                hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, PREP, false, MS, 2>), dim3(grid2), dim3(kQNT), 0, s, b);
+            return;
+        }
+    }
+    b.fold = grid <= res;
     if (b.alibi)
         hipLaunchKernelGGL((fwd_bf16_kernel<DKP, DVP, PREP, true, MS>), dim3(grid), dim3(kQNT), 0, s, b);
     else
